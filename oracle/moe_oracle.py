@@ -133,6 +133,7 @@ def quantize(w: np.ndarray, qbits: int) -> tuple[np.ndarray, np.ndarray]:
     first_max = np.argmax(np.abs(blocks), axis=-1)          # first index on ties
     m = np.take_along_axis(blocks, first_max[..., None], axis=-1)[..., 0]
     d16 = (m / np.float32(cmin)).astype(np.float32).astype(np.float16)
+    d16 = np.where(d16 == 0, np.float16(0.0), d16)          # a zero scale is stored as +0
     d32 = d16.astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = (blocks / d32[..., None]).astype(np.float32)
@@ -290,12 +291,20 @@ def combine(y_sorted: np.ndarray, pair_pos: np.ndarray, topk_w: np.ndarray,
     return out
 
 
-def layer_forward(x, w_router, bias, experts, shared, k: int, return_all: bool = False):
+def layer_forward(x, w_router, bias, experts, shared, k: int, return_all: bool = False, idx=None):
     """One MoE layer: route, permute, routed SwiGLU experts, shared expert,
     weighted combine.  `experts` is a sequence of QExpert (length E); `shared`
-    is a QExpert or None."""
+    is a QExpert or None.  If `idx` [T, k] is given it replaces the selection
+    (the weights are still the renormalised softmax of this layer's logits at
+    those experts) -- used to evaluate the layer at another implementation's
+    choice among near-tied experts."""
     x = np.asarray(x, dtype=np.float64)
-    logits, idx, w = route(x, w_router, bias, k)
+    if idx is None:
+        logits, idx, w = route(x, w_router, bias, k)
+    else:
+        logits = router_logits(x, w_router, bias)
+        idx = np.asarray(idx, dtype=np.int32)
+        w = topk_weights(logits, idx)
     counts, offsets, sorted_pair, pair_pos = permute(idx, len(experts))
     y = expert_outputs(x, idx, experts, sorted_pair, offsets)
     s = swiglu(x, *shared.dense()) if shared is not None else None
