@@ -1,0 +1,423 @@
+// C ABI of the MoE library: argument validation, workspace layout and
+// dispatch to the gfx950 kernels.  Every check runs on the host before any
+// HIP call; no C++ exception crosses the boundary.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+thread_local size_t g_required_ws = 0;
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_detail[0] = '\0';
+  return MOE_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Smallest M tile of the grouped GEMM (sizes the tile list).
+constexpr int kMinTileBM = 32;
+
+struct WsLayout {
+  size_t header, active, tile_expert, tile_m0, chunk_hist, h_routed, h_shared;
+  size_t end_perm, end_ffn;
+  size_t logits, end_route;
+  size_t topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos, y_sorted, shared_out, total;
+  int64_t max_tiles;
+};
+
+WsLayout ws_layout(const moe_shape& s, int64_t T) {
+  WsLayout L{};
+  const int64_t P = T * s.top_k;
+  const int64_t E = s.n_experts;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up(bytes);
+    return at;
+  };
+  L.max_tiles = (P + kMinTileBM - 1) / kMinTileBM + std::min<int64_t>(E, P) +
+                (s.shared_inter > 0 ? (T + kMinTileBM - 1) / kMinTileBM : 0) + 2;
+  L.header = take(moe::kHdrWords * 4);
+  L.active = take(size_t(E) * 4);
+  L.tile_expert = take(size_t(L.max_tiles) * 4);
+  L.tile_m0 = take(size_t(L.max_tiles) * 4);
+  const int64_t n_chunks = P > moe::kSmallPairs ? (P + moe::kPermChunk - 1) / moe::kPermChunk : 0;
+  L.chunk_hist = take(size_t(n_chunks) * size_t(E + 1) * 4);
+  L.end_perm = off;
+  L.h_routed = take(size_t(P) * s.inter * 2);
+  L.h_shared = take(size_t(T) * s.shared_inter * 2);
+  L.end_ffn = off;
+  L.logits = take(size_t(T) * E * 4);
+  L.end_route = off;
+  L.topk_idx = take(size_t(P) * 4);
+  L.topk_w = take(size_t(P) * 4);
+  L.counts = take(size_t(E) * 4);
+  L.offsets = take(size_t(E + 1) * 4);
+  L.sorted_pair = take(size_t(P) * 4);
+  L.pair_pos = take(size_t(P) * 4);
+  L.y_sorted = take(size_t(P) * s.hidden * 4);
+  L.shared_out = take(s.shared_inter > 0 ? size_t(T) * s.hidden * 4 : 0);
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (ws == nullptr || have < need) {
+    g_required_ws = need;
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes is too small: %zu bytes needed (%zu MiB short)", have,
+                need, (need - std::min(need, have) + (1u << 20) - 1) >> 20);
+  }
+  if (!aligned(ws, kAlign)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return MOE_OK;
+}
+
+int check_shape(const moe_shape* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->hidden <= 0 || s->hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 32", s->hidden);
+  if (s->inter <= 0 || s->inter % 32) return fail(MOE_ERR_INVALID_ARG, "inter=%d must be a positive multiple of 32", s->inter);
+  if (s->shared_inter < 0 || s->shared_inter % 32)
+    return fail(MOE_ERR_INVALID_ARG, "shared_inter=%d must be 0 or a positive multiple of 32", s->shared_inter);
+  if (s->n_experts < 1 || s->n_experts > moe::kMaxExperts)
+    return fail(MOE_ERR_INVALID_ARG, "n_experts=%d must be in [1, %d]", s->n_experts, moe::kMaxExperts);
+  if (s->top_k < 1 || s->top_k > std::min(s->n_experts, moe::kMaxTopK))
+    return fail(MOE_ERR_INVALID_ARG, "top_k=%d must be in [1, min(n_experts, %d)]", s->top_k, moe::kMaxTopK);
+  if (s->qbits != 2 && s->qbits != 3) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2 and 3 are supported", s->qbits);
+  return MOE_OK;
+}
+
+int check_T(int64_t T, const moe_shape* s) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%lld must be >= 0", (long long)T);
+  if (T * int64_t(s->top_k) > INT32_MAX) return fail(MOE_ERR_INVALID_ARG, "T*top_k exceeds 2^31-1");
+  return MOE_OK;
+}
+
+int check_dtype(moe_dtype d, const char* what) {
+  if (d != MOE_F32 && d != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "%s dtype %d is not MOE_F32 or MOE_BF16", what, int(d));
+  return MOE_OK;
+}
+
+int check_qw(const moe_qweights& q, const char* what, int n) {
+  for (int m = 0; m < 3; ++m) {
+    if (!q.codes[m] || !q.scales[m]) return fail(MOE_ERR_INVALID_ARG, "%s: codes/scales[%d] is NULL", what, m);
+    if (!aligned(q.codes[m], 16)) return fail(MOE_ERR_INVALID_ARG, "%s: codes[%d] must be 16-byte aligned", what, m);
+    if (!aligned(q.scales[m], 4)) return fail(MOE_ERR_INVALID_ARG, "%s: scales[%d] must be 4-byte aligned", what, m);
+  }
+  if (n > 1) {
+    if (q.code_stride <= 0 || q.code_stride % 16)
+      return fail(MOE_ERR_INVALID_ARG, "%s: code_stride=%lld must be a positive multiple of 16", what, (long long)q.code_stride);
+    if (q.scale_stride <= 0 || q.scale_stride % 2)
+      return fail(MOE_ERR_INVALID_ARG, "%s: scale_stride=%lld must be a positive even count", what, (long long)q.scale_stride);
+  }
+  return MOE_OK;
+}
+
+int check_layer(const moe_layer* L, const moe_shape* s, bool need_router, bool need_experts) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  if (need_router) {
+    if (!L->w_router) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
+    if (int r = check_dtype(L->router_dtype, "router")) return r;
+  }
+  if (need_experts) {
+    if (int r = check_qw(L->experts, "experts", s->n_experts)) return r;
+    if (s->shared_inter > 0)
+      if (int r = check_qw(L->shared, "shared", 1)) return r;
+  }
+  return MOE_OK;
+}
+
+moe::QMat qmat(const moe_qweights& q, int m) { return moe::QMat{q.codes[m], q.scales[m], q.code_stride, q.scale_stride}; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+moe_algo pick_algo(const moe_options* o, int64_t T) {
+  const moe_algo a = o ? o->ffn_algo : MOE_ALGO_AUTO;
+  if (a != MOE_ALGO_AUTO) return a;
+  (void)T;
+  return MOE_ALGO_GEMV;  // the grouped GEMM is not built yet
+}
+
+int check_opts(const moe_options* o) {
+  if (!o) return MOE_OK;
+  if (o->ffn_algo < MOE_ALGO_AUTO || o->ffn_algo > MOE_ALGO_GROUPED)
+    return fail(MOE_ERR_INVALID_ARG, "ffn_algo=%d is not a moe_algo", int(o->ffn_algo));
+  if (o->flags != 0) return fail(MOE_ERR_INVALID_ARG, "flags must be 0");
+  return MOE_OK;
+}
+
+// ---- the steps, shared by the single-step entry points and layer_forward
+
+hipError_t do_route(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s, float* logits,
+                    int32_t* idx, float* w, hipStream_t st) {
+  hipError_t e = moe::launch_router_gemv(x, xd == MOE_BF16, T, s->hidden, L->w_router, L->router_dtype == MOE_BF16,
+                                         L->router_bias, s->n_experts, logits, st);
+  if (e != hipSuccess) return e;
+  return moe::launch_topk(logits, T, s->n_experts, s->top_k, idx, w, st);
+}
+
+hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s,
+                  const int32_t* offsets, const int32_t* sorted_pair, float* y_sorted, float* shared_out,
+                  moe_algo algo, void* ws, const WsLayout& W, hipStream_t st) {
+  moe::FfnArgs a{};
+  a.x = x;
+  a.x_bf16 = xd == MOE_BF16;
+  a.T = T;
+  a.H = s->hidden;
+  a.I = s->inter;
+  a.Is = s->shared_inter;
+  a.k = s->top_k;
+  a.E = s->n_experts;
+  a.qbits = s->qbits;
+  a.has_shared = s->shared_inter > 0 && shared_out != nullptr;
+  a.rg = qmat(L->experts, 0);
+  a.ru = qmat(L->experts, 1);
+  a.rd = qmat(L->experts, 2);
+  if (s->shared_inter > 0) {
+    a.sg = qmat(L->shared, 0);
+    a.su = qmat(L->shared, 1);
+    a.sd = qmat(L->shared, 2);
+  }
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.header = at<int32_t>(ws, W.header);
+  a.plan_active = at<int32_t>(ws, W.active);
+  a.tile_expert = at<int32_t>(ws, W.tile_expert);
+  a.tile_m0 = at<int32_t>(ws, W.tile_m0);
+  a.h_routed = at<_Float16>(ws, W.h_routed);
+  a.h_shared = at<_Float16>(ws, W.h_shared);
+  a.y_sorted = y_sorted;
+  a.shared_out = shared_out;
+  const int tile_bm = algo == MOE_ALGO_GROUPED ? kMinTileBM : 0;
+  hipError_t e = moe::launch_plan(offsets, s->n_experts, T, a.has_shared, tile_bm, at<int32_t>(ws, W.header),
+                                  at<int32_t>(ws, W.active), at<int32_t>(ws, W.tile_expert),
+                                  at<int32_t>(ws, W.tile_m0), st);
+  if (e != hipSuccess) return e;
+  if (algo == MOE_ALGO_GROUPED) return moe::launch_ffn_grouped(a, tile_bm, W.max_tiles, st);
+  return moe::launch_ffn_gemv(a, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    case MOE_ERR_INDEX: return "MOE_ERR_INDEX";
+    default: return "unknown moe_status";
+  }
+}
+
+const char* moe_last_error_detail(void) { return g_detail; }
+size_t moe_last_required_workspace(void) { return g_required_ws; }
+
+size_t moe_workspace_bytes(const moe_shape* shape, int64_t T, const moe_options* opts) {
+  if (check_shape(shape) || check_T(T, shape) || check_opts(opts)) return 0;
+  return ws_layout(*shape, T).total;
+}
+
+int moe_route(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer, const moe_shape* shape,
+              float* logits, int32_t* topk_idx, float* topk_w, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  try {
+    if (int r = check_shape(shape)) return r;
+    if (int r = check_T(T, shape)) return r;
+    if (int r = check_layer(layer, shape, true, false)) return r;
+    if (int r = check_dtype(x_dtype, "x")) return r;
+    if (T == 0) return ok();
+    if (!x || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "x, topk_idx and topk_w must be non-NULL");
+    const WsLayout W = ws_layout(*shape, T);
+    if (!logits) {
+      if (int r = check_ws(workspace, workspace_bytes, W.end_route)) return r;
+      logits = at<float>(workspace, W.logits);
+    }
+    return device_status(do_route(x, x_dtype, T, layer, shape, logits, topk_idx, topk_w, as_stream(stream)),
+                         "moe_route");
+  } catch (...) {
+    return fail(MOE_ERR_DEVICE, "moe_route: unexpected exception");
+  }
+}
+
+int moe_permute(const int32_t* topk_idx, int64_t T, const moe_shape* shape, int32_t* counts, int32_t* offsets,
+                int32_t* sorted_pair, int32_t* pair_pos, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (int r = check_shape(shape)) return r;
+    if (int r = check_T(T, shape)) return r;
+    if (!counts || !offsets) return fail(MOE_ERR_INVALID_ARG, "counts and offsets must be non-NULL");
+    if (T > 0 && (!topk_idx || !sorted_pair || !pair_pos))
+      return fail(MOE_ERR_INVALID_ARG, "topk_idx, sorted_pair and pair_pos must be non-NULL");
+    const WsLayout W = ws_layout(*shape, T);
+    if (int r = check_ws(workspace, workspace_bytes, W.end_perm)) return r;
+    return device_status(moe::launch_permute(topk_idx, T * shape->top_k, shape->n_experts, counts, offsets,
+                                             sorted_pair, pair_pos, at<int32_t>(workspace, W.header),
+                                             at<int32_t>(workspace, W.chunk_hist), as_stream(stream)),
+                         "moe_permute");
+  } catch (...) {
+    return fail(MOE_ERR_DEVICE, "moe_permute: unexpected exception");
+  }
+}
+
+int moe_expert_ffn(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer, const moe_shape* shape,
+                   const int32_t* offsets, const int32_t* sorted_pair, float* y_sorted, float* shared_out,
+                   const moe_options* opts, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (int r = check_shape(shape)) return r;
+    if (int r = check_T(T, shape)) return r;
+    if (int r = check_opts(opts)) return r;
+    if (int r = check_layer(layer, shape, false, true)) return r;
+    if (int r = check_dtype(x_dtype, "x")) return r;
+    if (T == 0) return ok();
+    if (!x || !offsets || !sorted_pair || !y_sorted)
+      return fail(MOE_ERR_INVALID_ARG, "x, offsets, sorted_pair and y_sorted must be non-NULL");
+    if (!aligned(x, 16) || !aligned(y_sorted, 16) || (shared_out && !aligned(shared_out, 16)))
+      return fail(MOE_ERR_INVALID_ARG, "x, y_sorted and shared_out must be 16-byte aligned");
+    const WsLayout W = ws_layout(*shape, T);
+    if (int r = check_ws(workspace, workspace_bytes, W.end_ffn)) return r;
+    return device_status(do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y_sorted, shared_out,
+                                pick_algo(opts, T), workspace, W, as_stream(stream)),
+                         "moe_expert_ffn");
+  } catch (...) {
+    return fail(MOE_ERR_DEVICE, "moe_expert_ffn: unexpected exception");
+  }
+}
+
+int moe_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w, const float* shared_out,
+                int64_t T, const moe_shape* shape, float* out, float* residual, uint16_t* next_in_bf16,
+                void* stream) {
+  try {
+    if (int r = check_shape(shape)) return r;
+    if (int r = check_T(T, shape)) return r;
+    if (T == 0) return ok();
+    if (!y_sorted || !pair_pos || !topk_w) return fail(MOE_ERR_INVALID_ARG, "y_sorted, pair_pos and topk_w must be non-NULL");
+    if (!out && !residual) return fail(MOE_ERR_INVALID_ARG, "one of out and residual must be non-NULL");
+    if (next_in_bf16 && !residual) return fail(MOE_ERR_INVALID_ARG, "next_in_bf16 needs residual");
+    for (const void* p : {(const void*)y_sorted, (const void*)shared_out, (const void*)out, (const void*)residual})
+      if (p && !aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "float tensors must be 16-byte aligned");
+    return device_status(moe::launch_combine(y_sorted, pair_pos, topk_w, shared_out, T, shape->hidden,
+                                             shape->top_k, out, residual, next_in_bf16, as_stream(stream)),
+                         "moe_combine");
+  } catch (...) {
+    return fail(MOE_ERR_DEVICE, "moe_combine: unexpected exception");
+  }
+}
+
+int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer, const moe_shape* shape,
+                      float* out, float* residual, uint16_t* next_in_bf16, int32_t* topk_idx, float* topk_w,
+                      const moe_options* opts, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (int r = check_shape(shape)) return r;
+    if (int r = check_T(T, shape)) return r;
+    if (int r = check_opts(opts)) return r;
+    if (int r = check_layer(layer, shape, true, true)) return r;
+    if (int r = check_dtype(x_dtype, "x")) return r;
+    if (T == 0) return ok();
+    if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+    if (!out && !residual) return fail(MOE_ERR_INVALID_ARG, "one of out and residual must be non-NULL");
+    if (next_in_bf16 && !residual) return fail(MOE_ERR_INVALID_ARG, "next_in_bf16 needs residual");
+    for (const void* p : {(const void*)x, (const void*)out, (const void*)residual})
+      if (p && !aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "x, out and residual must be 16-byte aligned");
+    const WsLayout W = ws_layout(*shape, T);
+    if (int r = check_ws(workspace, workspace_bytes, W.total)) return r;
+    hipStream_t st = as_stream(stream);
+    void* ws = workspace;
+    int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, W.topk_idx);
+    float* w = topk_w ? topk_w : at<float>(ws, W.topk_w);
+    hipError_t e = do_route(x, x_dtype, T, layer, shape, at<float>(ws, W.logits), idx, w, st);
+    if (e != hipSuccess) return device_status(e, "moe_layer_forward/route");
+    int32_t* offsets = at<int32_t>(ws, W.offsets);
+    int32_t* sorted_pair = at<int32_t>(ws, W.sorted_pair);
+    int32_t* pair_pos = at<int32_t>(ws, W.pair_pos);
+    e = moe::launch_permute(idx, T * shape->top_k, shape->n_experts, at<int32_t>(ws, W.counts), offsets, sorted_pair,
+                            pair_pos, at<int32_t>(ws, W.header), at<int32_t>(ws, W.chunk_hist), st);
+    if (e != hipSuccess) return device_status(e, "moe_layer_forward/permute");
+    float* y = at<float>(ws, W.y_sorted);
+    float* s_out = shape->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;
+    e = do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, pick_algo(opts, T), ws, W, st);
+    if (e != hipSuccess) return device_status(e, "moe_layer_forward/ffn");
+    e = moe::launch_combine(y, pair_pos, w, s_out, T, shape->hidden, shape->top_k, out, residual, next_in_bf16, st);
+    return device_status(e, "moe_layer_forward/combine");
+  } catch (...) {
+    return fail(MOE_ERR_DEVICE, "moe_layer_forward: unexpected exception");
+  }
+}
+
+int moe_rmsnorm_bf16(const float* r, int64_t T, int32_t H, uint16_t* a, void* stream) {
+  if (T < 0 || H <= 0 || H % 4) return fail(MOE_ERR_INVALID_ARG, "bad T=%lld or H=%d", (long long)T, H);
+  if (T == 0) return ok();
+  if (!r || !a) return fail(MOE_ERR_INVALID_ARG, "r and a must be non-NULL");
+  return device_status(moe::launch_rmsnorm_bf16(r, T, H, a, as_stream(stream)), "moe_rmsnorm_bf16");
+}
+
+int moe_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int32_t cols, int32_t qbits, float* out,
+                void* stream) {
+  if (qbits != 2 && qbits != 3) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2 and 3 are supported", qbits);
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "rows=%lld cols=%d: cols must be a positive multiple of 32", (long long)rows, cols);
+  if (rows == 0) return ok();
+  if (!codes || !scales || !out) return fail(MOE_ERR_INVALID_ARG, "codes, scales and out must be non-NULL");
+  if (!aligned(codes, 8) || !aligned(scales, 2) || !aligned(out, 16))
+    return fail(MOE_ERR_INVALID_ARG, "codes must be 8-, scales 2- and out 16-byte aligned");
+  return device_status(moe::launch_dequant(codes, scales, rows, cols, qbits, out, as_stream(stream)), "moe_dequant");
+}
+
+int moe_quantize(const float* w, int64_t rows, int32_t cols, int32_t qbits, uint8_t* codes, uint16_t* scales,
+                 void* stream) {
+  if (qbits != 2 && qbits != 3) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2 and 3 are supported", qbits);
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "rows=%lld cols=%d: cols must be a positive multiple of 32", (long long)rows, cols);
+  if (rows == 0) return ok();
+  if (!codes || !scales || !w) return fail(MOE_ERR_INVALID_ARG, "w, codes and scales must be non-NULL");
+  if (!aligned(codes, 8) || !aligned(scales, 2) || !aligned(w, 16))
+    return fail(MOE_ERR_INVALID_ARG, "codes must be 8-, scales 2- and w 16-byte aligned");
+  return device_status(moe::launch_quantize(w, rows, cols, qbits, codes, scales, as_stream(stream)), "moe_quantize");
+}
+
+int moe_read_error(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < 256) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL or too small");
+  hipStream_t st = as_stream(stream);
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return device_status(e, "moe_read_error/sync");
+  int32_t err = 0;
+  e = hipMemcpy(&err, workspace, sizeof(err), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return device_status(e, "moe_read_error/copy");
+  if (err == 0) return ok();
+  const int32_t zero = 0;
+  e = hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return device_status(e, "moe_read_error/clear");
+  return fail(MOE_ERR_INDEX, "%d expert ids outside [0, n_experts) were skipped by the last permutation", err);
+}
+
+}  // extern "C"

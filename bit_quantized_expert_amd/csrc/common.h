@@ -1,0 +1,175 @@
+// Device helpers shared by the gfx950 kernels of the MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 f16;
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 32;  // weights per quantisation block
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ float load_act(const float* p) { return *p; }
+__device__ __forceinline__ float load_act(const uint16_t* p) { return bf16_to_f32(*p); }
+
+__device__ __forceinline__ uint32_t pack_half2(f16 lo, f16 hi) {
+  return uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+}
+
+__device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+__device__ __forceinline__ uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Wave-level reductions (wave64) through cross-lane shuffles.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// 16x16x32 fp16 MFMA, fp32 accumulate.  Operand lane layout (gfx950):
+//   A: lane l holds A[m = l%16][k = 8*(l/16) .. +7]
+//   B: lane l holds B[k = 8*(l/16) .. +7][n = l%16]
+//   D: lane l holds D[m = 4*(l/16) + j][n = l%16], j = 0..3
+__device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 fp16 MFMA, fp32 accumulate.  Operand lane layout (gfx950):
+//   A: lane l holds A[m = l%32][k = 8*(l/32) .. +7]
+//   B: lane l holds B[k = 8*(l/32) .. +7][n = l%32]
+//   D: lane l holds D[m = 8*(j/4) + 4*(l/32) + j%4][n = l%32], j = 0..15
+__device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float16v mfma32_bf16(bf16x8 a, bf16x8 b, float16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Dequantisation of one 32-bit word of 2-bit codes into fp16 pairs.
+//
+// A word holds 16 codes, code i at bits 2i..2i+1.  Pair i (i = 0..7) is
+// (code i, code i+8): low half from bits 2i, high half from bits 2i+16.
+// For i <= 4 the code is OR-ed into the mantissa of the fp16 constant
+// M_i = 2^(10-2i) whose unit in the last place is 4^-i, so the code lands
+// with weight 1 and the half holds M_i + q exactly; subtracting M_i + 2
+// leaves c = q - 2 exactly, and multiplying by the fp16 block scale gives
+// c * s exactly (|c| <= 2).  Pairs 5..7 reuse M_0..M_2 on the word shifted
+// right by 10.  Operand order within an MFMA k-slice therefore is
+// k = {0,8,1,9,2,10,3,11} (first slice) and {4,12,5,13,6,14,7,15} (second);
+// the activations are staged in LDS in the same order.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t magic_bits(int i) {
+  // fp16 bit pattern of 2^(10-2i) in both halves
+  const uint32_t e = uint32_t(25 - 2 * i) << 10;
+  return e | (e << 16);
+}
+__device__ __forceinline__ f16 magic_val(int i) { return f16(float(1 << (10 - 2 * i))); }
+
+// Dequantise 2-bit word w (16 codes) with block scale s2 (scale in both
+// halves) into two MFMA k-slices (8 fp16 each) in the permuted order.
+__device__ __forceinline__ void dq2_word(uint32_t w, half2v s2, half8& lo, half8& hi) {
+  const uint32_t w10 = w >> 10;
+  half2v p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = i < 5 ? i : i - 5;
+    const uint32_t src = i < 5 ? w : w10;
+    const uint32_t v = (src & (0x00030003u << (2 * j))) | magic_bits(j);
+    const f16 off = magic_val(j) + f16(2.0f);
+    half2v h = as_half2(v) - half2v{off, off};
+    p[i] = h * s2;
+  }
+  lo = half8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  hi = half8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+}
+
+// Spread the 16 bits of h to even bit positions: bit k -> bit 2k.
+__device__ __forceinline__ uint32_t spread16(uint32_t h) {
+  h &= 0xffffu;
+  h = (h | (h << 8)) & 0x00ff00ffu;
+  h = (h | (h << 4)) & 0x0f0f0f0fu;
+  h = (h | (h << 2)) & 0x33333333u;
+  h = (h | (h << 1)) & 0x55555555u;
+  return h;
+}
+
+// 3-bit variant: w holds the low two bits of 16 codes (2-bit layout) and
+// sp = spread16(high bits) holds bit 2 of code i at bit 2i.  Pairs 0..3 use
+// M_0..M_3 with the high bits moved to 2i+2 (sp << 2; bits up to 2i+2 <= 8
+// stay inside the mantissa); pairs 4..7 use w >> 8 and sp >> 6 with M_0..M_3
+// (shifting right keeps bit 30, the high bit of code 15).  c = q - 4.
+__device__ __forceinline__ void dq3_word(uint32_t w, uint32_t sp, half2v s2, half8& lo, half8& hi) {
+  const uint32_t w8 = w >> 8, hs = sp << 2, h8 = sp >> 6;
+  half2v p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = i < 4 ? i : i - 4;
+    const uint32_t src = i < 4 ? w : w8;
+    const uint32_t hsrc = i < 4 ? hs : h8;
+    const uint32_t v = (src & (0x00030003u << (2 * j))) | (hsrc & (0x00040004u << (2 * j))) | magic_bits(j);
+    const f16 off = magic_val(j) + f16(4.0f);
+    half2v h = as_half2(v) - half2v{off, off};
+    p[i] = h * s2;
+  }
+  lo = half8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  hi = half8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+}
+
+// Position of weight r (0..15) of a 16-weight group in the permuted order.
+__host__ __device__ __forceinline__ int perm16(int r) { return r < 8 ? 2 * r : 2 * (r - 8) + 1; }
+
+// Exclusive scan over n <= 4096 ints held in LDS, 1024 threads.  Returns the
+// total.  `tmp` has 1024 ints.
+__device__ inline int block_exclusive_scan_lds(int* vals, int n, int* tmp) {
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;  // <= 4
+  int local[4];
+  int s = 0;
+  for (int i = 0; i < per; ++i) {
+    const int idx = tid * per + i;
+    local[i] = idx < n ? vals[idx] : 0;
+    s += local[i];
+  }
+  tmp[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += v;
+    __syncthreads();
+  }
+  const int total = tmp[1023];
+  int run = tmp[tid] - s;  // exclusive prefix of this thread's group
+  __syncthreads();
+  for (int i = 0; i < per; ++i) {
+    const int idx = tid * per + i;
+    if (idx < n) vals[idx] = run;
+    run += local[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+}  // namespace moe

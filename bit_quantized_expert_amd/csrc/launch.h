@@ -1,0 +1,72 @@
+// Internal launchers of the MoE kernels (host side).  The C ABI in abi.cpp
+// validates arguments and then calls these; they only launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 4096;
+constexpr int kMaxTopK = 32;
+constexpr int kSmallPairs = 2048;   // single-workgroup permutation up to this many pairs
+constexpr int kPermChunk = 1024;    // pairs per workgroup in the multi-workgroup permutation
+constexpr int kGemvMaxM = 16;       // tokens per MFMA tile in the decode kernels
+
+// Workspace header (int32 words at the start of the workspace).
+enum HeaderWord { kHdrError = 0, kHdrActive = 1, kHdrTiles = 2, kHdrWords = 64 };
+
+struct QMat {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  int64_t code_stride;   // bytes between experts
+  int64_t scale_stride;  // fp16 elements between experts
+};
+
+// Everything the expert-FFN kernels read.  Slot s < n_active is routed expert
+// plan_active[s]; slot n_active is the shared expert when has_shared.
+struct FfnArgs {
+  const void* x;
+  int x_bf16;
+  int64_t T;
+  int H, I, Is, k, E, qbits, has_shared;
+  QMat rg, ru, rd;  // routed gate / up / down
+  QMat sg, su, sd;  // shared gate / up / down
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  const int32_t* header;       // workspace header (n_active, n_tiles)
+  const int32_t* plan_active;  // [E] active expert ids
+  const int32_t* tile_expert;  // grouped GEMM tiles: expert id (-1 = shared)
+  const int32_t* tile_m0;      //                     first row of the tile
+  _Float16* h_routed;          // [P][I] SwiGLU activations, sorted order
+  _Float16* h_shared;          // [T][Is]
+  float* y_sorted;             // [P][H]
+  float* shared_out;           // [T][H] or null
+};
+
+hipError_t launch_quantize(const float* w, int64_t rows, int cols, int qbits, uint8_t* codes,
+                           uint16_t* scales, hipStream_t stream);
+hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int cols,
+                          int qbits, float* out, hipStream_t stream);
+hipError_t launch_router_gemv(const void* x, bool x_bf16, int64_t T, int H, const void* w, bool w_bf16,
+                              const float* bias, int E, float* logits, hipStream_t stream);
+hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_t* w, const float* bias,
+                              int E, float* logits, hipStream_t stream);
+hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
+                       hipStream_t stream);
+hipError_t launch_rmsnorm_bf16(const float* r, int64_t T, int H, uint16_t* a, hipStream_t stream);
+hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, int32_t* header, int32_t* chunk_hist,
+                          hipStream_t stream);
+// Builds the active-expert list (and, when tile_bm > 0, the grouped-GEMM tile
+// list) from offsets.
+hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm,
+                       int32_t* header, int32_t* active, int32_t* tile_expert, int32_t* tile_m0,
+                       hipStream_t stream);
+hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream);
+hipError_t launch_ffn_grouped(const FfnArgs& a, int tile_bm, int64_t max_tiles, hipStream_t stream);
+hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                          const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
+                          uint16_t* next_in, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,216 @@
+// Token-to-expert permutation: histogram, exclusive scan and a stable
+// scatter of the (token, rank) pairs into expert-contiguous order.  This is
+// this library's on-device counterpart of the per-layer partition of the 10
+// selected experts ("How Strata runs a 125-billion-parameter model ...",
+// Step 2, "Mapped host doorbell and a single captured CUDA graph"); here the
+// IDs never leave the GPU.
+//
+// Pair p = t*k + j.  Within an expert's segment the pairs keep ascending p,
+// so the result is unique.  IDs outside [0, E) are skipped and counted in the
+// workspace header (word 0).
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Single-workgroup permutation for small batches (P <= kSmallPairs).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_pair,
+                                                            int32_t* __restrict__ pair_pos,
+                                                            int32_t* __restrict__ header) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int tmp[1024];
+  __shared__ int s_e[1024];
+  __shared__ int err;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  if (tid == 0) err = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) {
+    const int e = idx[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    else atomicAdd(&err, 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) counts[e] = cnt[e];
+  const int total = block_exclusive_scan_lds(cnt, E, tmp);
+  for (int e = tid; e < E; e += 1024) offsets[e] = cnt[e];
+  if (tid == 0) {
+    offsets[E] = total;
+    header[0] = err;
+  }
+  __syncthreads();
+  // stable scatter, 1024 pairs at a time; cnt[e] is the running base
+  for (int p0 = 0; p0 < P; p0 += 1024) {
+    const int p = p0 + tid;
+    const int n = min(1024, P - p0);
+    int e = -1;
+    if (p < P) {
+      e = idx[p];
+      if (e < 0 || e >= E) e = -1;
+    }
+    s_e[tid] = e;
+    __syncthreads();
+    int before = 0, after = 0;
+    if (e >= 0) {
+      for (int j = 0; j < n; ++j) {
+        const int o = s_e[j];
+        before += (j < tid && o == e);
+        after += (j > tid && o == e);
+      }
+    }
+    int base = 0;
+    if (e >= 0) base = cnt[e];
+    __syncthreads();
+    if (e >= 0) {
+      const int pos = base + before;
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+      if (after == 0) cnt[e] = pos + 1;
+    } else if (p < P) {
+      pair_pos[p] = -1;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-workgroup permutation: per-chunk histograms, a column scan, and a
+// stable per-chunk scatter.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                          int32_t* __restrict__ chunk_hist) {
+  __shared__ int cnt[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int64_t p0 = int64_t(blockIdx.x) * kPermChunk;
+  for (int i = tid; i < kPermChunk; i += 256) {
+    const int64_t p = p0 + i;
+    if (p >= P) break;
+    const int e = idx[p];
+    atomicAdd(&cnt[(e >= 0 && e < E) ? e : E], 1);
+  }
+  __syncthreads();
+  int32_t* row = chunk_hist + int64_t(blockIdx.x) * (E + 1);
+  for (int e = tid; e <= E; e += 256) row[e] = cnt[e];
+}
+
+// Column scan of the per-chunk histograms: chunk_hist[c][e] becomes the
+// number of pairs of expert e in chunks before c.  Workgroup = 64 experts x
+// 16 chunk groups.  Column totals go to counts[e] (and, for the extra column
+// E of out-of-range ids, to the header).
+__global__ __launch_bounds__(1024) void permute_colscan_kernel(int32_t* __restrict__ chunk_hist, int n_chunks,
+                                                              int E, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ header) {
+  __shared__ int part[16][64];
+  const int col = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + col;
+  const int per = (n_chunks + 15) / 16;
+  const int c_lo = min(n_chunks, grp * per), c_hi = min(n_chunks, c_lo + per);
+  int s = 0;
+  if (e <= E)
+    for (int c = c_lo; c < c_hi; ++c) s += chunk_hist[int64_t(c) * (E + 1) + e];
+  part[grp][col] = s;
+  __syncthreads();
+  if (grp == 0) {
+    int run = 0;
+    for (int g = 0; g < 16; ++g) {
+      const int v = part[g][col];
+      part[g][col] = run;
+      run += v;
+    }
+    if (e < E) counts[e] = run;
+    else if (e == E) header[kHdrError] = run;
+  }
+  __syncthreads();
+  if (e <= E) {
+    int run = part[grp][col];
+    for (int c = c_lo; c < c_hi; ++c) {
+      int32_t* cell = chunk_hist + int64_t(c) * (E + 1) + e;
+      const int v = *cell;
+      *cell = run;
+      run += v;
+    }
+  }
+}
+
+// offsets = exclusive scan of counts (one workgroup).
+__global__ __launch_bounds__(1024) void offsets_scan_kernel(const int32_t* __restrict__ counts, int E,
+                                                           int32_t* __restrict__ offsets) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int tmp[1024];
+  for (int e = threadIdx.x; e < E; e += 1024) cnt[e] = counts[e];
+  __syncthreads();
+  const int total = block_exclusive_scan_lds(cnt, E, tmp);
+  for (int e = threadIdx.x; e < E; e += 1024) offsets[e] = cnt[e];
+  if (threadIdx.x == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                             const int32_t* __restrict__ chunk_hist,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_pair,
+                                                             int32_t* __restrict__ pair_pos) {
+  __shared__ int base[kMaxExperts];
+  __shared__ int s_e[256];
+  const int tid = threadIdx.x;
+  const int32_t* row = chunk_hist + int64_t(blockIdx.x) * (E + 1);
+  for (int e = tid; e < E; e += 256) base[e] = offsets[e] + row[e];
+  __syncthreads();
+  const int64_t c0 = int64_t(blockIdx.x) * kPermChunk;
+  for (int i0 = 0; i0 < kPermChunk; i0 += 256) {
+    const int64_t p = c0 + i0 + tid;
+    const int n = int(min<int64_t>(256, P - (c0 + i0)));
+    if (n <= 0) break;
+    int e = -1;
+    if (p < P) {
+      e = idx[p];
+      if (e < 0 || e >= E) e = -1;
+    }
+    s_e[tid] = e;
+    __syncthreads();
+    int before = 0, after = 0;
+    if (e >= 0) {
+      for (int j = 0; j < n; ++j) {
+        const int o = s_e[j];
+        before += (j < tid && o == e);
+        after += (j > tid && o == e);
+      }
+    }
+    int b = 0;
+    if (e >= 0) b = base[e];
+    __syncthreads();
+    if (e >= 0) {
+      const int pos = b + before;
+      sorted_pair[pos] = int32_t(p);
+      pair_pos[p] = pos;
+      if (after == 0) base[e] = pos + 1;
+    } else if (p < P) {
+      pair_pos[p] = -1;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, int32_t* header, int32_t* chunk_hist,
+                          hipStream_t stream) {
+  if (P <= kSmallPairs) {
+    permute_small_kernel<<<1, 1024, 0, stream>>>(idx, int(P), E, counts, offsets, sorted_pair, pair_pos,
+                                                 header);
+    return hipGetLastError();
+  }
+  const int n_chunks = int((P + kPermChunk - 1) / kPermChunk);
+  permute_hist_kernel<<<n_chunks, 256, 0, stream>>>(idx, P, E, chunk_hist);
+  permute_colscan_kernel<<<(E + 1 + 63) / 64, 1024, 0, stream>>>(chunk_hist, n_chunks, E, counts, header);
+  offsets_scan_kernel<<<1, 1024, 0, stream>>>(counts, E, offsets);
+  permute_scatter_kernel<<<n_chunks, 256, 0, stream>>>(idx, P, E, chunk_hist, offsets, sorted_pair, pair_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,122 @@
+// Block quantiser and dequantiser for the 2-bit / 3-bit expert format.
+//
+// Format: blocks of 32 weights along the reduction axis share one fp16 scale;
+// code c in [-2^(b-1), 2^(b-1)-1] stored offset-binary.  2-bit codes: byte
+// k/4, bits 2*(k%4).  3-bit codes: that low plane, then a high plane with bit
+// 2 of q in byte k/8 at bit k%8.  (The pages say experts are stored and read
+// at 2 bits -- "How Strata runs a 125-billion-parameter model ...", intro and
+// Step 1 byte table; the block layout is this library's own.)
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// One thread per 32-weight block.
+template <int QBITS>
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, int64_t rows,
+                                                      int cols, uint8_t* __restrict__ codes,
+                                                      uint16_t* __restrict__ scales) {
+  const int bpr = cols / kBlock;
+  const int64_t nblk = rows * bpr;
+  const int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  const int64_t r = b / bpr;
+  const int j = int(b - r * bpr);
+  const float4v* src = reinterpret_cast<const float4v*>(w + r * cols + int64_t(j) * kBlock);
+  float v[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock / 4; ++i) {
+    float4v t = src[i];
+    v[4 * i] = t[0]; v[4 * i + 1] = t[1]; v[4 * i + 2] = t[2]; v[4 * i + 3] = t[3];
+  }
+  // signed element of largest magnitude, first index on ties
+  float m = v[0];
+#pragma unroll
+  for (int i = 1; i < kBlock; ++i)
+    if (fabsf(v[i]) > fabsf(m)) m = v[i];
+  constexpr int off = 1 << (QBITS - 1);
+  constexpr float cmin = -float(off), cmax = float(off - 1);
+  const f16 d16 = f16(m / cmin);  // m / c_min is exact (power of two); RNE to fp16
+  const float d = float(d16);
+  uint32_t q[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock; ++i) {
+    float c = 0.0f;
+    if (d != 0.0f) c = fminf(fmaxf(__builtin_rintf(__fdiv_rn(v[i], d)), cmin), cmax);
+    q[i] = uint32_t(int(c) + off);
+  }
+  // a zero scale is stored as +0 whatever the sign of the largest element
+  scales[b] = d == 0.0f ? uint16_t(0) : __builtin_bit_cast(uint16_t, d16);
+  // low plane: 8 bytes per block
+  uint32_t lo0 = 0, lo1 = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    lo0 |= (q[i] & 3u) << (2 * i);
+    lo1 |= (q[16 + i] & 3u) << (2 * i);
+  }
+  uint2v* dst = reinterpret_cast<uint2v*>(codes + (r * cols + int64_t(j) * kBlock) / 4);
+  *dst = uint2v{lo0, lo1};
+  if constexpr (QBITS == 3) {
+    uint32_t hi = 0;
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) hi |= ((q[i] >> 2) & 1u) << i;
+    uint32_t* hdst = reinterpret_cast<uint32_t*>(codes + rows * cols / 4 + (r * cols + int64_t(j) * kBlock) / 8);
+    *hdst = hi;
+  }
+}
+
+// One thread per 32-weight block: out = (q - off) * scale, exact in fp32.
+template <int QBITS>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                     const uint16_t* __restrict__ scales,
+                                                     int64_t rows, int cols, float* __restrict__ out) {
+  const int bpr = cols / kBlock;
+  const int64_t nblk = rows * bpr;
+  const int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  const int64_t base = b * kBlock;  // == r * cols + j * 32
+  const uint2v lo = *reinterpret_cast<const uint2v*>(codes + base / 4);
+  uint32_t hi = 0;
+  if constexpr (QBITS == 3) hi = *reinterpret_cast<const uint32_t*>(codes + rows * cols / 4 + base / 8);
+  const float s = float(__builtin_bit_cast(f16, scales[b]));
+  constexpr int off = 1 << (QBITS - 1);
+  float4v* dst = reinterpret_cast<float4v*>(out + base);
+#pragma unroll
+  for (int i = 0; i < kBlock / 4; ++i) {
+    float4v t;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = 4 * i + u;
+      uint32_t q = ((k < 16 ? lo[0] : lo[1]) >> (2 * (k & 15))) & 3u;
+      if constexpr (QBITS == 3) q |= ((hi >> k) & 1u) << 2;
+      t[u] = float(int(q) - off) * s;
+    }
+    dst[i] = t;
+  }
+}
+
+hipError_t launch_quantize(const float* w, int64_t rows, int cols, int qbits, uint8_t* codes,
+                           uint16_t* scales, hipStream_t stream) {
+  const int64_t nblk = rows * (cols / kBlock);
+  if (nblk == 0) return hipSuccess;
+  const dim3 grid(unsigned((nblk + 255) / 256));
+  if (qbits == 2)
+    quantize_kernel<2><<<grid, 256, 0, stream>>>(w, rows, cols, codes, scales);
+  else
+    quantize_kernel<3><<<grid, 256, 0, stream>>>(w, rows, cols, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int cols,
+                          int qbits, float* out, hipStream_t stream) {
+  const int64_t nblk = rows * (cols / kBlock);
+  if (nblk == 0) return hipSuccess;
+  const dim3 grid(unsigned((nblk + 255) / 256));
+  if (qbits == 2)
+    dequant_kernel<2><<<grid, 256, 0, stream>>>(codes, scales, rows, cols, out);
+  else
+    dequant_kernel<3><<<grid, 256, 0, stream>>>(codes, scales, rows, cols, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,205 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer with
+ * 2-bit / 3-bit block-quantised experts.
+ *
+ * The layer (sources: "How Strata runs a 125-billion-parameter model on a
+ * single 12 GB to 24 GB graphics card", intro and Step 2; "Strata Open-Source
+ * Runtime: Running a 125B-Parameter Qwen3 Model on a 12GB GPU", section "The
+ * Model Itself: The Compute-Storage Gap in Sparse MoE"): for every token a
+ * router scores E experts and keeps the top k; the k selected experts and one
+ * always-on shared expert run; the finished expert vectors are summed on the
+ * GPU with the router weights.  The pages fix the counts (E = 512, k = 10,
+ * one shared expert, 48 layers) and that experts are read from 2-bit storage;
+ * the expert function (SwiGLU), the renormalised softmax and the block format
+ * below are the workload's own definition.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership  : every pointer argument is caller-owned memory.  Tensor
+ *              arguments are DEVICE pointers (hipMalloc'd or from a device
+ *              allocator); structs passed by pointer (moe_shape, moe_layer,
+ *              moe_options) are HOST memory read during the call only.  The
+ *              library never allocates device memory; scratch comes from the
+ *              caller's workspace.
+ * Streams    : `stream` is a hipStream_t passed as void* (NULL = the default
+ *              stream).  Every call is asynchronous on that stream and never
+ *              synchronises the host, except moe_read_error.
+ * Errors     : arguments are validated on the host before any HIP call; a
+ *              failed check returns a negative moe_status and launches
+ *              nothing.  A launch failure returns MOE_ERR_DEVICE.  C++
+ *              exceptions never cross this boundary.  moe_status_string()
+ *              names a status; moe_last_error_detail() gives a one-line
+ *              explanation of the last failure on the calling thread.
+ * T == 0     : is valid and launches nothing.
+ *
+ * Quantised block format (the pages give none; this is the workload's format
+ * with the bit layout chosen here).  For a matrix W of shape [rows][K] whose
+ * reduction axis is K (K a multiple of 32):
+ *   - blocks of 32 consecutive weights along K share one fp16 scale s;
+ *   - code c in [-2^(b-1), 2^(b-1)-1], weight = c * s, stored offset-binary
+ *     q = c + 2^(b-1);
+ *   - 2-bit codes: row-major [rows][K/4] bytes, weight k of a row in byte
+ *     k/4 at bits 2*(k%4)..2*(k%4)+1;
+ *   - 3-bit codes: a low plane laid out exactly like the 2-bit codes (low two
+ *     bits of q), followed by a high plane [rows][K/8] bytes holding bit 2 of
+ *     q for weight k in byte k/8 at bit k%8;
+ *   - scales: fp16 bit patterns, row-major [rows][K/32].
+ * Expert matrices: gate [I][H], up [I][H] (K = H) and down [H][I] (K = I).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid request this build does not handle */
+  MOE_ERR_WORKSPACE = -3,   /* workspace too small; see moe_last_required_workspace */
+  MOE_ERR_DEVICE = -4,      /* a HIP call or kernel launch failed */
+  MOE_ERR_INDEX = -5        /* an expert id outside [0, E) reached moe_permute */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Expert-FFN algorithm.  GEMV: fused dequant-GEMV for few tokens per expert
+ * (decode).  GROUPED: dequantise tiles into LDS and run a grouped MFMA GEMM
+ * (prefill).  AUTO picks GEMV when T <= 16, else GROUPED.  Both compute the
+ * same function. */
+typedef enum { MOE_ALGO_AUTO = 0, MOE_ALGO_GEMV = 1, MOE_ALGO_GROUPED = 2 } moe_algo;
+
+typedef struct {
+  int32_t hidden;       /* H: model width, multiple of 32 */
+  int32_t inter;        /* I: routed expert intermediate size, multiple of 32 */
+  int32_t n_experts;    /* E: routed experts, 1..4096 */
+  int32_t top_k;        /* k: experts per token, 1..min(E, 32) */
+  int32_t shared_inter; /* shared expert intermediate size (multiple of 32), 0 = none */
+  int32_t qbits;        /* 2 or 3 */
+} moe_shape;
+
+/* Quantised weights of a set of experts.  Matrix m (0 = gate, 1 = up,
+ * 2 = down) of expert e starts at codes[m] + e * code_stride bytes, and its
+ * scales at scales[m] + e * scale_stride fp16 elements.  codes[m] and
+ * code_stride must be multiples of 16 bytes; scales[m] must be 4-byte aligned
+ * and scale_stride even. */
+typedef struct {
+  const uint8_t* codes[3];
+  const uint16_t* scales[3];
+  int64_t code_stride;
+  int64_t scale_stride;
+} moe_qweights;
+
+typedef struct {
+  const void* w_router;     /* [E][H] router weights, row-major, dtype router_dtype */
+  moe_dtype router_dtype;   /* MOE_F32 or MOE_BF16 */
+  const float* router_bias; /* [E] fp32, or NULL for no bias */
+  moe_qweights experts;     /* E routed experts, inter = shape.inter */
+  moe_qweights shared;      /* one expert (index 0), inter = shape.shared_inter;
+                               ignored when shared_inter == 0 */
+} moe_layer;
+
+typedef struct {
+  moe_algo ffn_algo;
+  int32_t flags; /* reserved, must be 0 */
+} moe_options;
+
+/* Bytes of workspace moe_layer_forward needs for T tokens (also enough for
+ * moe_route, moe_permute and moe_expert_ffn at the same T).  Returns 0 for an
+ * invalid shape. */
+size_t moe_workspace_bytes(const moe_shape* shape, int64_t T, const moe_options* opts);
+
+/* Router (page 1, Step 2, "Mapped host doorbell and a single captured CUDA
+ * graph": the router picks the experts of each layer on the GPU).
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h] + bias[e]   (fp32 accumulate)
+ *   topk_idx[t][j] = the k largest logits of token t, descending; ties go to
+ *                    the lower expert index
+ *   topk_w[t][j]   = softmax over the selected logits (= softmax over all E
+ *                    renormalised over the selection); weights sum to 1.
+ * x [T][H] (dtype x_dtype), logits [T][E] fp32 or NULL (then the workspace
+ * holds them), topk_idx [T][k] int32, topk_w [T][k] fp32. */
+int moe_route(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer,
+              const moe_shape* shape, float* logits, int32_t* topk_idx, float* topk_w,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Token-to-expert permutation (the analogue of the partition of a layer's
+ * selected experts, page 1, Step 2, "Mapped host doorbell ...").  Pair
+ * p = t*k + j.  Outputs: counts [E], offsets [E+1] (exclusive scan of counts),
+ * sorted_pair [T*k] (pairs grouped by expert, ascending p inside a group) and
+ * pair_pos [T*k] (inverse: sorted_pair[pair_pos[p]] == p).  Expert ids outside
+ * [0, E) are skipped (never written out of bounds) and recorded in the
+ * workspace; moe_read_error then returns MOE_ERR_INDEX. */
+int moe_permute(const int32_t* topk_idx, int64_t T, const moe_shape* shape, int32_t* counts,
+                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Routed and shared expert FFN read directly from the quantised weights
+ * (page 1 intro and Step 1: the experts are computed from their 2-bit
+ * storage).  For every sorted position s with pair p = sorted_pair[s] in
+ * expert e's segment [offsets[e], offsets[e+1]):
+ *   y_sorted[s] = W_down_e (silu(W_gate_e x_t) * (W_up_e x_t)),  t = p / k
+ * and, when shared_inter > 0 and shared_out != NULL, for every token t:
+ *   shared_out[t] = the same function with the shared expert's weights.
+ * x [T][H]; y_sorted [T*k][H] fp32; shared_out [T][H] fp32 or NULL. */
+int moe_expert_ffn(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer,
+                   const moe_shape* shape, const int32_t* offsets, const int32_t* sorted_pair,
+                   float* y_sorted, float* shared_out, const moe_options* opts, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Weighted combine (page 1, Step 2, "Dynamic PCIe and CPU co-execution": the
+ * GPU sums the finished expert vectors):
+ *   out[t] = shared_out[t] + sum_j topk_w[t][j] * y_sorted[pair_pos[t*k+j]]
+ * (j ascending; shared_out may be NULL).  Optional stack glue for stacked
+ * layers: if residual != NULL then residual[t] += out[t]; if also
+ * next_in_bf16 != NULL then next_in_bf16[t] = bf16_RNE(r / sqrt(mean(r^2) +
+ * 1e-6)) with r the updated residual row.  out [T][H] fp32 (may be NULL when
+ * residual is given). */
+int moe_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                const float* shared_out, int64_t T, const moe_shape* shape, float* out,
+                float* residual, uint16_t* next_in_bf16, void* stream);
+
+/* The whole layer: route, permute, expert FFN, shared expert and combine in
+ * one call, with the optional stack glue of moe_combine.  topk_idx / topk_w
+ * may be NULL (then the workspace holds them). */
+int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer,
+                      const moe_shape* shape, float* out, float* residual,
+                      uint16_t* next_in_bf16, int32_t* topk_idx, float* topk_w,
+                      const moe_options* opts, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* a[t] = bf16_RNE(r[t] / sqrt(mean(r[t]^2) + 1e-6)) for r [T][H] fp32 (the
+ * input of the first layer of a stack). */
+int moe_rmsnorm_bf16(const float* r, int64_t T, int32_t H, uint16_t* a, void* stream);
+
+/* out[r][k] = (q - 2^(b-1)) * scale[r][k/32] in fp32 (exact) for one matrix
+ * [rows][cols] in the block format above. */
+int moe_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int32_t cols,
+                int32_t qbits, float* out, void* stream);
+
+/* Quantise fp32 w [rows][cols] to the block format (used to build synthetic
+ * expert arenas).  Per block: m = signed element of largest magnitude (first
+ * on ties), d = fp16_RNE(m / c_min), c = clamp(rint_half_even(w / d), c_min,
+ * c_max), c = 0 for the whole block when d == 0 (then d is stored as +0);
+ * all in fp32. */
+int moe_quantize(const float* w, int64_t rows, int32_t cols, int32_t qbits, uint8_t* codes,
+                 uint16_t* scales, void* stream);
+
+/* Synchronises `stream`, then returns MOE_ERR_INDEX if the most recent
+ * moe_permute (or moe_layer_forward) on this workspace met an expert id
+ * outside [0, E), else MOE_OK; clears the record.  The only call that waits
+ * for the device. */
+int moe_read_error(void* workspace, size_t workspace_bytes, void* stream);
+
+const char* moe_status_string(int status);
+const char* moe_last_error_detail(void);
+/* Set when a call returns MOE_ERR_WORKSPACE: the bytes that call needed. */
+size_t moe_last_required_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

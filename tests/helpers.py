@@ -1,0 +1,123 @@
+"""Shared helpers of the test suite: building device layers from the seeded
+synthetic inputs, the matching oracle layers, and the parity metrics."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from bit_quantized_expert_amd import synth
+from oracle import moe_oracle as O
+
+REL_L2 = 1e-3          # output: relative L2 error bound
+MAX_ABS_RMS = 1e-2     # output: max abs error <= MAX_ABS_RMS * rms(reference)
+LOGIT_ABS = 1e-4       # router logits: max abs error vs float64
+TIE_TAU = 1e-4         # near-tie band for index disagreements
+
+
+def rel_l2(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+
+
+def assert_close_output(got, want, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    r = rel_l2(got, want)
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    mx = float(np.max(np.abs(got - want))) if want.size else 0.0
+    assert r <= REL_L2, f"{what}: relL2 {r:.3e} > {REL_L2}"
+    assert mx <= MAX_ABS_RMS * rms + 1e-30, f"{what}: max abs {mx:.3e} > {MAX_ABS_RMS} * rms {rms:.3e}"
+    return r, mx / max(rms, 1e-300)
+
+
+class DeviceLayer:
+    """One layer of a workload on the GPU (quantised with the library's
+    moe_quantize) plus lazily built oracle experts (quantised by the oracle
+    from the same fp32 draws)."""
+
+    def __init__(self, wl: synth.Workload, layer: int = 0, device="cuda"):
+        from bit_quantized_expert_amd import QArena, QLayer
+        self.wl, self.layer, self.s = wl, layer, wl.shape
+        s = self.s
+        self.w_router, self.bias = synth.router(wl, layer, device)
+        self.gate, self.up, self.down = synth.expert_weights(wl, layer, device)
+        arena = QArena(s.n_experts, s.hidden, s.inter, s.qbits, device)
+        for m, w in enumerate((self.gate, self.up, self.down)):
+            arena.quantize_from(m, w)
+        self.sw = synth.shared_weights(wl, layer, device)
+        sarena = None
+        if self.sw is not None:
+            sarena = QArena(1, s.hidden, s.shared_inter, s.qbits, device)
+            for m, w in enumerate(self.sw):
+                sarena.quantize_from(m, w[None])
+        self.q = QLayer(self.w_router, self.bias, arena, sarena)
+        self._oracle_experts = {}
+        self._oracle_shared = None
+
+    # ---- oracle side
+    def oracle_expert(self, e: int) -> O.QExpert:
+        if e not in self._oracle_experts:
+            self._oracle_experts[e] = O.QExpert.from_float(
+                self.gate[e].cpu().numpy(), self.up[e].cpu().numpy(), self.down[e].cpu().numpy(), self.s.qbits)
+        return self._oracle_experts[e]
+
+    def oracle_shared(self):
+        if self.sw is None:
+            return None
+        if self._oracle_shared is None:
+            self._oracle_shared = O.QExpert.from_float(*(w.cpu().numpy() for w in self.sw), self.s.qbits)
+        return self._oracle_shared
+
+    def oracle_router(self):
+        w = self.w_router.float().cpu().numpy().astype(np.float64)
+        b = None if self.bias is None else self.bias.cpu().numpy().astype(np.float64)
+        return w, b
+
+    class _Lazy:
+        def __init__(self, dl):
+            self.dl = dl
+
+        def __len__(self):
+            return self.dl.s.n_experts
+
+        def __getitem__(self, e):
+            return self.dl.oracle_expert(int(e))
+
+    def oracle_experts(self):
+        return DeviceLayer._Lazy(self)
+
+    def oracle_forward(self, x_np, idx=None, return_all=False):
+        w, b = self.oracle_router()
+        return O.layer_forward(x_np, w, b, self.oracle_experts(), self.oracle_shared(), self.s.top_k,
+                               return_all=return_all, idx=idx)
+
+
+def x_to_numpy(x: torch.Tensor) -> np.ndarray:
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def check_route_protocol(gpu_logits, gpu_idx, gpu_w, oracle_logits, k):
+    """Near-tie protocol for the router.  Returns the tokens whose GPU
+    selection differs from the oracle's (all within the tie band)."""
+    gl = np.asarray(gpu_logits, dtype=np.float64)
+    gi = np.asarray(gpu_idx)
+    ol = np.asarray(oracle_logits, dtype=np.float64)
+    # (i) logits
+    assert np.max(np.abs(gl - ol)) <= LOGIT_ABS, f"logits max abs {np.max(np.abs(gl - ol)):.3e}"
+    # (ii) the selection rule applied to the GPU's own logits gives the GPU's indices exactly
+    assert np.array_equal(O.topk_select(gl, k), gi), "GPU top-k differs from the rule on its own logits"
+    # weights: softmax over the selected GPU logits (fp32 arithmetic), sum to 1
+    want_w = O.topk_weights(gl, gi)
+    assert np.max(np.abs(np.asarray(gpu_w) - want_w)) <= 2e-6
+    assert np.max(np.abs(np.asarray(gpu_w).sum(1) - 1)) <= 2e-6
+    # (iii) disagreements with the oracle's own selection only inside the tie band
+    oi = O.topk_select(ol, k)
+    flagged = np.where(np.any(oi != gi, axis=1))[0]
+    for t in flagged:
+        gap = np.abs(ol[t, gi[t]] - ol[t, oi[t]])
+        assert np.all(gap <= TIE_TAU), f"token {t}: index swap outside the tie band (gap {gap.max():.3e})"
+    return flagged

@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+the header declares, and rejects bad arguments before any HIP call (these
+tests run without a GPU)."""
+
+import ctypes
+import os
+
+import pytest
+
+from bit_quantized_expert_amd import _lib as L
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libmoe.so not built")
+
+
+def _shape(**kw):
+    d = dict(hidden=2048, inter=704, n_experts=512, top_k=10, shared_inter=704, qbits=2)
+    d.update(kw)
+    return L.Shape(**d)
+
+
+def test_exports_every_header_symbol():
+    lib = L.lib()
+    names = L.header_symbols()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, name in [(0, "MOE_OK"), (-1, "MOE_ERR_INVALID_ARG"), (-2, "MOE_ERR_UNSUPPORTED"),
+                       (-3, "MOE_ERR_WORKSPACE"), (-4, "MOE_ERR_DEVICE"), (-5, "MOE_ERR_INDEX")]:
+        assert L.status_string(code) == name
+
+
+def test_workspace_bytes_and_bad_shapes():
+    lib = L.lib()
+    opts = L.Options(0, 0)
+    n1 = lib.moe_workspace_bytes(ctypes.byref(_shape()), 1, ctypes.byref(opts))
+    n16 = lib.moe_workspace_bytes(ctypes.byref(_shape()), 16, ctypes.byref(opts))
+    assert 0 < n1 < n16
+    # the workspace holds at least the sorted expert outputs (P x H fp32)
+    assert n16 >= 16 * 10 * 2048 * 4
+    for bad in [dict(hidden=100), dict(inter=0), dict(n_experts=0), dict(n_experts=5000), dict(top_k=0),
+                dict(top_k=33), dict(qbits=4), dict(shared_inter=48)]:
+        assert lib.moe_workspace_bytes(ctypes.byref(_shape(**bad)), 4, ctypes.byref(opts)) == 0, bad
+    assert lib.moe_workspace_bytes(ctypes.byref(_shape()), -1, None) == 0
+
+
+def _layer_struct():
+    lay = L.Layer()
+    lay.w_router = 0x10000
+    lay.router_dtype = 1
+    for q in (lay.experts, lay.shared):
+        for m in range(3):
+            q.codes[m] = 0x20000 + 0x1000 * m
+            q.scales[m] = 0x40000 + 0x1000 * m
+        q.code_stride = 1_351_680 // 3
+        q.scale_stride = 45056
+    return lay
+
+
+def test_validation_before_any_device_call():
+    lib = L.lib()
+    s = _shape()
+    lay = _layer_struct()
+    fake = ctypes.c_void_p(0x100000)
+    # NULL x
+    assert lib.moe_layer_forward(None, 1, 4, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None, None,
+                                 None, fake, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    # unsupported qbits
+    s4 = _shape(qbits=4)
+    assert lib.moe_layer_forward(fake, 1, 4, ctypes.byref(lay), ctypes.byref(s4), fake, None, None, None, None,
+                                 None, fake, 1 << 40, None) == L.MOE_ERR_UNSUPPORTED
+    # misaligned expert codes
+    bad = _layer_struct()
+    bad.experts.codes[1] = 0x20008
+    assert lib.moe_layer_forward(fake, 1, 4, ctypes.byref(bad), ctypes.byref(s), fake, None, None, None, None,
+                                 None, fake, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    assert "16-byte" in L.last_error_detail()
+    # workspace too small: reports the bytes needed
+    need = lib.moe_workspace_bytes(ctypes.byref(s), 4, None)
+    st = lib.moe_layer_forward(fake, 1, 4, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None, None,
+                               None, fake, 1024, None)
+    assert st == L.MOE_ERR_WORKSPACE
+    assert L.last_required_workspace() == need
+    assert "MiB short" in L.last_error_detail()
+    # bad options
+    o = L.Options(7, 0)
+    assert lib.moe_layer_forward(fake, 1, 4, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None, None,
+                                 ctypes.byref(o), fake, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    # next_in without residual
+    assert lib.moe_combine(fake, fake, fake, None, 4, ctypes.byref(s), fake, None, fake, None) \
+        == L.MOE_ERR_INVALID_ARG
+    # T == 0 is a valid no-op
+    assert lib.moe_layer_forward(fake, 1, 0, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None, None,
+                                 None, None, 0, None) == L.MOE_OK
+    assert lib.moe_quantize(None, 0, 64, 2, None, None, None) == L.MOE_OK
+    # quantize/dequant argument checks
+    assert lib.moe_quantize(fake, 4, 48, 2, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_dequant(fake, fake, 4, 64, 5, fake, None) == L.MOE_ERR_UNSUPPORTED
+    # permute with a too-small workspace
+    assert lib.moe_permute(fake, 4096, ctypes.byref(s), fake, fake, fake, fake, fake, 16, None) \
+        == L.MOE_ERR_WORKSPACE
+    assert lib.moe_read_error(None, 0, None) == L.MOE_ERR_INVALID_ARG

@@ -1,0 +1,136 @@
+"""GPU parity of the single-step kernels against the CPU oracle: quantiser
+and dequantiser (bit-exact), router (near-tie protocol), permutation
+(bit-exact)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from bit_quantized_expert_amd import synth
+from tests.helpers import check_route_protocol
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import bit_quantized_expert_amd as M
+    M.lib()
+    return M
+
+
+def _weights(rows, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    w = torch.randn(rows, k, generator=g) * 0.02
+    w[0, :32] = 0.0                       # an all-zero block
+    w[1, 0:32] = 0.01 * torch.tensor([1.0, -1.0] * 16)   # equal magnitudes: first index wins
+    w[min(2, rows - 1), 5] = 0.5          # an outlier
+    return w
+
+
+@pytest.mark.parametrize("qbits", [2, 3])
+@pytest.mark.parametrize("rows,k", [(3, 32), (17, 64), (40, 96), (64, 704), (33, 2048)])
+def test_quantize_and_dequant_bit_exact(qbits, rows, k):
+    M = _lib()
+    w = _weights(rows, k, seed=rows * 1000 + k)
+    codes = torch.empty(rows * k * qbits // 8, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(rows * k // 32, dtype=torch.int16, device="cuda")
+    M.quantize(w.cuda(), qbits, codes, scales)
+    want_codes, want_scales = O.quantize(w.numpy(), qbits)
+    assert np.array_equal(codes.cpu().numpy(), want_codes)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16).reshape(rows, k // 32), want_scales)
+    out = torch.empty(rows, k, dtype=torch.float32, device="cuda")
+    M.dequant(codes, scales, rows, k, qbits, out)
+    want = O.dequant(want_codes, want_scales, rows, k, qbits)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
+
+
+def _route(M, wl, T, layer=0):
+    s = wl.shape
+    w_r, bias = synth.router(wl, layer, "cuda")
+    x = synth.tokens(wl, "cuda", layer=layer, n_tokens=T)
+    arena = M.QArena(1, 64, 32, 2, "cuda")  # experts are not read by the router
+    q = M.QLayer(w_r, bias, arena, None)
+    logits = torch.empty(T, s.n_experts, device="cuda")
+    idx = torch.empty(T, s.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, s.top_k, device="cuda")
+    M.route(x, q, s, idx, w, logits=logits)
+    torch.cuda.synchronize()
+    ol = O.router_logits(x.float().cpu().numpy().astype(np.float64), w_r.float().cpu().numpy().astype(np.float64),
+                         None if bias is None else bias.cpu().numpy().astype(np.float64))
+    return logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), ol
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode1", 1), ("decode16", 16), ("decode16", 333)])
+def test_route_protocol(name, T):
+    M = _lib()
+    wl = synth.WORKLOADS[name]
+    gl, gi, gw, ol = _route(M, wl, T)
+    flagged = check_route_protocol(gl, gi, gw, ol, wl.shape.top_k)
+    assert len(flagged) <= max(1, T // 100)
+
+
+def test_route_all_equal_logits_tie_rule():
+    """Zero router weights and no bias: every logit ties, so the selection is
+    experts 0..k-1 with weight 1/k."""
+    M = _lib()
+    wl = synth.custom("ties", 64, 32, 40, 7, 0, 2, 9, seed=5, act_dtype=torch.bfloat16)
+    arena = M.QArena(1, 64, 32, 2, "cuda")
+    q = M.QLayer(torch.zeros(40, 64, dtype=torch.bfloat16, device="cuda"), None, arena, None)
+    x = synth.tokens(wl, "cuda")
+    idx = torch.empty(9, 7, dtype=torch.int32, device="cuda")
+    w = torch.empty(9, 7, device="cuda")
+    M.route(x, q, wl.shape, idx, w, ws=M.alloc_workspace(wl.shape, 9))
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(7), (9, 1)))
+    assert np.allclose(w.cpu().numpy(), 1 / 7, rtol=0, atol=1e-7)
+
+
+def _permute(M, idx_np, E, k):
+    T = idx_np.shape[0]
+    s = synth.MoEShape(64, 32, E, k, 0, 2)
+    ws = M.alloc_workspace(s, T)
+    idx = torch.from_numpy(idx_np.astype(np.int32)).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    M.permute(idx, T, s, counts, offsets, sp, pp, ws)
+    return ws, counts.cpu().numpy(), offsets.cpu().numpy(), sp.cpu().numpy(), pp.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,k,skew", [(1, 512, 10, 0), (16, 512, 10, 1), (37, 9, 3, 0), (204, 512, 10, 1),
+                                        (205, 512, 10, 1), (3000, 512, 10, 1), (32768, 512, 10, 1),
+                                        (4096, 512, 10, 0), (500, 1, 1, 0)])
+def test_permute_bit_exact(T, E, k, skew):
+    M = _lib()
+    rng = np.random.default_rng(T * 7 + E)
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p = p / p.sum()
+        idx = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(min(T, 2000))])
+        idx = np.concatenate([idx] * (T // len(idx) + 1))[:T]
+    else:
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    _, counts, offsets, sp, pp = _permute(M, idx, E, k)
+    wc, wo, wsp, wpp = O.permute(idx, E)
+    assert np.array_equal(counts, wc)
+    assert np.array_equal(offsets, wo)
+    assert np.array_equal(sp, wsp)
+    assert np.array_equal(pp, wpp)
+
+
+@pytest.mark.parametrize("T", [5, 3000])
+def test_permute_out_of_range_ids_are_reported(T):
+    M = _lib()
+    E, k = 16, 2
+    rng = np.random.default_rng(3)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    idx[1, 0] = E          # out of range
+    idx[2, 1] = -1         # out of range
+    ws, counts, offsets, sp, pp = _permute(M, idx, E, k)
+    assert counts.sum() == T * k - 2
+    assert pp[1 * k + 0] == -1 and pp[2 * k + 1] == -1
+    with pytest.raises(M.MoeError) as ei:
+        M.read_error(ws)
+    assert ei.value.status == -5
+    M.read_error(ws)  # cleared

@@ -1,0 +1,137 @@
+"""GPU parity of the expert FFN and the whole layer against the CPU oracle,
+on the tiny and full decode shapes and on ragged shapes."""
+
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_expert_amd import synth
+from tests.helpers import DeviceLayer, assert_close_output, check_route_protocol, x_to_numpy
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _layer(wl, layer=0):
+    key = (wl, layer)
+    if key not in _CACHE:
+        _CACHE.clear()
+        torch.cuda.empty_cache()
+        _CACHE[key] = DeviceLayer(wl, layer)
+    return _CACHE[key]
+
+
+def _run_layer(M, dl, x, algo="auto"):
+    s = dl.s
+    T = x.shape[0]
+    ws = M.alloc_workspace(s, T, algo=algo)
+    out = torch.empty(T, s.hidden, device="cuda")
+    idx = torch.empty(T, s.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, s.top_k, device="cuda")
+    M.layer_forward(x, dl.q, s, out=out, topk_idx=idx, topk_w=w, algo=algo, ws=ws)
+    logits = torch.empty(T, s.n_experts, device="cuda")
+    idx2 = torch.empty_like(idx)
+    w2 = torch.empty_like(w)
+    M.route(x, dl.q, s, idx2, w2, logits=logits)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(w, w2)
+    return out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), logits.cpu().numpy()
+
+
+def _check_layer(M, dl, x, algo="auto"):
+    out, idx, w, logits = _run_layer(M, dl, x, algo)
+    xn = x_to_numpy(x)
+    ref = dl.oracle_forward(xn, idx=idx, return_all=True)
+    check_route_protocol(logits, idx, w, ref["logits"], dl.s.top_k)
+    return assert_close_output(out, ref["out"], f"{dl.wl.name} T={x.shape[0]} {algo}")
+
+
+def _M():
+    import bit_quantized_expert_amd as M
+    M.lib()
+    return M
+
+
+RAGGED = [
+    # name, H, I, E, k, Is, qbits, T, dtype
+    ("r1", 96, 96, 5, 3, 64, 2, 37, torch.bfloat16),
+    ("r2", 96, 96, 5, 3, 64, 3, 37, torch.float32),
+    ("r3", 128, 160, 12, 4, 0, 2, 21, torch.bfloat16),
+    ("r4", 64, 32, 8, 2, 32, 3, 4, torch.float32),
+    ("r5", 256, 192, 33, 8, 96, 3, 17, torch.bfloat16),
+]
+
+
+def test_tiny_layer():
+    M = _M()
+    dl = _layer(synth.WORKLOADS["tiny"])
+    x = synth.tokens(dl.wl, "cuda")
+    _check_layer(M, dl, x, "gemv")
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+def test_ragged_layer(case):
+    M = _M()
+    name, H, I, E, k, Is, qb, T, dt = case
+    wl = synth.custom(name, H, I, E, k, Is, qb, T, seed=11, act_dtype=dt, zipf_bias=True)
+    dl = _layer(wl)
+    x = synth.tokens(wl, "cuda")
+    _check_layer(M, dl, x, "gemv")
+
+
+def test_decode1_full_shape():
+    M = _M()
+    dl = _layer(synth.WORKLOADS["decode1"])
+    for seed_layer in range(3):
+        x = synth.tokens(dl.wl, "cuda", layer=seed_layer)
+        _check_layer(M, dl, x, "gemv")
+
+
+def test_decode16_layer_and_batch_invariance():
+    M = _M()
+    wl = synth.WORKLOADS["decode16"]
+    dl = _layer(wl, layer=0)
+    x = synth.tokens(wl, "cuda")
+    _check_layer(M, dl, x, "gemv")
+    out_all, idx_all, _, _ = _run_layer(M, dl, x)
+    for t in (0, 7, 15):
+        out_t, idx_t, _, _ = _run_layer(M, dl, x[t:t + 1].contiguous())
+        assert np.array_equal(idx_t[0], idx_all[t])
+        assert np.array_equal(out_t[0], out_all[t]), f"token {t} depends on the rest of the batch"
+
+
+def test_stepwise_api_matches_layer_forward():
+    M = _M()
+    dl = _layer(synth.WORKLOADS["tiny"])
+    s = dl.s
+    x = synth.tokens(dl.wl, "cuda")
+    T = x.shape[0]
+    ws = M.alloc_workspace(s, T)
+    idx = torch.empty(T, s.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, s.top_k, device="cuda")
+    M.route(x, dl.q, s, idx, w, ws=ws)
+    counts = torch.empty(s.n_experts, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(s.n_experts + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * s.top_k, dtype=torch.int32, device="cuda")
+    pp = torch.empty_like(sp)
+    M.permute(idx, T, s, counts, offsets, sp, pp, ws)
+    y = torch.empty(T * s.top_k, s.hidden, device="cuda")
+    so = torch.empty(T, s.hidden, device="cuda")
+    M.expert_ffn(x, dl.q, s, offsets, sp, y, so, ws=ws)
+    out = torch.empty(T, s.hidden, device="cuda")
+    M.combine(y, pp, w, so, T, s, out=out)
+    out2, _, _, _ = _run_layer(M, dl, x)
+    assert np.array_equal(out.cpu().numpy(), out2)
+    # y_sorted and shared_out individually against the oracle
+    ref = dl.oracle_forward(x_to_numpy(x), idx=idx.cpu().numpy(), return_all=True)
+    assert_close_output(y.cpu().numpy(), ref["y"], "y_sorted")
+    assert_close_output(so.cpu().numpy(), ref["shared"], "shared_out")
+
+
+def test_zero_tokens_is_a_noop():
+    M = _M()
+    dl = _layer(synth.WORKLOADS["tiny"])
+    x = torch.empty(0, dl.s.hidden, device="cuda")
+    out = torch.empty(0, dl.s.hidden, device="cuda")
+    M.layer_forward(x, dl.q, dl.s, out=out, ws=None)
