@@ -70,12 +70,39 @@ def build_layers(wl, n_layers, device, log):
     return layers
 
 
-class Step:
-    """One pass of the layer through the C ABI in its four steps (the same
-    kernels moe_layer_forward runs), with HIP events around the expert FFN."""
+class DecodeSteps:
+    """G consecutive single-token steps, step i = layer i of the resident
+    stack with its own token, through moe_layer_forward (the fused decode
+    layer: router GEMV, selection, gate/up GEMV, down GEMV + combine).
+    Captured once in a HIP graph so the host launches nothing per step."""
 
-    def __init__(self, s, T, device):
-        self.s, self.T = s, T
+    def __init__(self, s, layers, xs, device):
+        self.s, self.layers, self.xs = s, layers, xs
+        self.ws = M.alloc_workspace(s, 1, device=device)
+        self.out = torch.empty(len(xs), 1, s.hidden, device=device)
+        self.graph = None
+
+    def eager(self):
+        for i, (layer, x) in enumerate(zip(self.layers, self.xs)):
+            M.layer_forward(x, layer, self.s, out=self.out[i], ws=self.ws)
+
+    def capture(self):
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.eager()
+
+    def replay(self):
+        self.graph.replay()
+
+
+class FfnState:
+    """Inputs of moe_expert_ffn for one token-batch on one layer: routing,
+    permutation and a workspace holding the slot table and activations."""
+
+    def __init__(self, s, T, device, shape=None):
+        self.s = shape or s
+        s = self.s
+        self.T = T
         P = T * s.top_k
         self.ws = M.alloc_workspace(s, T, device=device)
         self.idx = torch.empty(T, s.top_k, dtype=torch.int32, device=device)
@@ -86,23 +113,60 @@ class Step:
         self.pp = torch.empty(P, dtype=torch.int32, device=device)
         self.y = torch.empty(P, s.hidden, device=device)
         self.so = torch.empty(T, s.hidden, device=device)
-        self.out = torch.empty(T, s.hidden, device=device)
 
-    def __call__(self, x, layer, ev=None, residual=None, next_in=None):
-        s, T = self.s, self.T
-        M.route(x, layer, s, self.idx, self.w, ws=self.ws)
-        M.permute(self.idx, T, s, self.counts, self.offsets, self.sp, self.pp, self.ws)
-        if ev is not None:
-            ev[0].record()
-        M.expert_ffn(x, layer, s, self.offsets, self.sp, self.y, self.so, algo="gemv", ws=self.ws)
-        if ev is not None:
-            ev[1].record()
-        M.combine(self.y, self.pp, self.w, self.so, T, s, out=self.out if residual is None else None,
-                  residual=residual, next_in=next_in)
+    def prepare(self, x, layer):
+        M.route(x, layer, self.s, self.idx, self.w, ws=self.ws)
+        M.permute(self.idx, self.T, self.s, self.counts, self.offsets, self.sp, self.pp, self.ws)
+        self.run(x, layer, 0)
+
+    def run(self, x, layer, flags):
+        M.expert_ffn(x, layer, self.s, self.offsets, self.sp, self.y, self.so, algo="gemv", ws=self.ws,
+                     flags=flags)
 
 
-def unique_experts(step: Step) -> int:
-    return int((step.counts > 0).sum().item())
+def time_phase(states, xs, layers, skip, reps):
+    """Average duration (ms) of one projection kernel launched alone through
+    moe_expert_ffn(REUSE_PLAN | skip), HIP events on the launching stream,
+    walking the layers in turn."""
+    flags = M.FFN_REUSE_PLAN | skip
+    evs = []
+    for _ in range(reps):
+        for st, x, layer in zip(states, xs, layers):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            st.run(x, layer, flags)
+            b.record()
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def probe_gemv(s, layers, dev, log):
+    """Gate/up and down GEMV kernels over every expert of a layer: 16 tokens,
+    32 experts each, routed so that each of the 512 experts gets exactly one
+    (token, rank) pair."""
+    import dataclasses
+    ps = dataclasses.replace(s, top_k=32)
+    T = s.n_experts // 32
+    xs = synth.tokens(synth.WORKLOADS["decode16"], dev, layer=777, n_tokens=T)
+    sts = []
+    n = min(8, len(layers))
+    for l in range(n):
+        st = FfnState(s, T, dev, shape=ps)
+        st.offsets.copy_(torch.arange(s.n_experts + 1, dtype=torch.int32, device=dev))
+        st.sp.copy_(torch.arange(s.n_experts, dtype=torch.int32, device=dev))
+        st.run(xs, layers[l], 0)
+        sts.append(st)
+    torch.cuda.synchronize()
+    gu = time_phase(sts, [xs] * n, layers[:n], M.FFN_SKIP_DOWN, reps=3)
+    dn = time_phase(sts, [xs] * n, layers[:n], M.FFN_SKIP_GATEUP, reps=3)
+    gu_b = (s.n_experts * expert_bytes(s) + shared_bytes(s)) * 2 // 3
+    dn_b = (s.n_experts * expert_bytes(s) + shared_bytes(s)) // 3
+    log(f"probe: gate/up {gu * 1e3:.1f} us {gu_b / gu / 1e6:.0f} GB/s; down {dn * 1e3:.1f} us {dn_b / dn / 1e6:.0f} GB/s")
+    return {"what": "gate/up and down GEMV kernels alone over all 512 experts + shared of a layer "
+                    "(16 tokens x 32 experts, one pair per expert)",
+            "gateup": {"avg_us": gu * 1e3, "bytes": gu_b, "GBs": gu_b / gu / 1e6, "frac": gu_b / gu / 1e6 / HBM_PEAK_GBS},
+            "down": {"avg_us": dn * 1e3, "bytes": dn_b, "GBs": dn_b / dn / 1e6, "frac": dn_b / dn / 1e6 / HBM_PEAK_GBS}}
 
 
 def cpu_baseline(wl, layers_fp_seed, xs, n_sample, log):
@@ -178,67 +242,108 @@ def main():
     wl = synth.WORKLOADS["decode1"]
     s = wl.shape
     layers = build_layers(wl, args.layers, dev, log)
-    n_tot = args.warmup + args.steps
-    xs = [synth.tokens(wl, dev, layer=i, n_tokens=1) for i in range(n_tot)]
-    step = Step(s, 1, dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-
-    for i in range(args.warmup):
-        step(xs[i], layers[i % args.layers])
+    L = args.layers
+    replays = max(1, args.steps // L)
+    steps = replays * L
+    xs = [synth.tokens(wl, dev, layer=i, n_tokens=1) for i in range(L)]
+    dec = DecodeSteps(s, layers, xs, dev)
+    dec.eager()
     torch.cuda.synchronize()
-    uniq = []
+    eager_out = dec.out.clone()
+    dec.capture()
+    for _ in range(max(1, args.warmup // L)):
+        dec.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(dec.out, eager_out):
+        raise SystemExit("graph replay differs from the eager layer")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        j = args.warmup + i
-        step(xs[j], layers[j % args.layers], ev=evs[i])
+    ev[0].record()
+    for r in range(replays):
+        dec.replay()
+        ev[r + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    # bytes of one FFN launch: the experts it reads (10 routed, all distinct at T=1) + the shared expert
-    ffn_bytes = s.top_k * expert_bytes(s) + shared_bytes(s)
-    achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
-    log(f"decode1: {ms_per_step * 1e3:.1f} us/step, expert FFN {ffn_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    ev_ms = [ev[r].elapsed_time(ev[r + 1]) / L for r in range(replays)]
+    layer_ms = float(np.mean(ev_ms))
+    # algorithmic bytes of one layer step: router weights + 10 routed experts (all distinct at T = 1) + shared
+    router_bytes = s.n_experts * s.hidden * 2
+    layer_bytes = router_bytes + s.top_k * expert_bytes(s) + shared_bytes(s)
+    achieved = layer_bytes / (layer_ms * 1e-3) / 1e9
+    log(f"decode1: {ms_per_step * 1e3:.2f} us/step (wall), {layer_ms * 1e3:.2f} us/step (events), "
+        f"{achieved:.0f} GB/s")
 
-    # secondary: 16-token decode through the 48-layer stack
+    # the dominant kernel, alone: the gate/up dequant-GEMV of each layer's token, launched through
+    # moe_expert_ffn with the phase flags (slot table and activations prepared beforehand, one
+    # workspace per layer, layers walked in turn so the weights come from HBM)
+    ffn = []
+    for i in range(L):
+        st = FfnState(s, 1, dev)
+        st.prepare(xs[i], layers[i])
+        ffn.append(st)
+    torch.cuda.synchronize()
+    gu_ms = time_phase(ffn, xs, layers, M.FFN_SKIP_DOWN, reps=max(1, replays // 2))
+    dn_ms = time_phase(ffn, xs, layers, M.FFN_SKIP_GATEUP, reps=max(1, replays // 2))
+    gu_bytes = (s.top_k * expert_bytes(s) + shared_bytes(s)) * 2 // 3
+    dn_bytes = (s.top_k * expert_bytes(s) + shared_bytes(s)) // 3
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    log(f"gate/up GEMV alone: {gu_ms * 1e3:.2f} us, {gu_gbs:.0f} GB/s; down GEMV alone: {dn_ms * 1e3:.2f} us, "
+        f"{dn_bytes / dn_ms / 1e6:.0f} GB/s")
+    del ffn
+
+    # kernel probe (bandwidth regime): 16 tokens x top-32 = 512 pairs, one per expert, so the gate/up
+    # kernel streams all 512 experts (+ the shared one) of a layer
+    probe = probe_gemv(s, layers, dev, log)
+
+    # secondary: 16-token decode through the 48-layer stack, also as one graph
     T16 = 16
-    st16 = Step(s, T16, dev)
     r = torch.empty(T16, s.hidden, device=dev)
     a = torch.empty(T16, s.hidden, dtype=torch.bfloat16, device=dev)
     x16 = synth.tokens(synth.WORKLOADS["decode16"], dev).float()
-    uniq_bytes = []
+    ws16 = M.alloc_workspace(s, T16, device=dev)
+    idx16 = torch.empty(L, T16, s.top_k, dtype=torch.int32, device=dev)
 
-    def stack_pass(count_unique=False):
+    def stack_pass():
         r.copy_(x16)
         M.rmsnorm_bf16(r, a)
-        for l in range(args.layers):
-            st16(a, layers[l], residual=r, next_in=a)
-            if count_unique:
-                uniq_bytes.append(unique_experts(st16))
+        for l in range(L):
+            M.layer_forward(a, layers[l], s, residual=r, next_in=a, topk_idx=idx16[l], ws=ws16)
 
-    stack_pass(count_unique=True)
-    for _ in range(2):
-        stack_pass()
+    stack_pass()
     torch.cuda.synchronize()
-    ts = time.perf_counter()
+    r_eager = r.clone()
+    uniq = [int(torch.unique(idx16[l]).numel()) for l in range(L)]
+    g16 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g16):
+        stack_pass()
+    g16.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(r, r_eager):
+        raise SystemExit("stack graph replay differs from the eager stack")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(args.stack_steps):
-        stack_pass()
+        g16.replay()
+    e1.record()
     torch.cuda.synchronize()
-    stack_ms = (time.perf_counter() - ts) * 1e3 / args.stack_steps
-    stack_bytes = sum(u * expert_bytes(s) + shared_bytes(s) + s.n_experts * s.hidden * 2 for u in uniq_bytes)
+    stack_ms = e0.elapsed_time(e1) / args.stack_steps
+    stack_bytes = sum(u * expert_bytes(s) + shared_bytes(s) + router_bytes for u in uniq)
     log(f"decode16 stack: {stack_ms:.3f} ms/step, {T16 / stack_ms * 1e3:.0f} tok/s, "
-        f"{stack_bytes / stack_ms / 1e6:.0f} GB/s, unique experts/layer {np.mean(uniq_bytes):.1f}")
+        f"{stack_bytes / stack_ms / 1e6:.0f} GB/s, unique experts/layer {np.mean(uniq):.1f}")
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.layers, xs, args.cpu_sample, log)
+        cpu = cpu_baseline(wl, args.layers, [synth.tokens(wl, dev, layer=1000 + i, n_tokens=1)
+                                             for i in range(args.cpu_sample)], args.cpu_sample, log)
 
     res = {
         "metric": "MoE-layer tokens/s (single-token decode, one full-shape layer)",
         "value": 1e3 / ms_per_step,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
@@ -249,15 +354,19 @@ def main():
         "config": {"workload": "decode1: 1 token, hidden 2048, 512 experts, top-10, inter 704, shared 704, "
                                "2-bit/32-block fp16 scales, Zipf(1.1) router bias; 48 resident layers walked "
                                "in turn", "global_batch": 1, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "expert FFN step (plan + gate/up + down kernels), HIP events on its stream",
-                     "bytes_per_launch": ffn_bytes, "avg_us": ffn_ms * 1e3},
+        "roofline": {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gemv_gateup_kernel (gate/up dequant-GEMV + SwiGLU, one token, 10 routed + shared "
+                               "expert), launched alone, HIP events on its stream",
+                     "bytes_per_launch": gu_bytes, "avg_us": gu_ms * 1e3,
+                     "layer": {"avg_us": layer_ms * 1e3, "bytes": layer_bytes, "GBs": achieved},
+                     "down_gemv": {"avg_us": dn_ms * 1e3, "bytes": dn_bytes, "GBs": dn_bytes / dn_ms / 1e6},
+                     "probe": probe},
         "cpu_baseline": cpu,
         "secondary": {"decode16_stack": {"tokens_per_s": T16 / stack_ms * 1e3, "ms_per_step": stack_ms,
                                          "layers": args.layers, "achieved_GBs": stack_bytes / stack_ms / 1e6,
                                          "hbm_frac": stack_bytes / stack_ms / 1e6 / HBM_PEAK_GBS,
-                                         "unique_experts_per_layer": float(np.mean(uniq_bytes))}},
+                                         "unique_experts_per_layer": float(np.mean(uniq))}},
     }
     print(json.dumps(res), flush=True)
 

@@ -3,6 +3,6 @@ block-quantised experts: HIP kernels behind a C ABI (include/moe.h), bound
 here with ctypes."""
 
 from ._lib import (  # noqa: F401
-    MoeError, QArena, QLayer, Shape, alloc_workspace, combine, dequant, expert_ffn, layer_forward, lib, permute,
+    FFN_REUSE_PLAN, FFN_SKIP_DOWN, FFN_SKIP_GATEUP, MoeError, QArena, QLayer, Shape, alloc_workspace, combine, dequant, expert_ffn, layer_forward, lib, permute,
     quantize, read_error, rmsnorm_bf16, route, workspace_bytes,
 )

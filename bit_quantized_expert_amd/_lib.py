@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_INDEX = 0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16 = 0, 1
 ALGO = {"auto": 0, "gemv": 1, "grouped": 2}
+FFN_REUSE_PLAN, FFN_SKIP_GATEUP, FFN_SKIP_DOWN = 1, 2, 4
 
 
 class MoeError(RuntimeError):
@@ -137,8 +138,8 @@ def _dtype_code(t) -> int:
     raise ValueError(f"unsupported activation dtype {t.dtype}")
 
 
-def _opts(algo: str) -> Options:
-    return Options(ALGO[algo], 0)
+def _opts(algo: str, flags: int = 0) -> Options:
+    return Options(ALGO[algo], flags)
 
 
 # ------------------------------------------------------------------ arenas
@@ -239,11 +240,11 @@ def permute(topk_idx, T: int, shape, counts, offsets, sorted_pair, pair_pos, ws,
 
 
 def expert_ffn(x, layer: QLayer, shape, offsets, sorted_pair, y_sorted, shared_out=None, algo="auto", ws=None,
-               stream=None) -> None:
+               stream=None, flags: int = 0) -> None:
     wp, wn = _ws(ws)
     _check(lib().moe_expert_ffn(_ptr(x), _dtype_code(x), x.shape[0], ctypes.byref(layer.c_struct()),
                                 ctypes.byref(Shape.of(shape)), _ptr(offsets), _ptr(sorted_pair), _ptr(y_sorted),
-                                _ptr(shared_out), ctypes.byref(_opts(algo)), wp, wn, _stream(stream)),
+                                _ptr(shared_out), ctypes.byref(_opts(algo, flags)), wp, wn, _stream(stream)),
            "moe_expert_ffn")
 
 

@@ -44,7 +44,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 constexpr int kMinTileBM = 32;
 
 struct WsLayout {
-  size_t header, active, tile_expert, tile_m0, chunk_hist, h_routed, h_shared;
+  size_t header, slots, tile_expert, tile_m0, chunk_hist, h_routed, h_shared;
   size_t end_perm, end_ffn;
   size_t logits, end_route;
   size_t topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos, y_sorted, shared_out, total;
@@ -64,7 +64,7 @@ WsLayout ws_layout(const moe_shape& s, int64_t T) {
   L.max_tiles = (P + kMinTileBM - 1) / kMinTileBM + std::min<int64_t>(E, P) +
                 (s.shared_inter > 0 ? (T + kMinTileBM - 1) / kMinTileBM : 0) + 2;
   L.header = take(moe::kHdrWords * 4);
-  L.active = take(size_t(E) * 4);
+  L.slots = take(size_t(E + 1) * 16);
   L.tile_expert = take(size_t(L.max_tiles) * 4);
   L.tile_m0 = take(size_t(L.max_tiles) * 4);
   const int64_t n_chunks = P > moe::kSmallPairs ? (P + moe::kPermChunk - 1) / moe::kPermChunk : 0;
@@ -168,27 +168,39 @@ moe_algo pick_algo(const moe_options* o, int64_t T) {
   return MOE_ALGO_GEMV;  // the grouped GEMM is not built yet
 }
 
-int check_opts(const moe_options* o) {
+int check_opts(const moe_options* o, bool ffn_flags_ok = false) {
   if (!o) return MOE_OK;
   if (o->ffn_algo < MOE_ALGO_AUTO || o->ffn_algo > MOE_ALGO_GROUPED)
     return fail(MOE_ERR_INVALID_ARG, "ffn_algo=%d is not a moe_algo", int(o->ffn_algo));
-  if (o->flags != 0) return fail(MOE_ERR_INVALID_ARG, "flags must be 0");
+  const int allowed = ffn_flags_ok ? (MOE_FFN_REUSE_PLAN | MOE_FFN_SKIP_GATEUP | MOE_FFN_SKIP_DOWN) : 0;
+  if (o->flags & ~allowed) return fail(MOE_ERR_INVALID_ARG, "flags=0x%x not accepted by this call", unsigned(o->flags));
   return MOE_OK;
 }
 
 // ---- the steps, shared by the single-step entry points and layer_forward
 
+// Router logits: bf16 x bf16 on MFMA (products exact, fp32 accumulation),
+// anything with fp32 operands on the vector ALUs.
+hipError_t route_logits(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s,
+                        float* logits, hipStream_t st) {
+  if (xd == MOE_BF16 && L->router_dtype == MOE_BF16)
+    return moe::launch_router_mfma(static_cast<const uint16_t*>(x), T, s->hidden,
+                                   static_cast<const uint16_t*>(L->w_router), L->router_bias, s->n_experts, logits,
+                                   st);
+  return moe::launch_router_gemv(x, xd == MOE_BF16, T, s->hidden, L->w_router, L->router_dtype == MOE_BF16,
+                                 L->router_bias, s->n_experts, logits, st);
+}
+
 hipError_t do_route(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s, float* logits,
                     int32_t* idx, float* w, hipStream_t st) {
-  hipError_t e = moe::launch_router_gemv(x, xd == MOE_BF16, T, s->hidden, L->w_router, L->router_dtype == MOE_BF16,
-                                         L->router_bias, s->n_experts, logits, st);
+  hipError_t e = route_logits(x, xd, T, L, s, logits, st);
   if (e != hipSuccess) return e;
   return moe::launch_topk(logits, T, s->n_experts, s->top_k, idx, w, st);
 }
 
-hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s,
-                  const int32_t* offsets, const int32_t* sorted_pair, float* y_sorted, float* shared_out,
-                  moe_algo algo, void* ws, const WsLayout& W, hipStream_t st) {
+moe::FfnArgs ffn_args(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s,
+                      const int32_t* offsets, const int32_t* sorted_pair, float* y_sorted, float* shared_out,
+                      void* ws, const WsLayout& W) {
   moe::FfnArgs a{};
   a.x = x;
   a.x_bf16 = xd == MOE_BF16;
@@ -211,20 +223,58 @@ hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, co
   a.offsets = offsets;
   a.sorted_pair = sorted_pair;
   a.header = at<int32_t>(ws, W.header);
-  a.plan_active = at<int32_t>(ws, W.active);
+  a.slots = at<int4>(ws, W.slots);
   a.tile_expert = at<int32_t>(ws, W.tile_expert);
   a.tile_m0 = at<int32_t>(ws, W.tile_m0);
   a.h_routed = at<_Float16>(ws, W.h_routed);
   a.h_shared = at<_Float16>(ws, W.h_shared);
   a.y_sorted = y_sorted;
   a.shared_out = shared_out;
+  return a;
+}
+
+hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s,
+                  const int32_t* offsets, const int32_t* sorted_pair, float* y_sorted, float* shared_out,
+                  moe_algo algo, void* ws, const WsLayout& W, hipStream_t st, int flags = 0) {
+  moe::FfnArgs a = ffn_args(x, xd, T, L, s, offsets, sorted_pair, y_sorted, shared_out, ws, W);
   const int tile_bm = algo == MOE_ALGO_GROUPED ? kMinTileBM : 0;
-  hipError_t e = moe::launch_plan(offsets, s->n_experts, T, a.has_shared, tile_bm, at<int32_t>(ws, W.header),
-                                  at<int32_t>(ws, W.active), at<int32_t>(ws, W.tile_expert),
-                                  at<int32_t>(ws, W.tile_m0), st);
-  if (e != hipSuccess) return e;
+  if (!(flags & MOE_FFN_REUSE_PLAN)) {
+    hipError_t e = moe::launch_plan(offsets, s->n_experts, T, a.has_shared, tile_bm, at<int32_t>(ws, W.header),
+                                    at<int4>(ws, W.slots), at<int32_t>(ws, W.tile_expert),
+                                    at<int32_t>(ws, W.tile_m0), st);
+    if (e != hipSuccess) return e;
+  }
+  const int phases = (flags & MOE_FFN_SKIP_GATEUP ? 0 : moe::kPhaseGateUp) | (flags & MOE_FFN_SKIP_DOWN ? 0 : moe::kPhaseDown);
   if (algo == MOE_ALGO_GROUPED) return moe::launch_ffn_grouped(a, tile_bm, W.max_tiles, st);
-  return moe::launch_ffn_gemv(a, st);
+  return moe::launch_ffn_gemv(a, st, phases);
+}
+
+// The decode layer in five launches: router, one-workgroup selection (top-k,
+// permutation, slot table), gate/up GEMV, down GEMV, combine (with the stack
+// glue).  No workgroup waits on another inside a kernel.
+bool fused_decode_ok(int64_t T, const moe_shape* s, moe_algo algo) {
+  return algo == MOE_ALGO_GEMV && T <= 16 && T * s->top_k <= 1024;
+}
+
+hipError_t fused_decode(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s, float* out,
+                        float* residual, uint16_t* next_in, int32_t* idx, float* w, void* ws, const WsLayout& W,
+                        hipStream_t st) {
+  float* logits = at<float>(ws, W.logits);
+  hipError_t e = route_logits(x, xd, T, L, s, logits, st);
+  if (e != hipSuccess) return e;
+  int32_t* offsets = at<int32_t>(ws, W.offsets);
+  int32_t* sorted_pair = at<int32_t>(ws, W.sorted_pair);
+  int32_t* pair_pos = at<int32_t>(ws, W.pair_pos);
+  float* y = at<float>(ws, W.y_sorted);
+  float* s_out = s->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;
+  e = moe::launch_select_small(logits, int(T), s->n_experts, s->top_k, s_out != nullptr, idx, w,
+                               at<int32_t>(ws, W.counts), offsets, sorted_pair, pair_pos, at<int32_t>(ws, W.header),
+                               at<int4>(ws, W.slots), st);
+  if (e != hipSuccess) return e;
+  moe::FfnArgs a = ffn_args(x, xd, T, L, s, offsets, sorted_pair, y, s_out, ws, W);
+  e = moe::launch_ffn_gemv(a, st, moe::kPhaseGateUp | moe::kPhaseDown);
+  if (e != hipSuccess) return e;
+  return moe::launch_combine(y, pair_pos, w, s_out, T, s->hidden, s->top_k, out, residual, next_in, st);
 }
 
 }  // namespace
@@ -298,7 +348,7 @@ int moe_expert_ffn(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer*
   try {
     if (int r = check_shape(shape)) return r;
     if (int r = check_T(T, shape)) return r;
-    if (int r = check_opts(opts)) return r;
+    if (int r = check_opts(opts, true)) return r;
     if (int r = check_layer(layer, shape, false, true)) return r;
     if (int r = check_dtype(x_dtype, "x")) return r;
     if (T == 0) return ok();
@@ -309,7 +359,7 @@ int moe_expert_ffn(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer*
     const WsLayout W = ws_layout(*shape, T);
     if (int r = check_ws(workspace, workspace_bytes, W.end_ffn)) return r;
     return device_status(do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y_sorted, shared_out,
-                                pick_algo(opts, T), workspace, W, as_stream(stream)),
+                                pick_algo(opts, T), workspace, W, as_stream(stream), opts ? opts->flags : 0),
                          "moe_expert_ffn");
   } catch (...) {
     return fail(MOE_ERR_DEVICE, "moe_expert_ffn: unexpected exception");
@@ -357,6 +407,10 @@ int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_lay
     void* ws = workspace;
     int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, W.topk_idx);
     float* w = topk_w ? topk_w : at<float>(ws, W.topk_w);
+    const moe_algo algo = pick_algo(opts, T);
+    if (fused_decode_ok(T, shape, algo))
+      return device_status(fused_decode(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st),
+                           "moe_layer_forward");
     hipError_t e = do_route(x, x_dtype, T, layer, shape, at<float>(ws, W.logits), idx, w, st);
     if (e != hipSuccess) return device_status(e, "moe_layer_forward/route");
     int32_t* offsets = at<int32_t>(ws, W.offsets);
@@ -367,7 +421,7 @@ int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_lay
     if (e != hipSuccess) return device_status(e, "moe_layer_forward/permute");
     float* y = at<float>(ws, W.y_sorted);
     float* s_out = shape->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;
-    e = do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, pick_algo(opts, T), ws, W, st);
+    e = do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, algo, ws, W, st);
     if (e != hipSuccess) return device_status(e, "moe_layer_forward/ffn");
     e = moe::launch_combine(y, pair_pos, w, s_out, T, shape->hidden, shape->top_k, out, residual, next_in_bf16, st);
     return device_status(e, "moe_layer_forward/combine");

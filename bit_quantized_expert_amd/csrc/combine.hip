@@ -29,11 +29,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float ss = 0.0f;
   for (int c = threadIdx.x; c < H4; c += 256) {
     float4v acc = shared ? reinterpret_cast<const float4v*>(shared + t * H)[c] : float4v{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int p = s_pos[j];
-      if (p < 0) continue;  // pair of an out-of-range expert id: skipped
-      const float4v v = reinterpret_cast<const float4v*>(y + int64_t(p) * H)[c];
-      acc += s_w[j] * v;
+    // issue up to 8 row loads before using them (latency, not bandwidth, bounds one token)
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float4v v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = j0 + i < k ? s_pos[j0 + i] : -1;
+        v[i] = p >= 0 ? reinterpret_cast<const float4v*>(y + int64_t(p) * H)[c] : float4v{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (j0 + i < k)  // pairs of out-of-range ids (p < 0) add 0
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(s_w[j0 + i], v[i][q], acc[q]);
     }
     if (out) reinterpret_cast<float4v*>(out + t * H)[c] = acc;
     if (res) {

@@ -80,6 +80,21 @@ __device__ __forceinline__ float16v mfma32_bf16(bf16x8 a, bf16x8 b, float16v c) 
 // the activations are staged in LDS in the same order.
 // ---------------------------------------------------------------------------
 
+// d = (a & mask) | bits in one v_and_or_b32 (mask in a VGPR, bits in an SGPR:
+// gfx9 VOP3 reads one scalar operand and no literal).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(mask), "s"(bits));
+  return d;
+}
+
+// Same with every operand in VGPRs (for per-lane `bits`).
+__device__ __forceinline__ uint32_t and_or_v(uint32_t a, uint32_t mask, uint32_t bits) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(mask), "v"(bits));
+  return d;
+}
+
 __device__ __forceinline__ uint32_t magic_bits(int i) {
   // fp16 bit pattern of 2^(10-2i) in both halves
   const uint32_t e = uint32_t(25 - 2 * i) << 10;
@@ -96,7 +111,7 @@ __device__ __forceinline__ void dq2_word(uint32_t w, half2v s2, half8& lo, half8
   for (int i = 0; i < 8; ++i) {
     const int j = i < 5 ? i : i - 5;
     const uint32_t src = i < 5 ? w : w10;
-    const uint32_t v = (src & (0x00030003u << (2 * j))) | magic_bits(j);
+    const uint32_t v = and_or(src, 0x00030003u << (2 * j), magic_bits(j));
     const f16 off = magic_val(j) + f16(2.0f);
     half2v h = as_half2(v) - half2v{off, off};
     p[i] = h * s2;
@@ -128,7 +143,7 @@ __device__ __forceinline__ void dq3_word(uint32_t w, uint32_t sp, half2v s2, hal
     const int j = i < 4 ? i : i - 4;
     const uint32_t src = i < 4 ? w : w8;
     const uint32_t hsrc = i < 4 ? hs : h8;
-    const uint32_t v = (src & (0x00030003u << (2 * j))) | (hsrc & (0x00040004u << (2 * j))) | magic_bits(j);
+    const uint32_t v = and_or_v(src, 0x00030003u << (2 * j), and_or(hsrc, 0x00040004u << (2 * j), magic_bits(j)));
     const f16 off = magic_val(j) + f16(4.0f);
     half2v h = as_half2(v) - half2v{off, off};
     p[i] = h * s2;
@@ -165,6 +180,85 @@ __device__ inline int block_exclusive_scan_lds(int* vals, int n, int* tmp) {
   __syncthreads();
   for (int i = 0; i < per; ++i) {
     const int idx = tid * per + i;
+    if (idx < n) vals[idx] = run;
+    run += local[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// ---------------------------------------------------------------------------
+// DPP wave reductions (no LDS traffic).  Within each row of 16 lanes: xor 1
+// and xor 2 through quad permutes, then rotations by 4 and 8; the four row
+// results are combined from lanes 0, 16, 32, 48 with readlane, so the result
+// is uniform across the wave.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xb1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4e>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x124>(v));  // row_ror:4
+  v = max(v, dpp_u32<0x128>(v));  // row_ror:8
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0xb1>(v));
+  v = min(v, dpp_u32<0x4e>(v));
+  v = min(v, dpp_u32<0x124>(v));
+  v = min(v, dpp_u32<0x128>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+// Order-preserving map of a finite float to an unsigned key (-0 folds to +0).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum over a wave (shuffle-up steps).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan of vals[0..n) in LDS by a 1024-thread workgroup with two
+// barriers: each wave scans a contiguous run, then the wave totals.  `tmp`
+// holds 16 ints.  Returns the total.  n <= 4096.
+__device__ inline int block_scan_fast(int* vals, int n, int* tmp) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per = (n + 1023) / 1024;  // values per thread, <= 4
+  int local[4], s = 0;
+  for (int i = 0; i < per; ++i) {
+    const int idx = threadIdx.x * per + i;
+    local[i] = idx < n ? vals[idx] : 0;
+    s += local[i];
+  }
+  const int incl = wave_incl_scan(s);
+  if (lane == 63) tmp[wv] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int t = tmp[w];
+    base += w < wv ? t : 0;
+    total += t;
+  }
+  int run = base + incl - s;
+  for (int i = 0; i < per; ++i) {
+    const int idx = threadIdx.x * per + i;
     if (idx < n) vals[idx] = run;
     run += local[i];
   }

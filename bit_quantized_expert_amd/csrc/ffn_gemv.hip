@@ -24,27 +24,28 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Plan: active expert list (ascending ids with a non-empty segment) and the
-// grouped-GEMM tile list.  One workgroup.
+// Plan: slot table (active experts in ascending id order, then the shared
+// expert) and the grouped-GEMM tile list, from offsets.  One workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int64_t T,
                                                    int has_shared, int tile_bm, int32_t* __restrict__ header,
-                                                   int32_t* __restrict__ active, int32_t* __restrict__ tile_expert,
-                                                   int32_t* __restrict__ tile_m0) {
+                                                   int4* __restrict__ slots, int32_t* __restrict__ tile_expert,
+                                                   int32_t* __restrict__ tile_m0, int n_slots) {
   __shared__ int flag[kMaxExperts];
   __shared__ int ntile[kMaxExperts];
-  __shared__ int tmp[1024];
+  __shared__ int tmp[16];
   for (int e = threadIdx.x; e < E; e += 1024) {
     const int c = offsets[e + 1] - offsets[e];
     flag[e] = c > 0;
     ntile[e] = tile_bm > 0 ? (c + tile_bm - 1) / tile_bm : 0;
   }
   __syncthreads();
-  const int n_active = block_exclusive_scan_lds(flag, E, tmp);
-  const int n_routed_tiles = block_exclusive_scan_lds(ntile, E, tmp);
+  const int n_active = block_scan_fast(flag, E, tmp);
+  const int n_routed_tiles = block_scan_fast(ntile, E, tmp);
   for (int e = threadIdx.x; e < E; e += 1024) {
-    const int c = offsets[e + 1] - offsets[e];
-    if (c > 0) active[flag[e]] = e;
+    const int lo = offsets[e];
+    const int c = offsets[e + 1] - lo;
+    if (c > 0) slots[flag[e]] = int4{e, lo, c, 0};
     if (tile_bm > 0) {
       int pos = ntile[e];
       for (int m0 = 0; m0 < c; m0 += tile_bm, ++pos) {
@@ -53,6 +54,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       }
     }
   }
+  const int n_valid = n_active + (has_shared ? 1 : 0);
+  if (threadIdx.x == 0 && has_shared) slots[n_active] = int4{-1, 0, int(T), 0};
+  for (int s = n_valid + threadIdx.x; s < n_slots; s += 1024) slots[s] = int4{0, 0, 0, 0};
   int n_tiles = n_routed_tiles;
   if (tile_bm > 0 && has_shared) {
     const int st = int((T + tile_bm - 1) / tile_bm);
@@ -63,87 +67,54 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     n_tiles += st;
   }
   if (threadIdx.x == 0) {
+    header[kHdrError] = 0;
     header[kHdrActive] = n_active;
+    header[kHdrValid] = n_valid;
     header[kHdrTiles] = n_tiles;
   }
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm, int32_t* header,
-                       int32_t* active, int32_t* tile_expert, int32_t* tile_m0, hipStream_t stream) {
-  plan_kernel<<<1, 1024, 0, stream>>>(offsets, E, T, has_shared, tile_bm, header, active, tile_expert, tile_m0);
+                       int4* slots, int32_t* tile_expert, int32_t* tile_m0, hipStream_t stream) {
+  const int n_slots = int(std::min<int64_t>(E, T * 32)) + 1;  // covers min(E, T*k) + 1 for every k <= 32
+  plan_kernel<<<1, 1024, 0, stream>>>(offsets, E, T, has_shared, tile_bm, header, slots, tile_expert, tile_m0,
+                                      n_slots);
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Slot resolution shared by both decode kernels.
-// ---------------------------------------------------------------------------
-struct Slot {
-  bool valid, shared;
-  int e, lo, m_total;
-};
+// Column position of h element i: the activations of the down projection are
+// stored in the permuted 16-group order its MFMA operands use.
+__device__ __forceinline__ int hcol(int i) { return (i & ~15) | perm16(i & 15); }
 
-__device__ __forceinline__ Slot resolve_slot(const FfnArgs& a, int slot) {
-  Slot s{false, false, 0, 0, 0};
-  const int n_active = a.header[kHdrActive];
-  if (slot < n_active) {
-    s.valid = true;
-    s.e = a.plan_active[slot];
-    s.lo = a.offsets[s.e];
-    s.m_total = a.offsets[s.e + 1] - s.lo;
-  } else if (slot == n_active && a.has_shared) {
-    s.valid = true;
-    s.shared = true;
-    s.m_total = int(a.T);
+// 16 consecutive activations -> the two permuted fp16 MFMA k-slices.
+template <typename SRC>
+__device__ __forceinline__ void load_x16(const SRC* src, half8& lo, half8& hi) {
+  float v[16];
+  if constexpr (sizeof(SRC) == 4) {
+    const float4v* p = reinterpret_cast<const float4v*>(src);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4v t = p[q];
+      v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+    }
+  } else {
+    const uint4v* p = reinterpret_cast<const uint4v*>(src);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4v t = p[q];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[8 * q + 2 * u] = __uint_as_float(t[u] << 16);
+        v[8 * q + 2 * u + 1] = __uint_as_float(t[u] & 0xffff0000u);
+      }
+    }
   }
-  return s;
-}
-
-// Stage rows of fp16 activations (or fp32/bf16 inputs) into LDS in the
-// permuted 16-group order.  src_row(r) gives the row pointer of tile row r.
-template <typename SRC, typename RowFn>
-__device__ __forceinline__ void stage_rows(f16* lds, int ldsw, int mnow, int K, RowFn src_row) {
-  const int groups = K / 16;
-  for (int it = threadIdx.x; it < mnow * groups; it += blockDim.x) {
-    const int r = it / groups, gg = it - r * groups;
-    const SRC* src = src_row(r) + gg * 16;
-    float v[16];
-    if constexpr (sizeof(SRC) == 4) {
-      const float4v* p = reinterpret_cast<const float4v*>(src);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4v t = p[q];
-        v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
-      }
-    } else {
-      const uint4v* p = reinterpret_cast<const uint4v*>(src);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint4v t = p[q];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t wd = t[u];
-          if constexpr (std::is_same<SRC, f16>::value) {
-            const half2v h = as_half2(wd);
-            v[8 * q + 2 * u] = float(h[0]);
-            v[8 * q + 2 * u + 1] = float(h[1]);
-          } else {  // bf16
-            v[8 * q + 2 * u] = __uint_as_float(wd << 16);
-            v[8 * q + 2 * u + 1] = __uint_as_float(wd & 0xffff0000u);
-          }
-        }
-      }
-    }
-    half8 lo, hi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo[2 * i] = f16(v[i]);
-      lo[2 * i + 1] = f16(v[i + 8]);
-      hi[2 * i] = f16(v[4 + i]);
-      hi[2 * i + 1] = f16(v[12 + i]);
-    }
-    half8* dst = reinterpret_cast<half8*>(lds + r * ldsw + gg * 16);
-    dst[0] = lo;
-    dst[1] = hi;
+  for (int i = 0; i < 4; ++i) {
+    lo[2 * i] = f16(v[i]);
+    lo[2 * i + 1] = f16(v[i + 8]);
+    hi[2 * i] = f16(v[4 + i]);
+    hi[2 * i + 1] = f16(v[12 + i]);
   }
 }
 
@@ -205,19 +176,309 @@ __device__ __forceinline__ void dq_unit_word(const Unit<QBITS, UNIT>& U, int d, 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  grid = (ceil(max_rows / 64), slots), block = 256.
+// gate/up + SwiGLU.  grid = (ceil(max_rows / RPW), slots), block = 256.
+//
+// Unit u of a row (64 or 32 weights) is read in round r' = u / 4 by lane
+// group g = u % 4.  Rounds fall in four classes c = r' % 4, each with its own
+// accumulator, summed at the end as ((c0 + c1) + c2) + c3.  With S = 4 the
+// four waves of a workgroup own the four classes of the same 16 rows (the
+// reduction axis split 4 ways: 4x more waves for single tokens) and the sum
+// goes through LDS; with S = 1 each wave owns 16 rows and all four classes
+// (64 rows per workgroup, staged activations reused by more rows).  Both
+// orders are the same, so a token's result does not depend on the batch.
+// The weight loads of a wave are issued before the activations are staged.
+// DIRECT (used with S = 4 for one token) reads the activations straight from
+// global memory into the MFMA operands, with no LDS and no barrier.
+// h is written in the permuted column order of the down projection.
 // ---------------------------------------------------------------------------
-template <int QBITS, int UNIT, typename XT>
+template <int QBITS, int UNIT, int S, bool DIRECT, typename XT>
 __global__ __launch_bounds__(256) void gemv_gateup_kernel(FfnArgs a) {
+  static_assert(S == 1 || S == 4, "S is 1 or 4");
   extern __shared__ __attribute__((aligned(16))) f16 xs[];
-  const Slot sl = resolve_slot(a, blockIdx.y);
-  if (!sl.valid) return;
-  const int rows = sl.shared ? a.Is : a.I;
-  const int row_base = blockIdx.x * 64;
-  if (row_base >= rows || sl.m_total == 0) return;
-  const QMat G = sl.shared ? a.sg : a.rg;
-  const QMat U = sl.shared ? a.su : a.ru;
-  const int64_t ex = sl.shared ? 0 : sl.e;
+  __shared__ float red[S > 1 ? 4 : 1][2][4][64];
+  constexpr int RPW = 64 / S;   // rows per workgroup
+  constexpr int NC = 4 / S;     // accumulator classes per wave
+  constexpr int RB = 8 / S;     // rounds per load batch
+  const int4 si = a.slots[blockIdx.y];
+  const int m_total = si.z;
+  if (m_total == 0) return;
+  const bool shared = si.x < 0;
+  const int rows = shared ? a.Is : a.I;
+  const int row_base = blockIdx.x * RPW;
+  if (row_base >= rows) return;
+  const QMat G = shared ? a.sg : a.rg;
+  const QMat U = shared ? a.su : a.ru;
+  const int64_t ex = shared ? 0 : si.x;
+  const uint8_t* gc = G.codes + ex * G.code_stride;
+  const uint16_t* gs = G.scales + ex * G.scale_stride;
+  const uint8_t* uc = U.codes + ex * U.code_stride;
+  const uint16_t* us = U.scales + ex * U.scale_stride;
+  const int H = a.H, ldsw = H + 8;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int rg = wv / S, ks = wv % S;
+  const int n = lane & 15, g = lane >> 4;
+  const int row = row_base + rg * 16 + n;
+  const bool wave_on = row_base + rg * 16 < rows;
+  const int n_units = H / UNIT, rounds = (n_units + 3) / 4;  // rounds r' of 4 units
+  const XT* x = static_cast<const XT*>(a.x);
+  f16* hout = shared ? a.h_shared : a.h_routed;
+  const int hw = shared ? a.Is : a.I;
+
+  for (int mc = 0; mc < m_total; mc += kGemvMaxM) {
+    const int mnow = min(kGemvMaxM, m_total - mc);
+    // first load batch of this wave's weights, before anything waits
+    Unit<QBITS, UNIT> ug[RB], uu[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int rp = i * S + ks, u = rp * 4 + g;
+      if (wave_on && rp < rounds && u < n_units) {
+        load_unit(ug[i], gc, gs, rows, H, row, u);
+        load_unit(uu[i], uc, us, rows, H, row, u);
+      } else {
+        zero_unit(ug[i]);
+        zero_unit(uu[i]);
+      }
+    }
+    const bool a_on = n < mnow;  // this lane's A row (token) exists
+    // DIRECT: the whole first batch of this lane's activations, loaded now
+    half8 xa[DIRECT ? RB : 1][DIRECT ? UNIT / 16 : 1][2];
+    const XT* xg = nullptr;
+    if constexpr (DIRECT) {
+      if (a_on) xg = x + (shared ? int64_t(mc + n) : int64_t(a.sorted_pair[si.y + mc + n] / a.k)) * H;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int rp = i * S + ks, u = rp * 4 + g;
+#pragma unroll
+        for (int d = 0; d < UNIT / 16; ++d) {
+          if (wave_on && a_on && rp < rounds && u < n_units) {
+            load_x16(xg + u * UNIT + 16 * d, xa[i][d][0], xa[i][d][1]);
+          } else {
+            xa[i][d][0] = half8{};
+            xa[i][d][1] = half8{};
+          }
+        }
+      }
+    } else {
+      __syncthreads();
+      for (int it = threadIdx.x; it < mnow * (H / 16); it += blockDim.x) {
+        const int r = it / (H / 16), gg = it - r * (H / 16);
+        const int64_t t = shared ? int64_t(mc + r) : int64_t(a.sorted_pair[si.y + mc + r] / a.k);
+        half8 lo, hi;
+        load_x16(x + t * H + gg * 16, lo, hi);
+        half8* dst = reinterpret_cast<half8*>(xs + r * ldsw + gg * 16);
+        dst[0] = lo;
+        dst[1] = hi;
+      }
+      __syncthreads();
+    }
+    float4v accg[NC], accu[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) accg[c] = accu[c] = float4v{0.f, 0.f, 0.f, 0.f};
+    if (wave_on) {
+      const f16* xrow = xs + n * ldsw;
+      for (int b0 = 0; b0 * S < rounds; b0 += RB) {
+        if (b0 > 0) {
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const int rp = (b0 + i) * S + ks, u = rp * 4 + g;
+            if (rp < rounds && u < n_units) {
+              load_unit(ug[i], gc, gs, rows, H, row, u);
+              load_unit(uu[i], uc, us, rows, H, row, u);
+            } else {
+              zero_unit(ug[i]);
+              zero_unit(uu[i]);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int rp = (b0 + i) * S + ks;
+          if (rp >= rounds) break;
+          const int c = (b0 + i) % NC;  // class of round rp: ks (S = 4) or i % 4 (S = 1)
+          const int u = rp * 4 + g;
+          const bool on = a_on && u < n_units;
+#pragma unroll
+          for (int d = 0; d < UNIT / 16; ++d) {
+            half8 glo, ghi, ulo, uhi, alo = {}, ahi = {};
+            dq_unit_word(ug[i], d, glo, ghi);
+            dq_unit_word(uu[i], d, ulo, uhi);
+            if constexpr (DIRECT) {
+              if (b0 == 0) {
+                alo = xa[i][d][0];
+                ahi = xa[i][d][1];
+              } else if (on) {
+                load_x16(xg + u * UNIT + 16 * d, alo, ahi);
+              }
+            } else if (on) {
+              {
+                const half8* ap = reinterpret_cast<const half8*>(xrow + u * UNIT + 16 * d);
+                alo = ap[0];
+                ahi = ap[1];
+              }
+            }
+            accg[c] = mfma16(alo, glo, accg[c]);
+            accg[c] = mfma16(ahi, ghi, accg[c]);
+            accu[c] = mfma16(alo, ulo, accu[c]);
+            accu[c] = mfma16(ahi, uhi, accu[c]);
+          }
+        }
+      }
+    }
+    float4v sg = accg[0], su = accu[0];
+    if constexpr (S == 1) {
+#pragma unroll
+      for (int c = 1; c < 4; ++c) {
+        sg += accg[c];
+        su += accu[c];
+      }
+    } else {
+      if (ks > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          red[wv][0][j][lane] = accg[0][j];
+          red[wv][1][j][lane] = accu[0][j];
+        }
+      }
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sg[j] += red[wv + q][0][j][lane];
+            su[j] += red[wv + q][1][j][lane];
+          }
+      }
+      __syncthreads();  // red is reused by the next token chunk
+    }
+    if (wave_on && ks == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 4 * g + j;
+        if (m < mnow) {
+          const float hv = silu_f(sg[j]) * su[j];
+          const int64_t hr = shared ? int64_t(mc + m) : int64_t(si.y + mc + m);
+          hout[hr * hw + hcol(row)] = f16(hv);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down projection: y[m][n] = h_m . W_down[n].  grid = (ceil(H / 64), slots),
+// block = 256, 16 rows per wave.  The weight loads are issued first; the h
+// operands (already in the permuted order) are read straight from global
+// memory, so the kernel has no LDS and no barrier.
+// ---------------------------------------------------------------------------
+template <int QBITS, int UNIT>
+__global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
+  const int4 si = a.slots[blockIdx.y];
+  const int m_total = si.z;
+  if (m_total == 0) return;
+  const bool shared = si.x < 0;
+  if (shared && a.shared_out == nullptr) return;
+  const int H = a.H;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row_w = blockIdx.x * 64 + wv * 16;
+  if (row_w >= H) return;  // per wave: no barriers in this kernel
+  const int K = shared ? a.Is : a.I;
+  const QMat D = shared ? a.sd : a.rd;
+  const int64_t ex = shared ? 0 : si.x;
+  const uint8_t* dc = D.codes + ex * D.code_stride;
+  const uint16_t* ds = D.scales + ex * D.scale_stride;
+  const int n = lane & 15, g = lane >> 4;
+  const int row = row_w + n;
+  const int n_units = K / UNIT, rounds = (n_units + 3) / 4;
+  const f16* hin = shared ? a.h_shared : a.h_routed;
+  float* yout = shared ? a.shared_out : a.y_sorted;
+  constexpr int RB = 4;
+
+  for (int mc = 0; mc < m_total; mc += kGemvMaxM) {
+    const int mnow = min(kGemvMaxM, m_total - mc);
+    const bool a_on = n < mnow;
+    const f16* hrow = hin + (shared ? int64_t(mc + n) : int64_t(si.y + mc + n)) * K;
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < rounds; r0 += RB) {
+      Unit<QBITS, UNIT> ud[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int u = (r0 + i) * 4 + g;
+        if (r0 + i < rounds && u < n_units) load_unit(ud[i], dc, ds, H, K, row, u);
+        else zero_unit(ud[i]);
+      }
+      half8 av[RB][UNIT / 16][2];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int u = (r0 + i) * 4 + g;
+        const bool on = a_on && r0 + i < rounds && u < n_units;
+#pragma unroll
+        for (int d = 0; d < UNIT / 16; ++d) {
+          if (on) {
+            const half8* ap = reinterpret_cast<const half8*>(hrow + u * UNIT + 16 * d);
+            av[i][d][0] = ap[0];
+            av[i][d][1] = ap[1];
+          } else {
+            av[i][d][0] = half8{};
+            av[i][d][1] = half8{};
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (r0 + i >= rounds) break;
+#pragma unroll
+        for (int d = 0; d < UNIT / 16; ++d) {
+          half8 blo, bhi;
+          dq_unit_word(ud[i], d, blo, bhi);
+          acc = mfma16(av[i][d][0], blo, acc);
+          acc = mfma16(av[i][d][1], bhi, acc);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = 4 * g + j;
+      if (m < mnow) {
+        const int64_t yr = shared ? int64_t(mc + m) : int64_t(si.y + mc + m);
+        yout[yr * H + row] = acc[j];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Throughput versions for more than one token (decode batches, verify
+// windows): NW waves of 16 rows each per workgroup, activations staged once
+// in LDS for all of them, and a rolling pipeline that keeps the next D rounds
+// of weight loads in flight while the current round is dequantised and fed
+// to the MFMAs.  Accumulation classes and orders are those of the kernels
+// above, so results are bit-identical to the single-token path.
+// ---------------------------------------------------------------------------
+#ifndef MOE_TP_D
+#define MOE_TP_D 4
+#endif
+#ifndef MOE_TP_NW
+#define MOE_TP_NW 4
+#endif
+#ifndef MOE_TP_MINW
+#define MOE_TP_MINW 1
+#endif
+template <int QBITS, int UNIT, typename XT, int NW>
+__global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) f16 xs[];
+  constexpr int D = MOE_TP_D;
+  static_assert(D % 4 == 0, "the pipeline depth is a multiple of the 4 accumulation classes");
+  const int4 si = a.slots[blockIdx.y];
+  const int m_total = si.z;
+  if (m_total == 0) return;
+  const bool shared = si.x < 0;
+  const int rows = shared ? a.Is : a.I;
+  const int row_base = blockIdx.x * 16 * NW;
+  if (row_base >= rows) return;
+  const QMat G = shared ? a.sg : a.rg;
+  const QMat U = shared ? a.su : a.ru;
+  const int64_t ex = shared ? 0 : si.x;
   const uint8_t* gc = G.codes + ex * G.code_stride;
   const uint16_t* gs = G.scales + ex * G.scale_stride;
   const uint8_t* uc = U.codes + ex * U.code_stride;
@@ -229,129 +490,150 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(FfnArgs a) {
   const bool wave_on = row_base + wv * 16 < rows;
   const int n_units = H / UNIT, rounds = (n_units + 3) / 4;
   const XT* x = static_cast<const XT*>(a.x);
-  f16* hout = sl.shared ? a.h_shared : a.h_routed;
-  const int hw = sl.shared ? a.Is : a.I;
+  f16* hout = shared ? a.h_shared : a.h_routed;
+  const int hw = shared ? a.Is : a.I;
 
-  for (int mc = 0; mc < sl.m_total; mc += kGemvMaxM) {
-    const int mnow = min(kGemvMaxM, sl.m_total - mc);
-    __syncthreads();
-    stage_rows<XT>(xs, ldsw, mnow, H, [&](int r) -> const XT* {
-      const int64_t t = sl.shared ? int64_t(mc + r) : int64_t(a.sorted_pair[sl.lo + mc + r] / a.k);
-      return x + t * H;
-    });
-    __syncthreads();
-    if (!wave_on) continue;
-    float4v accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    const bool a_on = n < mnow;  // this lane's A row (token) exists
-    const f16* xrow = xs + n * ldsw;
-    constexpr int RB = 8;
-    for (int r0 = 0; r0 < rounds; r0 += RB) {
-      Unit<QBITS, UNIT> ug[RB], uu[RB];
+  for (int mc = 0; mc < m_total; mc += kGemvMaxM) {
+    const int mnow = min(kGemvMaxM, m_total - mc);
+    Unit<QBITS, UNIT> ug[D], uu[D];
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int u = (r0 + i) * 4 + g;
-        if (r0 + i < rounds && u < n_units) {
-          load_unit(ug[i], gc, gs, rows, H, row, u);
-          load_unit(uu[i], uc, us, rows, H, row, u);
-        } else {
-          zero_unit(ug[i]);
-          zero_unit(uu[i]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        if (r0 + i >= rounds) break;
-        const int u = (r0 + i) * 4 + g;
-        const bool on = a_on && u < n_units;
-#pragma unroll
-        for (int d = 0; d < UNIT / 16; ++d) {
-          half8 glo, ghi, ulo, uhi, alo = {}, ahi = {};
-          dq_unit_word(ug[i], d, glo, ghi);
-          dq_unit_word(uu[i], d, ulo, uhi);
-          if (on) {
-            const half8* ap = reinterpret_cast<const half8*>(xrow + u * UNIT + 16 * d);
-            alo = ap[0];
-            ahi = ap[1];
-          }
-          accg = mfma16(alo, glo, accg);
-          accg = mfma16(ahi, ghi, accg);
-          accu = mfma16(alo, ulo, accu);
-          accu = mfma16(ahi, uhi, accu);
-        }
+    for (int i = 0; i < D; ++i) {
+      const int u = i * 4 + g;
+      if (wave_on && i < rounds && u < n_units) {
+        load_unit(ug[i], gc, gs, rows, H, row, u);
+        load_unit(uu[i], uc, us, rows, H, row, u);
+      } else {
+        zero_unit(ug[i]);
+        zero_unit(uu[i]);
       }
     }
+    __syncthreads();
+    for (int it = threadIdx.x; it < mnow * (H / 16); it += blockDim.x) {
+      const int r = it / (H / 16), gg = it - r * (H / 16);
+      const int64_t t = shared ? int64_t(mc + r) : int64_t(a.sorted_pair[si.y + mc + r] / a.k);
+      half8 lo, hi;
+      load_x16(x + t * H + gg * 16, lo, hi);
+      half8* dst = reinterpret_cast<half8*>(xs + r * ldsw + gg * 16);
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+    __syncthreads();
+    float4v accg[4], accu[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = 4 * g + j;
-      if (m < mnow) {
-        const float hv = silu_f(accg[j]) * accu[j];
-        const int64_t hr = sl.shared ? int64_t(mc + m) : int64_t(sl.lo + mc + m);
-        hout[hr * hw + row] = f16(hv);
+    for (int c = 0; c < 4; ++c) accg[c] = accu[c] = float4v{0.f, 0.f, 0.f, 0.f};
+    if (wave_on) {
+      // Rows past the tokens (and units past K, whose weights are zero) read
+      // a real, finite row: MFMA rows are independent and the extra rows of
+      // the result are never stored, so no operand needs zeroing.
+      const f16* xrow = xs + min(n, mnow - 1) * ldsw;
+      for (int r0 = 0; r0 < rounds; r0 += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          const int r = r0 + i;
+          if (r >= rounds) break;
+          const Unit<QBITS, UNIT> cg = ug[i], cu = uu[i];
+          const int rn = r + D, un = rn * 4 + g;
+          if (rn < rounds && un < n_units) {
+            load_unit(ug[i], gc, gs, rows, H, row, un);
+            load_unit(uu[i], uc, us, rows, H, row, un);
+          }
+          const int u = r * 4 + g;
+          const int ua = u < n_units ? u : 0;
+#pragma unroll
+          for (int d = 0; d < UNIT / 16; ++d) {
+            half8 glo, ghi, ulo, uhi;
+            dq_unit_word(cg, d, glo, ghi);
+            dq_unit_word(cu, d, ulo, uhi);
+            const half8* ap = reinterpret_cast<const half8*>(xrow + ua * UNIT + 16 * d);
+            const half8 alo = ap[0], ahi = ap[1];
+            const int c = i & 3;  // class of round r = r0 + i (r0 is a multiple of D, D of 4)
+            accg[c] = mfma16(alo, glo, accg[c]);
+            accg[c] = mfma16(ahi, ghi, accg[c]);
+            accu[c] = mfma16(alo, ulo, accu[c]);
+            accu[c] = mfma16(ahi, uhi, accu[c]);
+          }
+        }
+      }
+      float4v sg = accg[0], su = accu[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) {
+        sg += accg[c];
+        su += accu[c];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 4 * g + j;
+        if (m < mnow) {
+          const float hv = silu_f(sg[j]) * su[j];
+          const int64_t hr = shared ? int64_t(mc + m) : int64_t(si.y + mc + m);
+          hout[hr * hw + hcol(row)] = f16(hv);
+        }
       }
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// down projection.  grid = (ceil(H / 64), slots), block = 256.
-// ---------------------------------------------------------------------------
-template <int QBITS, int UNIT>
-__global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a, int ldsw) {
+template <int QBITS, int UNIT, int NW>
+__global__ __launch_bounds__(64 * NW) void gemv_down_tp_kernel(FfnArgs a, int ldsw) {
   extern __shared__ __attribute__((aligned(16))) f16 hs[];
-  const Slot sl = resolve_slot(a, blockIdx.y);
-  if (!sl.valid) return;
+  constexpr int D = 4;
+  const int4 si = a.slots[blockIdx.y];
+  const int m_total = si.z;
+  if (m_total == 0) return;
+  const bool shared = si.x < 0;
+  if (shared && a.shared_out == nullptr) return;
   const int H = a.H;
-  const int row_base = blockIdx.x * 64;
-  if (row_base >= H || sl.m_total == 0) return;
-  if (sl.shared && a.shared_out == nullptr) return;
-  const int K = sl.shared ? a.Is : a.I;
-  const QMat D = sl.shared ? a.sd : a.rd;
-  const int64_t ex = sl.shared ? 0 : sl.e;
-  const uint8_t* dc = D.codes + ex * D.code_stride;
-  const uint16_t* ds = D.scales + ex * D.scale_stride;
+  const int row_base = blockIdx.x * 16 * NW;
+  if (row_base >= H) return;
+  const int K = shared ? a.Is : a.I;
+  const QMat Dm = shared ? a.sd : a.rd;
+  const int64_t ex = shared ? 0 : si.x;
+  const uint8_t* dc = Dm.codes + ex * Dm.code_stride;
+  const uint16_t* ds = Dm.scales + ex * Dm.scale_stride;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int row = row_base + wv * 16 + n;
   const bool wave_on = row_base + wv * 16 < H;
   const int n_units = K / UNIT, rounds = (n_units + 3) / 4;
-  const f16* hin = sl.shared ? a.h_shared : a.h_routed;
-  float* yout = sl.shared ? a.shared_out : a.y_sorted;
+  const f16* hin = shared ? a.h_shared : a.h_routed;
+  float* yout = shared ? a.shared_out : a.y_sorted;
 
-  for (int mc = 0; mc < sl.m_total; mc += kGemvMaxM) {
-    const int mnow = min(kGemvMaxM, sl.m_total - mc);
+  for (int mc = 0; mc < m_total; mc += kGemvMaxM) {
+    const int mnow = min(kGemvMaxM, m_total - mc);
+    Unit<QBITS, UNIT> ud[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int u = i * 4 + g;
+      if (wave_on && i < rounds && u < n_units) load_unit(ud[i], dc, ds, H, K, row, u);
+      else zero_unit(ud[i]);
+    }
     __syncthreads();
-    stage_rows<f16>(hs, ldsw, mnow, K, [&](int r) -> const f16* {
-      const int64_t hr = sl.shared ? int64_t(mc + r) : int64_t(sl.lo + mc + r);
-      return hin + hr * K;
-    });
+    // h rows are already in the MFMA operand order: plain 16-byte copies
+    for (int it = threadIdx.x; it < mnow * (K / 8); it += blockDim.x) {
+      const int r = it / (K / 8), c8 = it - r * (K / 8);
+      const int64_t hr = shared ? int64_t(mc + r) : int64_t(si.y + mc + r);
+      *reinterpret_cast<half8*>(hs + r * ldsw + c8 * 8) = *reinterpret_cast<const half8*>(hin + hr * K + c8 * 8);
+    }
     __syncthreads();
     if (!wave_on) continue;
+    const f16* hrow = hs + min(n, mnow - 1) * ldsw;  // see the gate/up kernel: finite, never stored
     float4v acc = {0.f, 0.f, 0.f, 0.f};
-    const bool a_on = n < mnow;
-    const f16* hrow = hs + n * ldsw;
-    constexpr int RB = 4;
-    for (int r0 = 0; r0 < rounds; r0 += RB) {
-      Unit<QBITS, UNIT> ud[RB];
+    for (int r0 = 0; r0 < rounds; r0 += D) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int u = (r0 + i) * 4 + g;
-        if (r0 + i < rounds && u < n_units) load_unit(ud[i], dc, ds, H, K, row, u);
-        else zero_unit(ud[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        if (r0 + i >= rounds) break;
-        const int u = (r0 + i) * 4 + g;
-        const bool on = a_on && u < n_units;
+      for (int i = 0; i < D; ++i) {
+        const int r = r0 + i;
+        if (r >= rounds) break;
+        const Unit<QBITS, UNIT> cd = ud[i];
+        const int rn = r + D, un = rn * 4 + g;
+        if (rn < rounds && un < n_units) load_unit(ud[i], dc, ds, H, K, row, un);
+        const int u = r * 4 + g;
+        const int ua = u < n_units ? u : 0;
 #pragma unroll
         for (int d = 0; d < UNIT / 16; ++d) {
-          half8 blo, bhi, alo = {}, ahi = {};
-          dq_unit_word(ud[i], d, blo, bhi);
-          if (on) {
-            const half8* ap = reinterpret_cast<const half8*>(hrow + u * UNIT + 16 * d);
-            alo = ap[0];
-            ahi = ap[1];
-          }
+          half8 blo, bhi;
+          dq_unit_word(cd, d, blo, bhi);
+          const half8* ap = reinterpret_cast<const half8*>(hrow + ua * UNIT + 16 * d);
+          const half8 alo = ap[0], ahi = ap[1];
           acc = mfma16(alo, blo, acc);
           acc = mfma16(ahi, bhi, acc);
         }
@@ -361,7 +643,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a, int ldsw) {
     for (int j = 0; j < 4; ++j) {
       const int m = 4 * g + j;
       if (m < mnow) {
-        const int64_t yr = sl.shared ? int64_t(mc + m) : int64_t(sl.lo + mc + m);
+        const int64_t yr = shared ? int64_t(mc + m) : int64_t(si.y + mc + m);
         yout[yr * H + row] = acc[j];
       }
     }
@@ -370,39 +652,52 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a, int ldsw) {
 
 // ---------------------------------------------------------------------------
 template <int QBITS>
-static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream) {
+static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases) {
+  constexpr int NW = MOE_TP_NW;
   const int64_t P = a.T * a.k;
   const int slots = int(std::min<int64_t>(a.E, P)) + (a.has_shared ? 1 : 0);
   const int mrows = int(std::min<int64_t>(kGemvMaxM, std::max<int64_t>(a.T, 1)));
   const int max_rows = std::max(a.I, a.has_shared ? a.Is : 0);
-  {
-    const dim3 grid(unsigned((max_rows + 63) / 64), unsigned(slots));
-    const size_t lds = size_t(mrows) * (a.H + 8) * sizeof(f16);
+  const bool one = a.T == 1;  // one token: latency-shaped kernels (no LDS on the gate/up side)
+  if (phases & kPhaseGateUp) {
     const bool u64 = a.H % 64 == 0;
-    if (a.x_bf16) {
-      if (u64) gemv_gateup_kernel<QBITS, 64, uint16_t><<<grid, 256, lds, stream>>>(a);
-      else gemv_gateup_kernel<QBITS, 32, uint16_t><<<grid, 256, lds, stream>>>(a);
+    if (one) {
+      const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
+#define GU(U_, X_) gemv_gateup_kernel<QBITS, U_, 4, true, X_><<<grid, 256, 0, stream>>>(a)
+      if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+      else { if (u64) GU(64, float); else GU(32, float); }
+#undef GU
     } else {
-      if (u64) gemv_gateup_kernel<QBITS, 64, float><<<grid, 256, lds, stream>>>(a);
-      else gemv_gateup_kernel<QBITS, 32, float><<<grid, 256, lds, stream>>>(a);
+      const size_t lds = size_t(mrows) * (a.H + 8) * sizeof(f16);
+      const dim3 grid(unsigned((max_rows + 16 * NW - 1) / (16 * NW)), unsigned(slots));
+#define GU(U_, X_) gemv_gateup_tp_kernel<QBITS, U_, X_, NW><<<grid, 64 * NW, lds, stream>>>(a)
+      if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+      else { if (u64) GU(64, float); else GU(32, float); }
+#undef GU
     }
   }
-  {
-    const int kmax = std::max(a.I, a.has_shared ? a.Is : 0);
-    const int ldsw = kmax + 8;
-    const dim3 grid(unsigned((a.H + 63) / 64), unsigned(slots));
-    const size_t lds = size_t(mrows) * ldsw * sizeof(f16);
+  if (phases & kPhaseDown) {
     // UNIT must divide both K values; 64 only when both are multiples of 64.
     const bool u64 = a.I % 64 == 0 && (!a.has_shared || a.Is % 64 == 0);
-    if (u64) gemv_down_kernel<QBITS, 64><<<grid, 256, lds, stream>>>(a, ldsw);
-    else gemv_down_kernel<QBITS, 32><<<grid, 256, lds, stream>>>(a, ldsw);
+    if (one) {
+      const dim3 grid(unsigned((a.H + 63) / 64), unsigned(slots));
+      if (u64) gemv_down_kernel<QBITS, 64><<<grid, 256, 0, stream>>>(a);
+      else gemv_down_kernel<QBITS, 32><<<grid, 256, 0, stream>>>(a);
+    } else {
+      const int kmax = std::max(a.I, a.has_shared ? a.Is : 0);
+      const int ldsw = kmax + 8;
+      const size_t lds = size_t(mrows) * ldsw * sizeof(f16);
+      const dim3 grid(unsigned((a.H + 16 * NW - 1) / (16 * NW)), unsigned(slots));
+      if (u64) gemv_down_tp_kernel<QBITS, 64, NW><<<grid, 64 * NW, lds, stream>>>(a, ldsw);
+      else gemv_down_tp_kernel<QBITS, 32, NW><<<grid, 64 * NW, lds, stream>>>(a, ldsw);
+    }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream) {
+hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases) {
   if (a.T == 0) return hipSuccess;
-  return a.qbits == 2 ? launch_gemv_q<2>(a, stream) : launch_gemv_q<3>(a, stream);
+  return a.qbits == 2 ? launch_gemv_q<2>(a, stream, phases) : launch_gemv_q<3>(a, stream, phases);
 }
 
 }  // namespace moe

@@ -6,9 +6,5 @@
 namespace moe {
 
 hipError_t launch_ffn_grouped(const FfnArgs&, int, int64_t, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_router_mfma(const uint16_t*, int64_t, int, const uint16_t*, const float*, int, float*,
-                              hipStream_t) {
-  return hipErrorNotSupported;
-}
 
 }  // namespace moe

@@ -14,7 +14,7 @@ constexpr int kPermChunk = 1024;    // pairs per workgroup in the multi-workgrou
 constexpr int kGemvMaxM = 16;       // tokens per MFMA tile in the decode kernels
 
 // Workspace header (int32 words at the start of the workspace).
-enum HeaderWord { kHdrError = 0, kHdrActive = 1, kHdrTiles = 2, kHdrWords = 64 };
+enum HeaderWord { kHdrError = 0, kHdrActive = 1, kHdrTiles = 2, kHdrValid = 3, kHdrWords = 64 };
 
 struct QMat {
   const uint8_t* codes;
@@ -23,8 +23,8 @@ struct QMat {
   int64_t scale_stride;  // fp16 elements between experts
 };
 
-// Everything the expert-FFN kernels read.  Slot s < n_active is routed expert
-// plan_active[s]; slot n_active is the shared expert when has_shared.
+// Everything the expert-FFN kernels read.  Slot s of the slot table is routed
+// expert slots[s].x (or the shared expert when slots[s].x < 0).
 struct FfnArgs {
   const void* x;
   int x_bf16;
@@ -34,11 +34,12 @@ struct FfnArgs {
   QMat sg, su, sd;  // shared gate / up / down
   const int32_t* offsets;
   const int32_t* sorted_pair;
-  const int32_t* header;       // workspace header (n_active, n_tiles)
-  const int32_t* plan_active;  // [E] active expert ids
+  const int32_t* header;       // workspace header (n_active, n_valid, n_tiles)
+  const int4* slots;           // slot table, see launch_select_small
   const int32_t* tile_expert;  // grouped GEMM tiles: expert id (-1 = shared)
   const int32_t* tile_m0;      //                     first row of the tile
-  _Float16* h_routed;          // [P][I] SwiGLU activations, sorted order
+  _Float16* h_routed;          // [P][I] SwiGLU activations, sorted order, columns
+                               //   permuted within groups of 16 (MFMA operand order)
   _Float16* h_shared;          // [T][Is]
   float* y_sorted;             // [P][H]
   float* shared_out;           // [T][H] or null
@@ -58,12 +59,21 @@ hipError_t launch_rmsnorm_bf16(const float* r, int64_t T, int H, uint16_t* a, hi
 hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos, int32_t* header, int32_t* chunk_hist,
                           hipStream_t stream);
-// Builds the active-expert list (and, when tile_bm > 0, the grouped-GEMM tile
-// list) from offsets.
+// Builds the slot table (and, when tile_bm > 0, the grouped-GEMM tile list)
+// from offsets, for the standalone expert FFN.
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm,
-                       int32_t* header, int32_t* active, int32_t* tile_expert, int32_t* tile_m0,
+                       int32_t* header, int4* slots, int32_t* tile_expert, int32_t* tile_m0,
                        hipStream_t stream);
-hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream);
+// Decode-layer selection on one workgroup (T <= 16): top-k + softmax weights,
+// permutation and the slot table (int4 {expert or -1 for shared, first sorted
+// position, token count, 0}; empty slots have count 0).
+hipError_t launch_select_small(const float* logits, int T, int E, int k, int has_shared, int32_t* idx, float* w,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                               int32_t* header, int4* slots, hipStream_t stream);
+
+// Routed + shared expert FFN on the decode kernels: h then y_sorted / shared_out.
+enum { kPhaseGateUp = 1, kPhaseDown = 2 };
+hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases);
 hipError_t launch_ffn_grouped(const FfnArgs& a, int tile_bm, int64_t max_tiles, hipStream_t stream);
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                           const float* shared_out, int64_t T, int H, int k, float* out, float* residual,

@@ -15,49 +15,164 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Router logits on the vector ALUs: logits[t][e] = x[t] . W[e] + b[e].
-// One wave per expert row, up to 16 tokens per workgroup; the activations
-// are staged in LDS (fp32) in K-chunks of 512 and reused by the 4 waves.
-// Used for decode-sized batches and for fp32 inputs.
+// One wave per expert row, 4 rows per workgroup, up to TT tokens per
+// workgroup (grid.y walks token chunks).  Lane l reads 8 consecutive weights
+// at h = 8l + 512i (one 128-bit load of bf16, two of fp32), so a wave streams
+// the row in 1 KB coalesced pieces.  For one token the activations come
+// straight from global memory (the same 4 KB for every wave, L2-resident);
+// for more tokens they are staged in LDS in K-chunks of KC.
 // ---------------------------------------------------------------------------
-constexpr int kRouteTT = 16;   // tokens per workgroup
-constexpr int kRouteKC = 512;  // K chunk staged in LDS
+template <typename T_>
+__device__ __forceinline__ void load8(const T_* p, float* v) {
+  if constexpr (sizeof(T_) == 2) {
+    const uint4v u = *reinterpret_cast<const uint4v*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  } else {
+    const float4v a = reinterpret_cast<const float4v*>(p)[0];
+    const float4v b = reinterpret_cast<const float4v*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+}
 
-template <typename XT, typename WT>
+template <typename XT, typename WT, int TT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const XT* __restrict__ x, int64_t T, int H,
                                                          const WT* __restrict__ w, const float* __restrict__ bias,
                                                          int E, float* __restrict__ logits) {
-  __shared__ float xs[kRouteTT][kRouteKC];
+  constexpr int KC = TT == 1 ? 0 : (32768 / (TT * int(sizeof(XT))));  // K chunk staged in LDS (32 KB)
+  __shared__ __attribute__((aligned(16))) XT xs[TT == 1 ? 1 : TT * KC];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int e = blockIdx.x * 4 + wv;
-  const int64_t t0 = int64_t(blockIdx.y) * kRouteTT;
-  const int tt = int(min<int64_t>(kRouteTT, T - t0));
-  float acc[kRouteTT];
+  const int64_t t0 = int64_t(blockIdx.y) * TT;
+  const int tt = int(min<int64_t>(TT, T - t0));
+  float acc[TT];
 #pragma unroll
-  for (int i = 0; i < kRouteTT; ++i) acc[i] = 0.0f;
-  for (int k0 = 0; k0 < H; k0 += kRouteKC) {
-    const int kc = min(kRouteKC, H - k0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < kRouteTT * kRouteKC; i += 256) {
-      const int r = i / kRouteKC, c = i % kRouteKC;
-      xs[r][c] = (r < tt && c < kc) ? load_act(x + (t0 + r) * H + k0 + c) : 0.0f;
-    }
-    __syncthreads();
+  for (int i = 0; i < TT; ++i) acc[i] = 0.0f;
+  const WT* wrow = w + int64_t(e < E ? e : 0) * H;
+  if constexpr (TT == 1) {
     if (e < E) {
-      for (int c = lane; c < kc; c += 64) {
-        const float wv_ = load_act(w + int64_t(e) * H + k0 + c);
+      for (int h = lane * 8; h < H; h += 512) {
+        float wv8[8], xv8[8];
+        load8(wrow + h, wv8);
+        load8(x + t0 * H + h, xv8);
 #pragma unroll
-        for (int i = 0; i < kRouteTT; ++i) acc[i] += wv_ * xs[i][c];
+        for (int i = 0; i < 8; ++i) acc[0] += wv8[i] * xv8[i];
+      }
+    }
+  } else {
+    for (int k0 = 0; k0 < H; k0 += KC) {
+      const int kc = min(KC, H - k0);
+      __syncthreads();
+      // stage x[t0 .. t0+tt)[k0 .. k0+kc) (8 elements per thread-step)
+      for (int i = threadIdx.x * 8; i < TT * kc; i += 256 * 8) {
+        const int r = i / kc, c = i - r * kc;
+        if (r < tt) {
+          const XT* src = x + (t0 + r) * H + k0 + c;
+          *reinterpret_cast<uint4v*>(&xs[r * KC + c]) = *reinterpret_cast<const uint4v*>(src);
+          if constexpr (sizeof(XT) == 4)
+            *reinterpret_cast<uint4v*>(&xs[r * KC + c + 4]) = *reinterpret_cast<const uint4v*>(src + 4);
+        }
+      }
+      __syncthreads();
+      if (e < E) {
+        for (int c = lane * 8; c < kc; c += 512) {
+          float wv8[8];
+          load8(wrow + k0 + c, wv8);
+#pragma unroll
+          for (int r = 0; r < TT; ++r) {
+            if (r < tt) {
+              float xv8[8];
+              load8(&xs[r * KC + c], xv8);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) acc[r] += wv8[i] * xv8[i];
+            }
+          }
+        }
       }
     }
   }
   if (e >= E) return;
   const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
-  for (int i = 0; i < kRouteTT; ++i) {
-    const float s = wave_sum(acc[i]);
-    if (lane == 0 && i < tt) logits[(t0 + i) * E + e] = s + b;
+  for (int i = 0; i < TT; ++i) {
+    if (i < tt) {
+      const float s = wave_sum(acc[i]);
+      if (lane == 0) logits[(t0 + i) * E + e] = s + b;
+    }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Router logits on MFMA for bf16 activations and bf16 router weights
+// (v_mfma_f32_16x16x32_bf16: bf16 x bf16 products are exact in fp32).
+// Workgroup = 16 experts x 16 tokens, 8 waves; wave w takes the 32-wide
+// K blocks w, w+8, w+16, ...  Partial tiles are summed through LDS in wave
+// order, so a token's logits never depend on the other tokens.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
+                                                         const uint16_t* __restrict__ w,
+                                                         const float* __restrict__ bias, int E,
+                                                         float* __restrict__ logits) {
+  __shared__ float red[8][4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int e0 = blockIdx.x * 16;
+  const int64_t t0 = int64_t(blockIdx.y) * 16;
+  const int nkb = H / 32;
+  const bool b_on = e0 + n < E;
+  const bool a_on = t0 + n < T;
+  const uint16_t* wrow = w + int64_t(b_on ? e0 + n : 0) * H + 8 * g;
+  const uint16_t* xrow = x + (a_on ? t0 + n : 0) * H + 8 * g;
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int B = 8;  // K blocks per load batch
+  for (int kb0 = wv; kb0 < nkb; kb0 += 8 * B) {
+    uint4v bw[B], ax[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int kb = kb0 + 8 * i;
+      const bool in = kb < nkb;
+      bw[i] = (in && b_on) ? *reinterpret_cast<const uint4v*>(wrow + kb * 32) : uint4v{0u, 0u, 0u, 0u};
+      ax[i] = (in && a_on) ? *reinterpret_cast<const uint4v*>(xrow + kb * 32) : uint4v{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+      if (kb0 + 8 * i < nkb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ax[i]),
+                                                      __builtin_bit_cast(bf16x8, bw[i]), acc, 0, 0, 0);
+  }
+  if (wv > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[wv][j][lane] = acc[j];
+  }
+  __syncthreads();
+  if (wv != 0) return;
+#pragma unroll
+  for (int q = 1; q < 8; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += red[q][j][lane];
+  if (!b_on) return;
+  const float b = bias ? bias[e0 + n] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = t0 + 4 * g + j;
+    if (t < T) logits[t * E + e0 + n] = acc[j] + b;
+  }
+}
+
+hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_t* w, const float* bias, int E,
+                              float* logits, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid(unsigned((E + 15) / 16), unsigned((T + 15) / 16));
+  router_mfma_kernel<<<grid, 512, 0, stream>>>(x, T, H, w, bias, E, logits);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -141,22 +256,25 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
+template <typename XT, typename WT>
+static void router_launch(const void* x, int64_t T, int H, const void* w, const float* bias, int E, float* logits,
+                          hipStream_t stream) {
+  if (T == 1) {
+    router_gemv_kernel<XT, WT, 1><<<dim3(unsigned((E + 3) / 4), 1), 256, 0, stream>>>(
+        (const XT*)x, T, H, (const WT*)w, bias, E, logits);
+  } else {
+    router_gemv_kernel<XT, WT, 16><<<dim3(unsigned((E + 3) / 4), unsigned((T + 15) / 16)), 256, 0, stream>>>(
+        (const XT*)x, T, H, (const WT*)w, bias, E, logits);
+  }
+}
+
 hipError_t launch_router_gemv(const void* x, bool x_bf16, int64_t T, int H, const void* w, bool w_bf16,
                               const float* bias, int E, float* logits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid(unsigned((E + 3) / 4), unsigned((T + kRouteTT - 1) / kRouteTT));
-  if (x_bf16 && w_bf16)
-    router_gemv_kernel<uint16_t, uint16_t><<<grid, 256, 0, stream>>>(
-        (const uint16_t*)x, T, H, (const uint16_t*)w, bias, E, logits);
-  else if (x_bf16)
-    router_gemv_kernel<uint16_t, float><<<grid, 256, 0, stream>>>((const uint16_t*)x, T, H, (const float*)w,
-                                                                  bias, E, logits);
-  else if (w_bf16)
-    router_gemv_kernel<float, uint16_t><<<grid, 256, 0, stream>>>((const float*)x, T, H, (const uint16_t*)w,
-                                                                  bias, E, logits);
-  else
-    router_gemv_kernel<float, float><<<grid, 256, 0, stream>>>((const float*)x, T, H, (const float*)w, bias,
-                                                               E, logits);
+  if (x_bf16 && w_bf16) router_launch<uint16_t, uint16_t>(x, T, H, w, bias, E, logits, stream);
+  else if (x_bf16) router_launch<uint16_t, float>(x, T, H, w, bias, E, logits, stream);
+  else if (w_bf16) router_launch<float, uint16_t>(x, T, H, w, bias, E, logits, stream);
+  else router_launch<float, float>(x, T, H, w, bias, E, logits, stream);
   return hipGetLastError();
 }
 

@@ -1,0 +1,157 @@
+// Decode-layer selection on a single workgroup (T <= 16 tokens): top-k with
+// renormalised softmax weights, the stable token-to-expert permutation and
+// the slot table of the expert FFN -- everything between the router logits
+// and the expert FFN in one launch.  Same rules as the standalone kernels:
+// ranks ordered by router weight with ties to the lower expert index ("How
+// Strata runs a 125-billion-parameter model ...", Step 2, "Verify-window
+// route tail skip"), pairs grouped by expert in ascending (token, rank) order.
+#include <limits.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kSelMaxT = 16;
+
+// One wave: top-k of one token's logits.  Lane l holds experts l + 64v.
+// Each round takes the largest key (DPP max), then the lowest expert index
+// among the lanes holding it (DPP min).  Lane j < k returns selection j.
+template <int V>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, float& my_val, int& my_idx) {
+  const int lane = threadIdx.x & 63;
+  float val[V];
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = lane + 64 * v;
+    val[v] = e < E ? row[e] : 0.0f;
+    key[v] = e < E ? float_key(val[v]) : 0u;  // 0 is below every real key
+  }
+  uint64_t taken = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (lane + 64 * v >= E) taken |= 1ull << v;
+  my_val = 0.0f;
+  my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    // best (largest key, then lowest index) of this lane; lower v = lower index
+    uint32_t bk = 0;
+    int bv = -1;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (!((taken >> v) & 1ull) && (bv < 0 || key[v] > bk)) {
+        bk = key[v];
+        bv = v;
+      }
+    const uint32_t top = wave_max_u32(bv >= 0 ? bk : 0u);
+    const uint32_t cand = (bv >= 0 && bk == top) ? uint32_t(lane + 64 * bv) : 0xffffffffu;
+    const uint32_t win = wave_min_u32(cand);  // uniform: the winning expert id
+    const int owner = int(win & 63), wv_ = int(win >> 6);
+    float wval = 0.0f;
+    if (lane == owner) {
+      taken |= 1ull << wv_;
+#pragma unroll
+      for (int q = 0; q < V; ++q)
+        if (q == wv_) wval = val[q];
+    }
+    wval = __shfl(wval, owner, 64);
+    if (lane == j) {
+      my_val = wval;
+      my_idx = int(win);
+    }
+  }
+}
+
+template <int V>
+__global__ __launch_bounds__(1024) void select_small_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                           int has_shared, int32_t* __restrict__ idx_out,
+                                                           float* __restrict__ w_out, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_pair,
+                                                           int32_t* __restrict__ pair_pos,
+                                                           int32_t* __restrict__ header, int4* __restrict__ slots) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int flag[kMaxExperts];
+  __shared__ int tmp[16];
+  __shared__ int s_idx[kSelMaxT * kMaxTopK];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += 1024) cnt[e] = 0;
+
+  // ---- top-k of token wv (one wave per token)
+  if (wv < T) {
+    float my_val;
+    int my_idx;
+    wave_topk<V>(logits + int64_t(wv) * E, E, k, my_val, my_idx);
+    const float top = __shfl(my_val, 0, 64);
+    const float p = lane < k ? expf(my_val - top) : 0.0f;
+    const float sum = wave_sum(p);
+    if (lane < k) {
+      idx_out[wv * k + lane] = my_idx;
+      w_out[wv * k + lane] = p / sum;
+      s_idx[wv * k + lane] = my_idx;
+    }
+  }
+  __syncthreads();
+
+  // ---- histogram, offsets
+  const int P = T * k;
+  for (int p = threadIdx.x; p < P; p += 1024) atomicAdd(&cnt[s_idx[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    counts[e] = cnt[e];
+    flag[e] = cnt[e] > 0;
+  }
+  const int total = block_scan_fast(cnt, E, tmp);
+  for (int e = threadIdx.x; e < E; e += 1024) offsets[e] = cnt[e];
+  if (threadIdx.x == 0) offsets[E] = total;
+
+  // ---- stable scatter (P <= 1024: one pair per thread)
+  if (threadIdx.x < P) {
+    const int p = threadIdx.x;
+    const int e = s_idx[p];
+    int before = 0;
+    for (int j = 0; j < p; ++j) before += s_idx[j] == e;
+    const int pos = cnt[e] + before;
+    sorted_pair[pos] = p;
+    pair_pos[p] = pos;
+  }
+
+  // ---- slot table: active experts in ascending id order, then the shared expert
+  const int n_active = block_scan_fast(flag, E, tmp);
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    const int c = (e + 1 < E ? cnt[e + 1] : total) - cnt[e];
+    if (c > 0) slots[flag[e]] = int4{e, cnt[e], c, 0};
+  }
+  const int n_valid = n_active + (has_shared ? 1 : 0);
+  if (threadIdx.x == 0) {
+    if (has_shared) slots[n_active] = int4{-1, 0, T, 0};
+    header[kHdrError] = 0;
+    header[kHdrActive] = n_active;
+    header[kHdrValid] = n_valid;
+  }
+  // slots past the valid ones are empty (m = 0) so any grid size is safe
+  const int n_slots = min(E, P) + 1;
+  for (int s = n_valid + threadIdx.x; s < n_slots; s += 1024) slots[s] = int4{0, 0, 0, 0};
+}
+
+hipError_t launch_select_small(const float* logits, int T, int E, int k, int has_shared, int32_t* idx, float* w,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                               int32_t* header, int4* slots, hipStream_t stream) {
+  if (T > kSelMaxT || T * k > 1024) return hipErrorInvalidValue;
+  const int v = (E + 63) / 64;
+#define SEL(V_)                                                                                                \
+  select_small_kernel<V_><<<1, 1024, 0, stream>>>(logits, T, E, k, has_shared, idx, w, counts, offsets,      \
+                                                  sorted_pair, pair_pos, header, slots)
+  if (v <= 1) SEL(1);
+  else if (v <= 2) SEL(2);
+  else if (v <= 4) SEL(4);
+  else if (v <= 8) SEL(8);
+  else if (v <= 16) SEL(16);
+  else if (v <= 32) SEL(32);
+  else SEL(64);
+#undef SEL
+  return hipGetLastError();
+}
+
+}  // namespace moe

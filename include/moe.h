@@ -103,9 +103,22 @@ typedef struct {
                                ignored when shared_inter == 0 */
 } moe_layer;
 
+/* Phase control of moe_expert_ffn (flags of moe_options; moe_layer_forward
+ * takes none).  For running one projection kernel alone, e.g. to time it:
+ * REUSE_PLAN skips building the slot table from offsets (reusing the one the
+ * previous moe_expert_ffn call on this workspace built, for the same offsets
+ * and T); SKIP_GATEUP skips the gate/up projection (reusing the activations
+ * left in the workspace by the previous call); SKIP_DOWN skips the down
+ * projection (y_sorted and shared_out are then not written). */
+enum {
+  MOE_FFN_REUSE_PLAN = 1,
+  MOE_FFN_SKIP_GATEUP = 2,
+  MOE_FFN_SKIP_DOWN = 4
+};
+
 typedef struct {
   moe_algo ffn_algo;
-  int32_t flags; /* reserved, must be 0 */
+  int32_t flags; /* MOE_FFN_* bits for moe_expert_ffn; 0 for every other call */
 } moe_options;
 
 /* Bytes of workspace moe_layer_forward needs for T tokens (also enough for

@@ -85,7 +85,7 @@ def test_validation_before_any_device_call():
     assert L.last_required_workspace() == need
     assert "MiB short" in L.last_error_detail()
     # bad options
-    o = L.Options(7, 0)
+    o = L.Options(0, 1)
     assert lib.moe_layer_forward(fake, 1, 4, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None, None,
                                  ctypes.byref(o), fake, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
     # next_in without residual
