@@ -82,42 +82,6 @@ hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared,
   return hipGetLastError();
 }
 
-// Column position of h element i: the activations of the down projection are
-// stored in the permuted 16-group order its MFMA operands use.
-__device__ __forceinline__ int hcol(int i) { return (i & ~15) | perm16(i & 15); }
-
-// 16 consecutive activations -> the two permuted fp16 MFMA k-slices.
-template <typename SRC>
-__device__ __forceinline__ void load_x16(const SRC* src, half8& lo, half8& hi) {
-  float v[16];
-  if constexpr (sizeof(SRC) == 4) {
-    const float4v* p = reinterpret_cast<const float4v*>(src);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4v t = p[q];
-      v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
-    }
-  } else {
-    const uint4v* p = reinterpret_cast<const uint4v*>(src);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint4v t = p[q];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v[8 * q + 2 * u] = __uint_as_float(t[u] << 16);
-        v[8 * q + 2 * u + 1] = __uint_as_float(t[u] & 0xffff0000u);
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo[2 * i] = f16(v[i]);
-    lo[2 * i + 1] = f16(v[i + 8]);
-    hi[2 * i] = f16(v[4 + i]);
-    hi[2 * i + 1] = f16(v[12 + i]);
-  }
-}
-
 // One quantised unit of a row: UNIT = 64 weights (16 code bytes, 2 scales)
 // or 32 (8 code bytes, 1 scale).  3-bit adds UNIT/32 high-plane words.
 template <int QBITS, int UNIT>

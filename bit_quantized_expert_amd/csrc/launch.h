@@ -74,7 +74,10 @@ hipError_t launch_select_small(const float* logits, int T, int E, int k, int has
 // Routed + shared expert FFN on the decode kernels: h then y_sorted / shared_out.
 enum { kPhaseGateUp = 1, kPhaseDown = 2 };
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases);
-hipError_t launch_ffn_grouped(const FfnArgs& a, int tile_bm, int64_t max_tiles, hipStream_t stream);
+// Grouped-GEMM expert FFN over the tile list of launch_plan (tile_bm =
+// kGroupedBM); max_tiles bounds the list for the launch grid.
+constexpr int kGroupedBM = 128;
+hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases);
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                           const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
                           uint16_t* next_in, hipStream_t stream);
