@@ -11,7 +11,9 @@ them, so the expert bytes come from HBM and not from a warm 256 MB Infinity
 Cache.
 
 Also reported (secondary): the 16-token decode stack through the same 48
-layers with the residual/RMSNorm/bf16 glue.
+layers with the residual/RMSNorm/bf16 glue; one 32,768-token prefill layer
+(grouped-GEMM path, MFMA roofline of its gate/up and down kernels); the
+4,096-token 3-bit prefill through a 48-layer stack with uniform routing.
 
 Output: one JSON line (see the keys below).  --gpus N with N > 1 exits: this
 build runs on one GPU.
@@ -99,8 +101,9 @@ class FfnState:
     """Inputs of moe_expert_ffn for one token-batch on one layer: routing,
     permutation and a workspace holding the slot table and activations."""
 
-    def __init__(self, s, T, device, shape=None):
+    def __init__(self, s, T, device, shape=None, algo="gemv"):
         self.s = shape or s
+        self.algo = algo
         s = self.s
         self.T = T
         P = T * s.top_k
@@ -120,7 +123,7 @@ class FfnState:
         self.run(x, layer, 0)
 
     def run(self, x, layer, flags):
-        M.expert_ffn(x, layer, self.s, self.offsets, self.sp, self.y, self.so, algo="gemv", ws=self.ws,
+        M.expert_ffn(x, layer, self.s, self.offsets, self.sp, self.y, self.so, algo=self.algo, ws=self.ws,
                      flags=flags)
 
 
@@ -167,6 +170,98 @@ def probe_gemv(s, layers, dev, log):
                     "(16 tokens x 32 experts, one pair per expert)",
             "gateup": {"avg_us": gu * 1e3, "bytes": gu_b, "GBs": gu_b / gu / 1e6, "frac": gu_b / gu / 1e6 / HBM_PEAK_GBS},
             "down": {"avg_us": dn * 1e3, "bytes": dn_b, "GBs": dn_b / dn / 1e6, "frac": dn_b / dn / 1e6 / HBM_PEAK_GBS}}
+
+
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
+
+
+def ffn_flops(s, T) -> tuple[int, int]:
+    """Algorithmic flops of the gate/up and down projections for T tokens
+    (routed pairs plus the shared expert)."""
+    P = T * s.top_k
+    gu = 2 * s.hidden * 2 * (P * s.inter + T * s.shared_inter)
+    dn = 2 * s.hidden * (P * s.inter + T * s.shared_inter)
+    return gu, dn
+
+
+def prefill_bench(wl, layer, dev, log, reps=5):
+    """One prefill layer (T tokens through route, permute, grouped-GEMM FFN,
+    combine), and the grouped gate/up and down kernels launched alone."""
+    s = wl.shape
+    T = wl.tokens
+    x = synth.tokens(wl, dev)
+    ws = M.alloc_workspace(s, T, device=dev)
+    out = torch.empty(T, s.hidden, device=dev)
+    M.layer_forward(x, layer, s, out=out, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        M.layer_forward(x, layer, s, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    layer_ms = e0.elapsed_time(e1) / reps
+    del ws
+    st = FfnState(s, T, dev, algo="grouped")
+    st.prepare(x, layer)
+    torch.cuda.synchronize()
+    gu = time_phase([st], [x], [layer], M.FFN_SKIP_DOWN, reps=reps)
+    dn = time_phase([st], [x], [layer], M.FFN_SKIP_GATEUP, reps=reps)
+    used = int((st.counts > 0).sum().item())
+    top = int(st.counts.max().item())
+    del st
+    gu_f, dn_f = ffn_flops(s, T)
+    rt_f = 2 * T * s.hidden * s.n_experts
+    tot = gu_f + dn_f + rt_f
+    log(f"{wl.name}: layer {layer_ms:.3f} ms ({T / layer_ms * 1e3:.0f} tok/s, {tot / layer_ms / 1e9:.0f} TFLOP/s); "
+        f"gate/up {gu:.3f} ms {gu_f / gu / 1e9:.0f} TFLOP/s; down {dn:.3f} ms {dn_f / dn / 1e9:.0f} TFLOP/s; "
+        f"experts used {used}, largest {top} tokens")
+    return {"tokens": T, "layer_ms": layer_ms, "tokens_per_s": T / layer_ms * 1e3,
+            "layer_tflops": tot / layer_ms / 1e9, "layer_mfma_frac": tot / layer_ms / 1e9 / MFMA_PEAK_TFLOPS,
+            "gateup": {"avg_ms": gu, "flops": gu_f, "tflops": gu_f / gu / 1e9,
+                       "frac": gu_f / gu / 1e9 / MFMA_PEAK_TFLOPS},
+            "down": {"avg_ms": dn, "flops": dn_f, "tflops": dn_f / dn / 1e9,
+                     "frac": dn_f / dn / 1e9 / MFMA_PEAK_TFLOPS},
+            "experts_used": used, "largest_expert_tokens": top}
+
+
+def prefill3_stack_bench(dev, log, n_layers, steps=2):
+    """4,096 tokens through the 48-layer 3-bit stack (uniform routing), with
+    the residual / RMSNorm / bf16 glue between layers."""
+    wl = synth.WORKLOADS["prefill3"]
+    s = wl.shape
+    layers = build_layers(wl, n_layers, dev, log)
+    T = wl.tokens
+    x0 = synth.tokens(wl, dev).float()
+    r = torch.empty(T, s.hidden, device=dev)
+    a = torch.empty(T, s.hidden, dtype=torch.bfloat16, device=dev)
+    ws = M.alloc_workspace(s, T, device=dev)
+
+    def step():
+        r.copy_(x0)
+        M.rmsnorm_bf16(r, a)
+        for l in range(n_layers):
+            M.layer_forward(a, layers[l], s, residual=r, next_in=a, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gu_f, dn_f = ffn_flops(s, T)
+    tot = n_layers * (gu_f + dn_f + 2 * T * s.hidden * s.n_experts)
+    wbytes = n_layers * (s.n_experts * expert_bytes(s) + shared_bytes(s) + s.n_experts * s.hidden * 2)
+    log(f"prefill3 stack: {ms:.1f} ms/step ({T / ms * 1e3:.0f} tok/s, {tot / ms / 1e9:.0f} TFLOP/s, "
+        f"weights {wbytes / ms / 1e6:.0f} GB/s)")
+    del layers, ws
+    torch.cuda.empty_cache()
+    return {"tokens": T, "layers": n_layers, "ms_per_step": ms, "tokens_per_s": T / ms * 1e3,
+            "tflops": tot / ms / 1e9, "mfma_frac": tot / ms / 1e9 / MFMA_PEAK_TFLOPS,
+            "weight_GBs": wbytes / ms / 1e6}
 
 
 def cpu_baseline(wl, layers_fp_seed, xs, n_sample, log):
@@ -223,6 +318,9 @@ def main():
     ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--cpu-sample", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill3", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 10 times (scales the HBM byte counters)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
 
@@ -237,6 +335,14 @@ def main():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
     dev = "cuda:0"
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read_per_launch": src.numel() * 4}))
+        return
     M.lib()
 
     wl = synth.WORKLOADS["decode1"]
@@ -333,6 +439,13 @@ def main():
     log(f"decode16 stack: {stack_ms:.3f} ms/step, {T16 / stack_ms * 1e3:.0f} tok/s, "
         f"{stack_bytes / stack_ms / 1e6:.0f} GB/s, unique experts/layer {np.mean(uniq):.1f}")
 
+    # secondary: prefill workloads on the grouped-GEMM path
+    prefill = prefill_bench(synth.WORKLOADS["prefill"], layers[0], dev, log)
+    torch.cuda.empty_cache()
+    prefill3 = None
+    if not args.no_prefill3:
+        prefill3 = prefill3_stack_bench(dev, log, args.layers)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.layers, [synth.tokens(wl, dev, layer=1000 + i, n_tokens=1)
@@ -363,7 +476,8 @@ def main():
                      "down_gemv": {"avg_us": dn_ms * 1e3, "bytes": dn_bytes, "GBs": dn_bytes / dn_ms / 1e6},
                      "probe": probe},
         "cpu_baseline": cpu,
-        "secondary": {"decode16_stack": {"tokens_per_s": T16 / stack_ms * 1e3, "ms_per_step": stack_ms,
+        "secondary": {"prefill32k_layer": prefill, "prefill3_4k_stack": prefill3,
+                      "decode16_stack": {"tokens_per_s": T16 / stack_ms * 1e3, "ms_per_step": stack_ms,
                                          "layers": args.layers, "achieved_GBs": stack_bytes / stack_ms / 1e6,
                                          "hbm_frac": stack_bytes / stack_ms / 1e6 / HBM_PEAK_GBS,
                                          "unique_experts_per_layer": float(np.mean(uniq))}},
