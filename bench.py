@@ -129,19 +129,25 @@ class FfnState:
 
 def time_phase(states, xs, layers, skip, reps):
     """Average duration (ms) of one projection kernel launched alone through
-    moe_expert_ffn(REUSE_PLAN | skip), HIP events on the launching stream,
-    walking the layers in turn."""
+    moe_expert_ffn(REUSE_PLAN | skip), walking the layers in turn.  The
+    launches are captured back to back in one HIP graph (no host gap between
+    them) and timed with HIP events on the capturing stream, so the average
+    is the kernel's own duration plus the graph's inter-dispatch gap."""
     flags = M.FFN_REUSE_PLAN | skip
-    evs = []
-    for _ in range(reps):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
         for st, x, layer in zip(states, xs, layers):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
             st.run(x, layer, flags)
-            b.record()
-            evs.append((a, b))
+    g.replay()
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / (reps * len(states))
 
 
 def probe_gemv(s, layers, dev, log):
@@ -173,6 +179,32 @@ def probe_gemv(s, layers, dev, log):
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gateup_decode1_traffic.txt")
+TRAFFIC_SOURCES = ("ffn_gemv.hip", "common.h", "launch.h")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode gate/up kernel from the committed
+    FETCH_SIZE / WRITE_SIZE counter runs (scaled by the copy-kernel
+    calibration), or None when the kernel source changed since they were
+    taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            with open(os.path.join(ROOT, "bit_quantized_expert_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != kv["source_sha256"]:
+            return None
+        return (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) + float(kv["write_kib"]) * float(kv["write_scale"])) * 1024
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def ffn_flops(s, T) -> tuple[int, int]:
@@ -468,7 +500,7 @@ def main():
                                "2-bit/32-block fp16 scales, Zipf(1.1) router bias; 48 resident layers walked "
                                "in turn", "global_batch": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "gemv_gateup_kernel (gate/up dequant-GEMV + SwiGLU, one token, 10 routed + shared "
                                "expert), launched alone, HIP events on its stream",
                      "bytes_per_launch": gu_bytes, "avg_us": gu_ms * 1e3,
