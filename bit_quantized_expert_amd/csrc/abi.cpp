@@ -281,6 +281,27 @@ hipError_t fused_decode(const void* x, moe_dtype xd, int64_t T, const moe_layer*
   return moe::launch_combine(y, pair_pos, w, s_out, T, s->hidden, s->top_k, out, residual, next_in, st);
 }
 
+// The single-token decode layer in three launches (four with the stack
+// glue): router logits; gate/up with the top-k made from the logits inside
+// every workgroup (no selection kernel, no slot table); down projection of
+// all selected experts and the shared expert with the combine done inside
+// the workgroup; then the residual RMSNorm when next_in is asked for.
+bool decode1_ok(int64_t T, const moe_shape* s, moe_algo algo) {
+  return algo == MOE_ALGO_GEMV && T == 1 && s->n_experts <= moe::kDecode1MaxExperts;
+}
+
+hipError_t decode1(const void* x, moe_dtype xd, const moe_layer* L, const moe_shape* s, float* out, float* residual,
+                   uint16_t* next_in, int32_t* idx, float* w, void* ws, const WsLayout& W, hipStream_t st) {
+  float* logits = at<float>(ws, W.logits);
+  hipError_t e = route_logits(x, xd, 1, L, s, logits, st);
+  if (e != hipSuccess) return e;
+  float* s_out = s->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;  // only marks the shared expert
+  moe::FfnArgs a = ffn_args(x, xd, 1, L, s, nullptr, nullptr, nullptr, s_out, ws, W);
+  e = moe::launch_decode1_ffn(a, logits, idx, w, at<int32_t>(ws, W.header), out, residual, st);
+  if (e != hipSuccess || !next_in) return e;
+  return moe::launch_residual_rmsnorm(residual, 1, s->hidden, next_in, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,6 +433,9 @@ int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_lay
     int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, W.topk_idx);
     float* w = topk_w ? topk_w : at<float>(ws, W.topk_w);
     const moe_algo algo = pick_algo(opts, T);
+    if (decode1_ok(T, shape, algo))
+      return device_status(decode1(x, x_dtype, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st),
+                           "moe_layer_forward");
     if (fused_decode_ok(T, shape, algo))
       return device_status(fused_decode(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st),
                            "moe_layer_forward");

@@ -12,6 +12,29 @@
 
 namespace moe {
 
+// Sum of squares of a float4, in one fixed order (the combine and the
+// stand-alone residual RMSNorm must give the same bits).
+__device__ __forceinline__ float sumsq4(float4v r) {
+  return __builtin_fmaf(r[3], r[3], __builtin_fmaf(r[2], r[2], __builtin_fmaf(r[1], r[1], r[0] * r[0])));
+}
+
+// a = bf16_RNE(res / sqrt(ss_total / H + 1e-6)) for one row, ss per thread
+// accumulated over the float4 columns c = threadIdx.x, +256, ...
+__device__ __forceinline__ void rmsnorm_row(const float* __restrict__ res, int H, float ss, float* red,
+                                            uint16_t* __restrict__ next_in) {
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float denom = sqrtf((red[0] + red[1] + red[2] + red[3]) / float(H) + 1e-6f);
+  const int H4 = H / 4;
+  for (int c = threadIdx.x; c < H4; c += 256) {
+    const float4v r = reinterpret_cast<const float4v*>(res)[c];
+    uint16_t* dst = next_in + 4 * c;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[u] = f32_to_bf16_rne(r[u] / denom);
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ pos,
                                                      const float* __restrict__ w, const float* __restrict__ shared,
                                                      int H, int k, float* __restrict__ out, float* __restrict__ res,
@@ -28,14 +51,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int H4 = H / 4;
   float ss = 0.0f;
   for (int c = threadIdx.x; c < H4; c += 256) {
-    float4v acc = shared ? reinterpret_cast<const float4v*>(shared + t * H)[c] : float4v{0.f, 0.f, 0.f, 0.f};
-    // issue up to 8 row loads before using them (latency, not bandwidth, bounds one token)
+    // every load unconditional (clamped rows) so that they are in flight together: latency, not
+    // bandwidth, bounds one token.  y has at least T rows, so row t of it stands in for a
+    // missing shared output; out-of-range pairs (p < 0) read row 0 and add 0.
+    const float4v s4 = reinterpret_cast<const float4v*>((shared ? shared : y) + t * H)[c];
+    float4v acc = shared ? s4 : float4v{0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < k; j0 += 8) {
       float4v v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int p = j0 + i < k ? s_pos[j0 + i] : -1;
-        v[i] = p >= 0 ? reinterpret_cast<const float4v*>(y + int64_t(p) * H)[c] : float4v{0.f, 0.f, 0.f, 0.f};
+        const float4v l = reinterpret_cast<const float4v*>(y + int64_t(p >= 0 ? p : 0) * H)[c];
+        v[i] = p >= 0 ? l : float4v{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -48,20 +75,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       float4v r = reinterpret_cast<float4v*>(res + t * H)[c];
       r += acc;
       reinterpret_cast<float4v*>(res + t * H)[c] = r;
-      ss += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
+      ss += sumsq4(r);
     }
   }
   if (!res || !next_in) return;  // uniform across the workgroup
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float denom = sqrtf((red[0] + red[1] + red[2] + red[3]) / float(H) + 1e-6f);
-  for (int c = threadIdx.x; c < H4; c += 256) {
-    const float4v r = reinterpret_cast<const float4v*>(res + t * H)[c];
-    uint16_t* dst = next_in + t * H + 4 * c;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dst[u] = f32_to_bf16_rne(r[u] / denom);
-  }
+  rmsnorm_row(res + t * H, H, ss, red, next_in + t * H);
+}
+
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const float* __restrict__ res, int H,
+                                                              uint16_t* __restrict__ next_in) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const int H4 = H / 4;
+  float ss = 0.0f;
+  for (int c = threadIdx.x; c < H4; c += 256) ss += sumsq4(reinterpret_cast<const float4v*>(res + t * H)[c]);
+  rmsnorm_row(res + t * H, H, ss, red, next_in + t * H);
+}
+
+hipError_t launch_residual_rmsnorm(const float* res, int64_t T, int H, uint16_t* next_in, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  residual_rmsnorm_kernel<<<dim3(unsigned(T)), 256, 0, stream>>>(res, H, next_in);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,

@@ -159,28 +159,40 @@ __host__ __device__ __forceinline__ int perm16(int r) { return r < 8 ? 2 * r : 2
 // stored in the permuted 16-group order its MFMA operands use.
 __device__ __forceinline__ int hcol(int i) { return (i & ~15) | perm16(i & 15); }
 
-// 16 consecutive activations -> the two permuted fp16 MFMA k-slices.
+// 16 consecutive activations as loaded (bf16 or fp32), before conversion.
+// Loading and converting are separate steps so that a batch of loads is in
+// flight together: a conversion placed right after its load makes the wave
+// wait for that load alone.
 template <typename SRC>
-__device__ __forceinline__ void load_x16(const SRC* src, half8& lo, half8& hi) {
+struct Raw16 {
+  uint4v q[sizeof(SRC) == 4 ? 4 : 2];
+};
+
+template <typename SRC>
+__device__ __forceinline__ void load_raw16(const SRC* src, Raw16<SRC>& r) {
+  const uint4v* p = reinterpret_cast<const uint4v*>(src);
+#pragma unroll
+  for (int i = 0; i < int(sizeof(r.q) / sizeof(r.q[0])); ++i) r.q[i] = p[i];
+}
+
+// -> the two permuted fp16 MFMA k-slices (lo = weights {0,8,1,9,2,10,3,11},
+// hi = {4,12,5,13,6,14,7,15}).
+template <typename SRC>
+__device__ __forceinline__ void cvt_raw16(const Raw16<SRC>& r, half8& lo, half8& hi) {
   float v[16];
   if constexpr (sizeof(SRC) == 4) {
-    const float4v* p = reinterpret_cast<const float4v*>(src);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4v t = p[q];
-      v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
-    }
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[4 * q + u] = __uint_as_float(r.q[q][u]);
   } else {
-    const uint4v* p = reinterpret_cast<const uint4v*>(src);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint4v t = p[q];
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        v[8 * q + 2 * u] = __uint_as_float(t[u] << 16);
-        v[8 * q + 2 * u + 1] = __uint_as_float(t[u] & 0xffff0000u);
+        v[8 * q + 2 * u] = __uint_as_float(r.q[q][u] << 16);
+        v[8 * q + 2 * u + 1] = __uint_as_float(r.q[q][u] & 0xffff0000u);
       }
-    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -189,6 +201,13 @@ __device__ __forceinline__ void load_x16(const SRC* src, half8& lo, half8& hi) {
     hi[2 * i] = f16(v[4 + i]);
     hi[2 * i + 1] = f16(v[12 + i]);
   }
+}
+
+template <typename SRC>
+__device__ __forceinline__ void load_x16(const SRC* src, half8& lo, half8& hi) {
+  Raw16<SRC> r;
+  load_raw16(src, r);
+  cvt_raw16(r, lo, hi);
 }
 
 
@@ -301,6 +320,80 @@ __device__ inline int block_scan_fast(int* vals, int n, int* tmp) {
   }
   __syncthreads();
   return total;
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of one token's logits on one wave, ties to the lower expert index,
+// then the renormalised softmax weights of the selection.
+// ---------------------------------------------------------------------------
+// Inverse of float_key.
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// One wave: top-k of one token's logits.  Lane l holds experts l + 64v as
+// order-preserving keys.  Each round takes the largest key (DPP max), then
+// the lowest expert index holding it (a ballot per v, lowest v first, then
+// the lowest lane) and zeroes that key (0 is below every finite key).  Lane
+// j < k returns selection j; its value is recovered from the key (a -0
+// logit comes back as +0, which changes no weight).
+template <int V>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, float& my_val, int& my_idx) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[V];
+  float f[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) f[v] = row[min(lane + 64 * v, E - 1)];
+  // Pin every load as unconditional, so the V loads are in flight together
+  // (a load feeding only one side of a select is otherwise moved into a
+  // branch with its own wait).
+#pragma unroll
+  for (int v = 0; v < V; ++v) asm volatile("" : "+v"(f[v]));
+#pragma unroll
+  for (int v = 0; v < V; ++v) key[v] = lane + 64 * v < E ? float_key(f[v]) : 0u;
+  uint32_t my_key = 0;
+  my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    uint32_t bk = key[0];
+#pragma unroll
+    for (int v = 1; v < V; ++v) bk = max(bk, key[v]);
+    const uint32_t top = wave_max_u32(bk);
+    int win = -1;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      if (win < 0) {
+        const uint64_t m = __ballot(key[v] == top);
+        if (m) win = 64 * v + __builtin_ctzll(m);
+      }
+    }
+    const int owner = win & 63, wv_ = win >> 6;
+    if (lane == owner) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (v == wv_) key[v] = 0u;
+    }
+    if (lane == j) {
+      my_key = top;
+      my_idx = win;
+    }
+  }
+  my_val = key_float(my_key);
+}
+
+// Lane j < k returns selection j: its expert and weight
+// exp(l_j - l_0) / sum_{j' < k} exp(l_j' - l_0).  Every caller of the
+// layer's selection goes through this one function, so all paths pick the
+// same experts with the same weight bits.
+template <int V>
+__device__ __forceinline__ void wave_topk_softmax(const float* __restrict__ row, int E, int k, int& my_idx,
+                                                  float& my_w) {
+  float my_val;
+  wave_topk<V>(row, E, k, my_val, my_idx);
+  const float top = __shfl(my_val, 0, 64);
+  const int lane = threadIdx.x & 63;
+  const float p = lane < k ? expf(my_val - top) : 0.0f;
+  const float sum = wave_sum(p);
+  my_w = p / sum;
 }
 
 }  // namespace moe

@@ -140,62 +140,98 @@ __device__ __forceinline__ void dq_unit_word(const Unit<QBITS, UNIT>& U, int d, 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU.  grid = (ceil(max_rows / RPW), slots), block = 256.
+// Single-token gate/up + SwiGLU.  grid = (ceil(max_rows / 16), slots),
+// block = 256.
 //
 // Unit u of a row (64 or 32 weights) is read in round r' = u / 4 by lane
-// group g = u % 4.  Rounds fall in four classes c = r' % 4, each with its own
-// accumulator, summed at the end as ((c0 + c1) + c2) + c3.  With S = 4 the
-// four waves of a workgroup own the four classes of the same 16 rows (the
-// reduction axis split 4 ways: 4x more waves for single tokens) and the sum
-// goes through LDS; with S = 1 each wave owns 16 rows and all four classes
-// (64 rows per workgroup, staged activations reused by more rows).  Both
-// orders are the same, so a token's result does not depend on the batch.
-// The weight loads of a wave are issued before the activations are staged.
-// DIRECT (used with S = 4 for one token) reads the activations straight from
-// global memory into the MFMA operands, with no LDS and no barrier.
-// h is written in the permuted column order of the down projection.
+// group g = u % 4.  Rounds fall in four classes c = r' % 4: wave c of the
+// workgroup takes the rounds of class c for the workgroup's 16 rows (the
+// reduction axis split four ways: four times more waves for one token), and
+// the partial sums meet in LDS as ((c0 + c1) + c2) + c3 -- the order of the
+// multi-token kernels, so a token's result does not depend on the batch.
+// The activations (always token 0) go straight from global memory into the
+// MFMA operands: no LDS staging, and they are requested before anything
+// else.  h is written in the permuted column order of the down projection.
+//
+// Slot source.  With `logits` null, slot s of the slot table (standalone
+// expert FFN: h row = the pair's sorted position).  With `logits` set (the
+// fused decode layer), every wave selects the token's top-k itself from the
+// router logits (the shared selection routine, so the experts and weights
+// are those of every other path): slot j < k is the rank-j expert, h row j;
+// slot k is the shared expert.  Workgroup (0, 0) stores the selection.
 // ---------------------------------------------------------------------------
-template <int QBITS, int UNIT, int S, bool DIRECT, typename XT>
-__global__ __launch_bounds__(256) void gemv_gateup_kernel(FfnArgs a) {
-  static_assert(S == 1 || S == 4, "S is 1 or 4");
-  extern __shared__ __attribute__((aligned(16))) f16 xs[];
-  __shared__ float red[S > 1 ? 4 : 1][2][4][64];
-  constexpr int RPW = 64 / S;   // rows per workgroup
-  constexpr int NC = 4 / S;     // accumulator classes per wave
-  constexpr int RB = 8 / S;     // rounds per load batch
-  const int4 si = a.slots[blockIdx.y];
-  const int m_total = si.z;
-  if (m_total == 0) return;
-  const bool shared = si.x < 0;
+template <int QBITS, int UNIT, typename XT>
+__global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, const float* __restrict__ logits,
+                                                              int32_t* __restrict__ idx_out,
+                                                              float* __restrict__ w_out,
+                                                              int32_t* __restrict__ header) {
+  __shared__ float red[4][2][16];
+  constexpr int RB = 2;  // rounds per wave per load batch (rounds c and c + 4)
+  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int j = blockIdx.y;
+  const int H = a.H;
+  const int n_units = H / UNIT, rounds = (n_units + 3) / 4;
+  const XT* xg = static_cast<const XT*>(a.x);
+
+  // the first batch of activations, independent of the slot: raw loads now
+  // (clamped units, all in flight together), conversion once the weight
+  // loads are out
+  Raw16<XT> xr[RB][UNIT / 16];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    const int rp = i * 4 + ks, u = rp * 4 + g;
+    const int uc = rp < rounds && u < n_units ? u : 0;
+#pragma unroll
+    for (int d = 0; d < UNIT / 16; ++d) load_raw16(xg + uc * UNIT + 16 * d, xr[i][d]);
+  }
+
+  bool shared;
+  int64_t ex;
+  int hrow;
+  if (logits) {
+    shared = j >= a.k;
+    if (blockIdx.x * 16 >= (shared ? a.Is : a.I)) return;
+    ex = 0;
+    hrow = shared ? 0 : j;
+    if (!shared) {
+      int my_idx;
+      float my_w;
+      wave_topk_softmax<8>(logits, a.E, a.k, my_idx, my_w);
+      ex = __shfl(my_idx, j, 64);
+      if (blockIdx.x == 0 && j == 0 && ks == 0) {
+        if (lane < a.k) {
+          idx_out[lane] = my_idx;
+          w_out[lane] = my_w;
+        }
+        if (lane == 0) header[kHdrError] = 0;
+      }
+    }
+  } else {
+    const int4 si = a.slots[j];
+    if (si.z == 0) return;
+    shared = si.x < 0;
+    if (blockIdx.x * 16 >= (shared ? a.Is : a.I)) return;
+    ex = shared ? 0 : si.x;
+    hrow = shared ? 0 : si.y;
+  }
   const int rows = shared ? a.Is : a.I;
-  const int row_base = blockIdx.x * RPW;
-  if (row_base >= rows) return;
+  const int row = blockIdx.x * 16 + n;  // rows are multiples of 32: every row of the tile exists
   const QMat G = shared ? a.sg : a.rg;
   const QMat U = shared ? a.su : a.ru;
-  const int64_t ex = shared ? 0 : si.x;
   const uint8_t* gc = G.codes + ex * G.code_stride;
   const uint16_t* gs = G.scales + ex * G.scale_stride;
   const uint8_t* uc = U.codes + ex * U.code_stride;
   const uint16_t* us = U.scales + ex * U.scale_stride;
-  const int H = a.H, ldsw = H + 8;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int rg = wv / S, ks = wv % S;
-  const int n = lane & 15, g = lane >> 4;
-  const int row = row_base + rg * 16 + n;
-  const bool wave_on = row_base + rg * 16 < rows;
-  const int n_units = H / UNIT, rounds = (n_units + 3) / 4;  // rounds r' of 4 units
-  const XT* x = static_cast<const XT*>(a.x);
-  f16* hout = shared ? a.h_shared : a.h_routed;
-  const int hw = shared ? a.Is : a.I;
 
-  for (int mc = 0; mc < m_total; mc += kGemvMaxM) {
-    const int mnow = min(kGemvMaxM, m_total - mc);
-    // first load batch of this wave's weights, before anything waits
-    Unit<QBITS, UNIT> ug[RB], uu[RB];
+  Unit<QBITS, UNIT> ug[RB], uu[RB];
+  float4v accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  const bool a_on = n == 0;  // MFMA row 0 is the token; rows 1..15 are zero
+  for (int b0 = 0; b0 * 4 < rounds; b0 += RB) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int rp = i * S + ks, u = rp * 4 + g;
-      if (wave_on && rp < rounds && u < n_units) {
+      const int rp = (b0 + i) * 4 + ks, u = rp * 4 + g;
+      if (rp < rounds && u < n_units) {
         load_unit(ug[i], gc, gs, rows, H, row, u);
         load_unit(uu[i], uc, us, rows, H, row, u);
       } else {
@@ -203,129 +239,189 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(FfnArgs a) {
         zero_unit(uu[i]);
       }
     }
-    const bool a_on = n < mnow;  // this lane's A row (token) exists
-    // DIRECT: the whole first batch of this lane's activations, loaded now
-    half8 xa[DIRECT ? RB : 1][DIRECT ? UNIT / 16 : 1][2];
-    const XT* xg = nullptr;
-    if constexpr (DIRECT) {
-      if (a_on) xg = x + (shared ? int64_t(mc + n) : int64_t(a.sorted_pair[si.y + mc + n] / a.k)) * H;
+    if (b0 > 0) {  // later batches (hidden > 2048): their activations, loaded after the weights
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
-        const int rp = i * S + ks, u = rp * 4 + g;
+        const int rp = (b0 + i) * 4 + ks, u = rp * 4 + g;
+        const int ucl = rp < rounds && u < n_units ? u : 0;
 #pragma unroll
-        for (int d = 0; d < UNIT / 16; ++d) {
-          if (wave_on && a_on && rp < rounds && u < n_units) {
-            load_x16(xg + u * UNIT + 16 * d, xa[i][d][0], xa[i][d][1]);
-          } else {
-            xa[i][d][0] = half8{};
-            xa[i][d][1] = half8{};
-          }
-        }
+        for (int d = 0; d < UNIT / 16; ++d) load_raw16(xg + ucl * UNIT + 16 * d, xr[i][d]);
       }
-    } else {
-      __syncthreads();
-      for (int it = threadIdx.x; it < mnow * (H / 16); it += blockDim.x) {
-        const int r = it / (H / 16), gg = it - r * (H / 16);
-        const int64_t t = shared ? int64_t(mc + r) : int64_t(a.sorted_pair[si.y + mc + r] / a.k);
-        half8 lo, hi;
-        load_x16(x + t * H + gg * 16, lo, hi);
-        half8* dst = reinterpret_cast<half8*>(xs + r * ldsw + gg * 16);
-        dst[0] = lo;
-        dst[1] = hi;
-      }
-      __syncthreads();
     }
-    float4v accg[NC], accu[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) accg[c] = accu[c] = float4v{0.f, 0.f, 0.f, 0.f};
-    if (wave_on) {
-      const f16* xrow = xs + n * ldsw;
-      for (int b0 = 0; b0 * S < rounds; b0 += RB) {
-        if (b0 > 0) {
+    for (int i = 0; i < RB; ++i) {
+      const int rp = (b0 + i) * 4 + ks;
+      if (rp >= rounds) break;
+      const int u = rp * 4 + g;
+      const bool on = a_on && u < n_units;
 #pragma unroll
-          for (int i = 0; i < RB; ++i) {
-            const int rp = (b0 + i) * S + ks, u = rp * 4 + g;
-            if (rp < rounds && u < n_units) {
-              load_unit(ug[i], gc, gs, rows, H, row, u);
-              load_unit(uu[i], uc, us, rows, H, row, u);
-            } else {
-              zero_unit(ug[i]);
-              zero_unit(uu[i]);
-            }
-          }
-        }
+      for (int d = 0; d < UNIT / 16; ++d) {
+        half8 glo, ghi, ulo, uhi, alo = {}, ahi = {};
+        dq_unit_word(ug[i], d, glo, ghi);
+        dq_unit_word(uu[i], d, ulo, uhi);
+        if (on) cvt_raw16(xr[i][d], alo, ahi);
+        accg = mfma16(alo, glo, accg);
+        accg = mfma16(ahi, ghi, accg);
+        accu = mfma16(alo, ulo, accu);
+        accu = mfma16(ahi, uhi, accu);
+      }
+    }
+  }
+  // row 0 of the result: lanes 0..15, element 0
+  if (ks > 0 && lane < 16) {
+    red[ks][0][n] = accg[0];
+    red[ks][1][n] = accu[0];
+  }
+  __syncthreads();
+  if (ks == 0 && lane < 16) {
+    float sg = accg[0], su = accu[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      sg += red[q][0][n];
+      su += red[q][1][n];
+    }
+    f16* hout = shared ? a.h_shared : a.h_routed;
+    hout[int64_t(hrow) * rows + hcol(row)] = f16(silu_f(sg) * su);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Single-token down projection of the k selected experts and the shared
+// expert, combined inside the workgroup (the fused decode layer):
+//   out[r] = shared[r] + sum_{j<k} w_j * y_j[r]
+// in the combine's order (shared first, then ranks 0..k-1, one fma each).
+// grid = H / 16, block = 64 * NW: wave w takes slots w, w + NW, ... (slot
+// j < k = rank j, h row j; slot k = shared) and computes 16 output rows of
+// its slot with the same MFMA sequence as the standalone down kernel.  The
+// weight loads of a wave's first slot go out first; meanwhile the workgroup
+// copies the h rows of all slots into LDS (their addresses depend on
+// nothing), and the MFMA operands are read from there.  The rows of all
+// slots meet in LDS for the combine.
+// ---------------------------------------------------------------------------
+struct DownSlot {
+  const uint8_t* dc;
+  const uint16_t* ds;
+  int K, n_units, rounds;
+};
+
+// Down weights of slot s of the fused single-token layer (s < k: the rank-s
+// expert; s == k: the shared expert).
+template <int UNIT>
+__device__ __forceinline__ DownSlot down_slot(const FfnArgs& a, const int32_t* __restrict__ idx, int s) {
+  const bool shared = s >= a.k;
+  const QMat D = shared ? a.sd : a.rd;
+  const int64_t ex = shared ? 0 : idx[s];
+  DownSlot r;
+  r.K = shared ? a.Is : a.I;
+  r.dc = D.codes + ex * D.code_stride;
+  r.ds = D.scales + ex * D.scale_stride;
+  r.n_units = r.K / UNIT;
+  r.rounds = (r.n_units + 3) / 4;
+  return r;
+}
+
+template <int QBITS, int UNIT>
+__global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a, const int32_t* __restrict__ idx,
+                                                                     const float* __restrict__ w,
+                                                                     float* __restrict__ out,
+                                                                     float* __restrict__ res, int ldh) {
+  extern __shared__ __attribute__((aligned(16))) f16 hs[];  // [n_slots][ldh]
+  __shared__ float ys[kMaxTopK + 1][16];
+  __shared__ float s_w[kMaxTopK];
+  constexpr int RB = 4;
+  const int nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int H = a.H;
+  const int row = blockIdx.x * 16 + n;  // H is a multiple of 32
+  const int n_slots = a.k + (a.has_shared ? 1 : 0);
+  if (threadIdx.x < a.k) s_w[threadIdx.x] = w[threadIdx.x];
+
+  Unit<QBITS, UNIT> ud[RB];
+  DownSlot sl{};
+  if (wv < n_slots) {
+    sl = down_slot<UNIT>(a, idx, wv);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int u = i * 4 + g;
+      if (i < sl.rounds && u < sl.n_units) load_unit(ud[i], sl.dc, sl.ds, H, sl.K, row, u);
+      else zero_unit(ud[i]);
+    }
+  }
+  // h rows of every slot -> LDS, 16 bytes per item, all loads of a thread first
+  {
+    const int ch = ldh / 8;  // 16-byte chunks per LDS row (covers the longest K)
+    const int items = n_slots * ch;
+    for (int base = 0; base < items; base += 4 * int(blockDim.x)) {
+      half8 v[4];
+      bool on[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int it = base + q * int(blockDim.x) + int(threadIdx.x);
+        const int s = min(it, items - 1) / ch, c = min(it, items - 1) - s * ch;
+        const int Ks = s >= a.k ? a.Is : a.I;
+        on[q] = it < items && 8 * c < Ks;
+        const f16* src = s >= a.k ? a.h_shared : a.h_routed + int64_t(s) * Ks;
+        v[q] = *reinterpret_cast<const half8*>(src + (8 * c < Ks ? 8 * c : 0));  // unconditional (clamped)
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int it = base + q * int(blockDim.x) + int(threadIdx.x);
+        if (on[q]) *reinterpret_cast<half8*>(hs + it / ch * ldh + 8 * (it % ch)) = v[q];
+      }
+    }
+  }
+  __syncthreads();
+
+  const bool a_on = n == 0;  // MFMA row 0 is the token; rows 1..15 are zero
+  for (int s = wv; s < n_slots; s += nw) {
+    if (s != wv) {
+      sl = down_slot<UNIT>(a, idx, s);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int u = i * 4 + g;
+        if (i < sl.rounds && u < sl.n_units) load_unit(ud[i], sl.dc, sl.ds, H, sl.K, row, u);
+        else zero_unit(ud[i]);
+      }
+    }
+    const f16* hrow = hs + s * ldh;
+    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < sl.rounds; r0 += RB) {
+      if (r0 > 0) {
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
-          const int rp = (b0 + i) * S + ks;
-          if (rp >= rounds) break;
-          const int c = (b0 + i) % NC;  // class of round rp: ks (S = 4) or i % 4 (S = 1)
-          const int u = rp * 4 + g;
-          const bool on = a_on && u < n_units;
+          const int u = (r0 + i) * 4 + g;
+          if (r0 + i < sl.rounds && u < sl.n_units) load_unit(ud[i], sl.dc, sl.ds, H, sl.K, row, u);
+          else zero_unit(ud[i]);
+        }
+      }
 #pragma unroll
-          for (int d = 0; d < UNIT / 16; ++d) {
-            half8 glo, ghi, ulo, uhi, alo = {}, ahi = {};
-            dq_unit_word(ug[i], d, glo, ghi);
-            dq_unit_word(uu[i], d, ulo, uhi);
-            if constexpr (DIRECT) {
-              if (b0 == 0) {
-                alo = xa[i][d][0];
-                ahi = xa[i][d][1];
-              } else if (on) {
-                load_x16(xg + u * UNIT + 16 * d, alo, ahi);
-              }
-            } else if (on) {
-              {
-                const half8* ap = reinterpret_cast<const half8*>(xrow + u * UNIT + 16 * d);
-                alo = ap[0];
-                ahi = ap[1];
-              }
-            }
-            accg[c] = mfma16(alo, glo, accg[c]);
-            accg[c] = mfma16(ahi, ghi, accg[c]);
-            accu[c] = mfma16(alo, ulo, accu[c]);
-            accu[c] = mfma16(ahi, uhi, accu[c]);
+      for (int i = 0; i < RB; ++i) {
+        if (r0 + i >= sl.rounds) break;
+        const int u = (r0 + i) * 4 + g;
+        const bool on = a_on && u < sl.n_units;
+#pragma unroll
+        for (int d = 0; d < UNIT / 16; ++d) {
+          half8 blo, bhi, alo = {}, ahi = {};
+          dq_unit_word(ud[i], d, blo, bhi);
+          if (on) {
+            const half8* ap = reinterpret_cast<const half8*>(hrow + u * UNIT + 16 * d);
+            alo = ap[0];
+            ahi = ap[1];
           }
+          acc = mfma16(alo, blo, acc);
+          acc = mfma16(ahi, bhi, acc);
         }
       }
     }
-    float4v sg = accg[0], su = accu[0];
-    if constexpr (S == 1) {
-#pragma unroll
-      for (int c = 1; c < 4; ++c) {
-        sg += accg[c];
-        su += accu[c];
-      }
-    } else {
-      if (ks > 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          red[wv][0][j][lane] = accg[0][j];
-          red[wv][1][j][lane] = accu[0][j];
-        }
-      }
-      __syncthreads();
-      if (ks == 0) {
-#pragma unroll
-        for (int q = 1; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            sg[j] += red[wv + q][0][j][lane];
-            su[j] += red[wv + q][1][j][lane];
-          }
-      }
-      __syncthreads();  // red is reused by the next token chunk
-    }
-    if (wave_on && ks == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = 4 * g + j;
-        if (m < mnow) {
-          const float hv = silu_f(sg[j]) * su[j];
-          const int64_t hr = shared ? int64_t(mc + m) : int64_t(si.y + mc + m);
-          hout[hr * hw + hcol(row)] = f16(hv);
-        }
-      }
-    }
+    if (lane < 16) ys[s][n] = acc[0];
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float v = a.has_shared ? ys[a.k][n] : 0.0f;
+    for (int j = 0; j < a.k; ++j) v = __builtin_fmaf(s_w[j], ys[j][n], v);
+    if (out) out[row] = v;
+    if (res) res[row] += v;
   }
 }
 
@@ -361,7 +457,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
   for (int mc = 0; mc < m_total; mc += kGemvMaxM) {
     const int mnow = min(kGemvMaxM, m_total - mc);
     const bool a_on = n < mnow;
-    const f16* hrow = hin + (shared ? int64_t(mc + n) : int64_t(si.y + mc + n)) * K;
+    const int nr = a_on ? n : 0;  // rows past the tokens read token 0's row (loads are unconditional)
+    const f16* hrow = hin + (shared ? int64_t(mc + nr) : int64_t(si.y + mc + nr)) * K;
     float4v acc = {0.f, 0.f, 0.f, 0.f};
     for (int r0 = 0; r0 < rounds; r0 += RB) {
       Unit<QBITS, UNIT> ud[RB];
@@ -376,16 +473,13 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
       for (int i = 0; i < RB; ++i) {
         const int u = (r0 + i) * 4 + g;
         const bool on = a_on && r0 + i < rounds && u < n_units;
+        const int uc = on ? u : 0;  // unconditional loads from a clamped unit
 #pragma unroll
         for (int d = 0; d < UNIT / 16; ++d) {
-          if (on) {
-            const half8* ap = reinterpret_cast<const half8*>(hrow + u * UNIT + 16 * d);
-            av[i][d][0] = ap[0];
-            av[i][d][1] = ap[1];
-          } else {
-            av[i][d][0] = half8{};
-            av[i][d][1] = half8{};
-          }
+          const half8* ap = reinterpret_cast<const half8*>(hrow + uc * UNIT + 16 * d);
+          const half8 l0 = ap[0], l1 = ap[1];
+          av[i][d][0] = on ? l0 : half8{};
+          av[i][d][1] = on ? l1 : half8{};
         }
       }
 #pragma unroll
@@ -472,14 +566,39 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
       }
     }
     __syncthreads();
-    for (int it = threadIdx.x; it < mnow * (H / 16); it += blockDim.x) {
-      const int r = it / (H / 16), gg = it - r * (H / 16);
-      const int64_t t = shared ? int64_t(mc + r) : int64_t(a.sorted_pair[si.y + mc + r] / a.k);
-      half8 lo, hi;
-      load_x16(x + t * H + gg * 16, lo, hi);
-      half8* dst = reinterpret_cast<half8*>(xs + r * ldsw + gg * 16);
-      dst[0] = lo;
-      dst[1] = hi;
+    {
+      // stage the tokens: per thread NB items at a time, the token ids, then
+      // the activation loads, then the conversions, each step as one batch
+      constexpr int NB = sizeof(XT) == 4 ? 4 : 8;
+      const int chunks = H / 16, items = mnow * chunks;
+      for (int base = 0; base < items; base += NB * int(blockDim.x)) {
+        int64_t tok[NB];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int it = min(base + q * int(blockDim.x) + int(threadIdx.x), items - 1);
+          const int r = it / chunks;
+          tok[q] = shared ? int64_t(mc + r) : int64_t(a.sorted_pair[si.y + mc + r] / a.k);
+        }
+        Raw16<XT> raw[NB];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int it = min(base + q * int(blockDim.x) + int(threadIdx.x), items - 1);
+          const int r = it / chunks, gg = it - r * chunks;
+          load_raw16(x + tok[q] * H + gg * 16, raw[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int it = base + q * int(blockDim.x) + int(threadIdx.x);
+          if (it < items) {
+            const int r = it / chunks, gg = it - r * chunks;
+            half8 lo, hi;
+            cvt_raw16(raw[q], lo, hi);
+            half8* dst = reinterpret_cast<half8*>(xs + r * ldsw + gg * 16);
+            dst[0] = lo;
+            dst[1] = hi;
+          }
+        }
+      }
     }
     __syncthreads();
     float4v accg[4], accu[4];
@@ -572,11 +691,29 @@ __global__ __launch_bounds__(64 * NW) void gemv_down_tp_kernel(FfnArgs a, int ld
       else zero_unit(ud[i]);
     }
     __syncthreads();
-    // h rows are already in the MFMA operand order: plain 16-byte copies
-    for (int it = threadIdx.x; it < mnow * (K / 8); it += blockDim.x) {
-      const int r = it / (K / 8), c8 = it - r * (K / 8);
-      const int64_t hr = shared ? int64_t(mc + r) : int64_t(si.y + mc + r);
-      *reinterpret_cast<half8*>(hs + r * ldsw + c8 * 8) = *reinterpret_cast<const half8*>(hin + hr * K + c8 * 8);
+    {
+      // h rows are already in the MFMA operand order: plain 16-byte copies,
+      // NB loads in flight per thread before their stores
+      constexpr int NB = 8;
+      const int chunks = K / 8, items = mnow * chunks;
+      for (int base = 0; base < items; base += NB * int(blockDim.x)) {
+        half8 v[NB];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int it = min(base + q * int(blockDim.x) + int(threadIdx.x), items - 1);
+          const int r = it / chunks, c8 = it - r * chunks;
+          const int64_t hr = shared ? int64_t(mc + r) : int64_t(si.y + mc + r);
+          v[q] = *reinterpret_cast<const half8*>(hin + hr * K + c8 * 8);
+        }
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const int it = base + q * int(blockDim.x) + int(threadIdx.x);
+          if (it < items) {
+            const int r = it / chunks, c8 = it - r * chunks;
+            *reinterpret_cast<half8*>(hs + r * ldsw + c8 * 8) = v[q];
+          }
+        }
+      }
     }
     __syncthreads();
     if (!wave_on) continue;
@@ -627,7 +764,8 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
     const bool u64 = a.H % 64 == 0;
     if (one) {
       const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
-#define GU(U_, X_) gemv_gateup_kernel<QBITS, U_, 4, true, X_><<<grid, 256, 0, stream>>>(a)
+#define GU(U_, X_) \
+  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 256, 0, stream>>>(a, nullptr, nullptr, nullptr, nullptr)
       if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
       else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
@@ -662,6 +800,38 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases) {
   if (a.T == 0) return hipSuccess;
   return a.qbits == 2 ? launch_gemv_q<2>(a, stream, phases) : launch_gemv_q<3>(a, stream, phases);
+}
+
+template <int QBITS>
+static hipError_t launch_decode1_q(const FfnArgs& a, const float* logits, int32_t* idx, float* w, int32_t* header,
+                                   float* out, float* res, hipStream_t stream) {
+  const int slots = a.k + (a.has_shared ? 1 : 0);
+  const int max_rows = std::max(a.I, a.has_shared ? a.Is : 0);
+  {
+    const bool u64 = a.H % 64 == 0;
+    const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
+#define GU(U_, X_) gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 256, 0, stream>>>(a, logits, idx, w, header)
+    if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+    else { if (u64) GU(64, float); else GU(32, float); }
+#undef GU
+  }
+  {
+    const bool u64 = a.I % 64 == 0 && (!a.has_shared || a.Is % 64 == 0);
+    const int nw = std::min(slots, 12);  // within the kernel's 768-thread bound
+    const dim3 grid(unsigned(a.H / 16));
+    const int ldh = std::max(a.I, a.has_shared ? a.Is : 0) + 8;
+    const size_t lds = size_t(slots) * ldh * sizeof(_Float16);
+    if (u64) gemv_down_combine_1tok_kernel<QBITS, 64><<<grid, 64 * nw, lds, stream>>>(a, idx, w, out, res, ldh);
+    else gemv_down_combine_1tok_kernel<QBITS, 32><<<grid, 64 * nw, lds, stream>>>(a, idx, w, out, res, ldh);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode1_ffn(const FfnArgs& a, const float* logits, int32_t* idx, float* w, int32_t* header,
+                              float* out, float* res, hipStream_t stream) {
+  if (a.E > kDecode1MaxExperts || a.T != 1) return hipErrorInvalidValue;
+  return a.qbits == 2 ? launch_decode1_q<2>(a, logits, idx, w, header, out, res, stream)
+                      : launch_decode1_q<3>(a, logits, idx, w, header, out, res, stream);
 }
 
 }  // namespace moe

@@ -78,6 +78,15 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases);
 // kGroupedBM); max_tiles bounds the list for the launch grid.
 constexpr int kGroupedBM = 128;
 hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases);
+// The fused single-token decode FFN (needs E <= kDecode1MaxExperts): gate/up
+// with the selection made from `logits` in every workgroup (writes idx, w and
+// clears the error word), then down + combine into out and/or res.
+constexpr int kDecode1MaxExperts = 512;
+hipError_t launch_decode1_ffn(const FfnArgs& a, const float* logits, int32_t* idx, float* w, int32_t* header,
+                              float* out, float* res, hipStream_t stream);
+// res[t] -> a[t] = bf16_RNE(res[t] / sqrt(mean(res[t]^2) + 1e-6)) with the
+// reduction order of the combine kernel (so both give the same bits).
+hipError_t launch_residual_rmsnorm(const float* res, int64_t T, int H, uint16_t* next_in, hipStream_t stream);
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                           const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
                           uint16_t* next_in, hipStream_t stream);

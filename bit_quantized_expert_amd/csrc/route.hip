@@ -136,11 +136,14 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
   for (int kb0 = wv; kb0 < nkb; kb0 += 8 * B) {
     uint4v bw[B], ax[B];
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
+    for (int i = 0; i < B; ++i) {  // unconditional loads (clamped block, rows clamped above)
       const int kb = kb0 + 8 * i;
       const bool in = kb < nkb;
-      bw[i] = (in && b_on) ? *reinterpret_cast<const uint4v*>(wrow + kb * 32) : uint4v{0u, 0u, 0u, 0u};
-      ax[i] = (in && a_on) ? *reinterpret_cast<const uint4v*>(xrow + kb * 32) : uint4v{0u, 0u, 0u, 0u};
+      const int kbc = in ? kb : 0;
+      const uint4v wl = *reinterpret_cast<const uint4v*>(wrow + kbc * 32);
+      const uint4v xl = *reinterpret_cast<const uint4v*>(xrow + kbc * 32);
+      bw[i] = (in && b_on) ? wl : uint4v{0u, 0u, 0u, 0u};
+      ax[i] = (in && a_on) ? xl : uint4v{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < B; ++i)

@@ -14,55 +14,6 @@ namespace moe {
 
 constexpr int kSelMaxT = 16;
 
-// One wave: top-k of one token's logits.  Lane l holds experts l + 64v.
-// Each round takes the largest key (DPP max), then the lowest expert index
-// among the lanes holding it (DPP min).  Lane j < k returns selection j.
-template <int V>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, float& my_val, int& my_idx) {
-  const int lane = threadIdx.x & 63;
-  float val[V];
-  uint32_t key[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int e = lane + 64 * v;
-    val[v] = e < E ? row[e] : 0.0f;
-    key[v] = e < E ? float_key(val[v]) : 0u;  // 0 is below every real key
-  }
-  uint64_t taken = 0;
-#pragma unroll
-  for (int v = 0; v < V; ++v)
-    if (lane + 64 * v >= E) taken |= 1ull << v;
-  my_val = 0.0f;
-  my_idx = 0;
-  for (int j = 0; j < k; ++j) {
-    // best (largest key, then lowest index) of this lane; lower v = lower index
-    uint32_t bk = 0;
-    int bv = -1;
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (!((taken >> v) & 1ull) && (bv < 0 || key[v] > bk)) {
-        bk = key[v];
-        bv = v;
-      }
-    const uint32_t top = wave_max_u32(bv >= 0 ? bk : 0u);
-    const uint32_t cand = (bv >= 0 && bk == top) ? uint32_t(lane + 64 * bv) : 0xffffffffu;
-    const uint32_t win = wave_min_u32(cand);  // uniform: the winning expert id
-    const int owner = int(win & 63), wv_ = int(win >> 6);
-    float wval = 0.0f;
-    if (lane == owner) {
-      taken |= 1ull << wv_;
-#pragma unroll
-      for (int q = 0; q < V; ++q)
-        if (q == wv_) wval = val[q];
-    }
-    wval = __shfl(wval, owner, 64);
-    if (lane == j) {
-      my_val = wval;
-      my_idx = int(win);
-    }
-  }
-}
-
 template <int V>
 __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                            int has_shared, int32_t* __restrict__ idx_out,
@@ -80,15 +31,12 @@ __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restr
 
   // ---- top-k of token wv (one wave per token)
   if (wv < T) {
-    float my_val;
     int my_idx;
-    wave_topk<V>(logits + int64_t(wv) * E, E, k, my_val, my_idx);
-    const float top = __shfl(my_val, 0, 64);
-    const float p = lane < k ? expf(my_val - top) : 0.0f;
-    const float sum = wave_sum(p);
+    float my_w;
+    wave_topk_softmax<V>(logits + int64_t(wv) * E, E, k, my_idx, my_w);
     if (lane < k) {
       idx_out[wv * k + lane] = my_idx;
-      w_out[wv * k + lane] = p / sum;
+      w_out[wv * k + lane] = my_w;
       s_idx[wv * k + lane] = my_idx;
     }
   }

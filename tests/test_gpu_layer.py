@@ -60,6 +60,12 @@ RAGGED = [
     ("r3", 128, 160, 12, 4, 0, 2, 21, torch.bfloat16),
     ("r4", 64, 32, 8, 2, 32, 3, 4, torch.float32),
     ("r5", 256, 192, 33, 8, 96, 3, 17, torch.bfloat16),
+    # single-token layers (the fused one-token path), 64- and 32-weight units
+    ("s1", 96, 96, 5, 3, 64, 2, 1, torch.bfloat16),
+    ("s2", 64, 32, 8, 2, 32, 3, 1, torch.float32),
+    ("s3", 128, 160, 12, 4, 0, 2, 1, torch.bfloat16),
+    ("s4", 256, 192, 33, 8, 96, 3, 1, torch.bfloat16),
+    ("s5", 192, 128, 40, 32, 64, 2, 1, torch.bfloat16),
 ]
 
 
@@ -101,7 +107,7 @@ def test_decode16_layer_and_batch_invariance():
         assert np.array_equal(out_t[0], out_all[t]), f"token {t} depends on the rest of the batch"
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode16"])
+@pytest.mark.parametrize("name", ["tiny", "decode16", "decode1"])
 def test_stepwise_api_matches_layer_forward(name):
     """The four single-step entry points (separate kernels) and the fused
     decode layer give the same bits."""
@@ -130,6 +136,41 @@ def test_stepwise_api_matches_layer_forward(name):
     ref = dl.oracle_forward(x_to_numpy(x), idx=idx.cpu().numpy(), return_all=True)
     assert_close_output(y.cpu().numpy(), ref["y"], "y_sorted")
     assert_close_output(so.cpu().numpy(), ref["shared"], "shared_out")
+
+
+def test_single_token_glue_matches_batch():
+    """One token through the layer with the residual + RMSNorm + bf16 glue
+    (the single-token path) gives the same out, residual and next input bits
+    as the same token inside a 16-token batch."""
+    M = _M()
+    wl = synth.WORKLOADS["decode16"]
+    s = wl.shape
+    dl = _layer(wl, layer=0)
+    x = synth.tokens(wl, "cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    r0 = torch.randn(16, s.hidden, device="cuda", generator=g)
+
+    def run(xx, rr):
+        T = xx.shape[0]
+        ws = M.alloc_workspace(s, T)
+        out = torch.empty(T, s.hidden, device="cuda")
+        a = torch.empty(T, s.hidden, dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty(T, s.top_k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, s.top_k, device="cuda")
+        M.layer_forward(xx, dl.q, s, out=out, residual=rr, next_in=a, topk_idx=idx, topk_w=w, ws=ws)
+        torch.cuda.synchronize()
+        return out, a, idx, w
+
+    r_all = r0.clone()
+    out_all, a_all, idx_all, w_all = run(x, r_all)
+    for t in (0, 9, 15):
+        r_t = r0[t:t + 1].clone()
+        out_t, a_t, idx_t, w_t = run(x[t:t + 1].contiguous(), r_t)
+        assert torch.equal(idx_t[0], idx_all[t]) and torch.equal(w_t[0], w_all[t])
+        assert torch.equal(out_t[0], out_all[t]), f"token {t}: out"
+        assert torch.equal(r_t[0], r_all[t]), f"token {t}: residual"
+        assert torch.equal(a_t[0], a_all[t]), f"token {t}: next input"
 
 
 def test_zero_tokens_is_a_noop():
