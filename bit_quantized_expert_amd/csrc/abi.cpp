@@ -47,7 +47,7 @@ struct WsLayout {
   size_t header, slots, tile_expert, tile_m0, chunk_hist, h_routed, h_shared;
   size_t end_perm, end_ffn;
   size_t logits, end_route;
-  size_t topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos, y_sorted, shared_out, total;
+  size_t topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos, slot_expert, y_sorted, shared_out, total;
   int64_t max_tiles;
 };
 
@@ -81,6 +81,7 @@ WsLayout ws_layout(const moe_shape& s, int64_t T) {
   L.offsets = take(size_t(E + 1) * 4);
   L.sorted_pair = take(size_t(P) * 4);
   L.pair_pos = take(size_t(P) * 4);
+  L.slot_expert = take(size_t(moe::kMaxTopK) * 4);
   L.y_sorted = take(size_t(P) * s.hidden * 4);
   L.shared_out = take(s.shared_inter > 0 ? size_t(T) * s.hidden * 4 : 0);
   L.total = off;
@@ -297,7 +298,9 @@ hipError_t decode1(const void* x, moe_dtype xd, const moe_layer* L, const moe_sh
   if (e != hipSuccess) return e;
   float* s_out = s->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;  // only marks the shared expert
   moe::FfnArgs a = ffn_args(x, xd, 1, L, s, nullptr, nullptr, nullptr, s_out, ws, W);
-  e = moe::launch_decode1_ffn(a, logits, idx, w, at<int32_t>(ws, W.header), out, residual, st);
+  const moe::Decode1Sel sel{logits, idx, w, at<int32_t>(ws, W.pair_pos), at<int32_t>(ws, W.slot_expert),
+                            at<int32_t>(ws, W.header)};
+  e = moe::launch_decode1_ffn(a, sel, out, residual, st);
   if (e != hipSuccess || !next_in) return e;
   return moe::launch_residual_rmsnorm(residual, 1, s->hidden, next_in, st);
 }

@@ -17,6 +17,7 @@ typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 32;  // weights per quantisation block
+constexpr int kMaxTopKLds = 32;  // top-k entries a wave can rank (the library's largest k)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
@@ -331,16 +332,60 @@ __device__ __forceinline__ float key_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-// One wave: top-k of one token's logits.  Lane l holds experts l + 64v as
-// order-preserving keys.  Each round takes the largest key (DPP max), then
-// the lowest expert index holding it (a ballot per v, lowest v first, then
-// the lowest lane) and zeroes that key (0 is below every finite key).  Lane
-// j < k returns selection j; its value is recovered from the key (a -0
-// logit comes back as +0, which changes no weight).
+// Set bits of m below this lane.
+__device__ __forceinline__ int bits_below(uint64_t m) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+}
+
+// Lanes whose v >= t, as a mask in its own scalar register pair.  Written
+// out so that the compares go to distinct registers and issue back to back
+// (four per statement): compares through the shared VCC register, or each
+// followed by its bit count, serialise on the vector-to-scalar latency.
+__device__ __forceinline__ uint64_t ballot_ge(uint32_t v, uint32_t t) {
+  uint64_t m;
+  asm("v_cmp_le_u32_e64 %0, %1, %2" : "=s"(m) : "s"(t), "v"(v));
+  return m;
+}
+
+__device__ __forceinline__ void ballot_ge4(const uint32_t* v, uint32_t t, uint64_t* m) {
+  asm("v_cmp_le_u32_e64 %0, %4, %5\n\t"
+      "v_cmp_le_u32_e64 %1, %4, %6\n\t"
+      "v_cmp_le_u32_e64 %2, %4, %7\n\t"
+      "v_cmp_le_u32_e64 %3, %4, %8"
+      : "=&s"(m[0]), "=&s"(m[1]), "=&s"(m[2]), "=&s"(m[3])
+      : "s"(t), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+}
+
+// Number of keys >= t over the wave.
 template <int V>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, float& my_val, int& my_idx) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&key)[V], uint32_t t) {
+  uint64_t m[V];
+  if constexpr (V % 4 == 0) {
+#pragma unroll
+    for (int v = 0; v < V; v += 4) ballot_ge4(key + v, t, m + v);
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) m[v] = ballot_ge(key[v], t);
+  }
+  int c = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) c += __builtin_popcountll(m[v]);
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of one token's E logits on one wave: ranks ordered by (logit desc,
+// expert index asc).  Lane l holds experts l + 64v (v < V) as
+// order-preserving keys; 0 marks padding (every real key is >= 1).
+// ---------------------------------------------------------------------------
+template <int V>
+struct WaveKeys {
   uint32_t key[V];
+};
+
+template <int V>
+__device__ __forceinline__ void wave_keys(const float* __restrict__ row, int E, WaveKeys<V>& K) {
+  const int lane = threadIdx.x & 63;
   float f[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) f[v] = row[min(lane + 64 * v, E - 1)];
@@ -350,50 +395,154 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
 #pragma unroll
   for (int v = 0; v < V; ++v) asm volatile("" : "+v"(f[v]));
 #pragma unroll
-  for (int v = 0; v < V; ++v) key[v] = lane + 64 * v < E ? float_key(f[v]) : 0u;
-  uint32_t my_key = 0;
-  my_idx = 0;
-  for (int j = 0; j < k; ++j) {
-    uint32_t bk = key[0];
-#pragma unroll
-    for (int v = 1; v < V; ++v) bk = max(bk, key[v]);
-    const uint32_t top = wave_max_u32(bk);
-    int win = -1;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      if (win < 0) {
-        const uint64_t m = __ballot(key[v] == top);
-        if (m) win = 64 * v + __builtin_ctzll(m);
-      }
-    }
-    const int owner = win & 63, wv_ = win >> 6;
-    if (lane == owner) {
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (v == wv_) key[v] = 0u;
-    }
-    if (lane == j) {
-      my_key = top;
-      my_idx = win;
-    }
-  }
-  my_val = key_float(my_key);
+  for (int v = 0; v < V; ++v) K.key[v] = lane + 64 * v < E ? float_key(f[v]) : 0u;
 }
 
-// Lane j < k returns selection j: its expert and weight
-// exp(l_j - l_0) / sum_{j' < k} exp(l_j' - l_0).  Every caller of the
-// layer's selection goes through this one function, so all paths pick the
-// same experts with the same weight bits.
+// The selected set, as one lane mask per v: the k largest keys, ties at the
+// k-th place going to the lowest expert indices.
+//  1. The k-th largest key T by bisection, keeping count(>= lo) >= k and
+//     count(>= hi + 1) < k with one ballot count per step; a cut point whose
+//     count is exactly k ends it (the keys >= it are the top-k).  The search
+//     starts at hi = the largest key and lo = the smallest maximum over 64/G
+//     disjoint groups of G lanes, G the largest power of two with 64/G >= k
+//     (at least 64/G >= k keys are >= lo).
+//  2. Keys > T, then the lowest-index keys == T up to k.
 template <int V>
-__device__ __forceinline__ void wave_topk_softmax(const float* __restrict__ row, int E, int k, int& my_idx,
-                                                  float& my_w) {
-  float my_val;
-  wave_topk<V>(row, E, k, my_val, my_idx);
+__device__ __forceinline__ void wave_select(const WaveKeys<V>& K, int k, uint64_t (&msel)[V]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t bk = K.key[0];
+#pragma unroll
+  for (int v = 1; v < V; ++v) bk = max(bk, K.key[v]);
+  // group maxima: G lanes per group through the same DPP steps as wave_max_u32
+  const int G = k <= 2 ? 32 : k <= 4 ? 16 : k <= 8 ? 8 : k <= 16 ? 4 : 2;  // k <= 32
+  uint32_t gm = bk;
+  if (G >= 2) gm = max(gm, dpp_u32<0xb1>(gm));   // quad_perm [1,0,3,2]: pairs
+  if (G >= 4) gm = max(gm, dpp_u32<0x4e>(gm));   // quad_perm [2,3,0,1]: quads
+  if (G >= 8) gm = max(gm, dpp_u32<0x124>(gm));  // row_ror:4: lanes 8i hold 8-lane groups
+  if (G >= 16) gm = max(gm, dpp_u32<0x128>(gm)); // row_ror:8: lanes 16i hold rows
+  uint32_t hi = wave_max_u32(bk);
+  // k <= 2 (G >= 32): no group step; the search starts from the whole key range
+  uint32_t lo = G >= 32 ? 1u : max(wave_min_u32(lane % G == 0 ? gm : 0xffffffffu), 1u);
+  bool exact = false;
+  while (lo < hi) {
+    // cut at the midpoint of the logit values (a few steps cover the span
+    // of the logits); when that does not split the key range, at the
+    // midpoint of the keys (exact termination whatever the values)
+    uint32_t mid = float_key(0.5f * key_float(lo) + 0.5f * key_float(hi));
+    if (mid <= lo || mid > hi) mid = lo + (hi - lo + 1u) / 2u;
+    const int c = wave_count_ge<V>(K.key, mid);
+    if (c == k) {
+      lo = mid;
+      exact = true;
+      break;
+    }
+    if (c > k) lo = mid;
+    else hi = mid - 1u;
+  }
+  if (exact) {
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+      for (int v = 0; v < V; v += 4) ballot_ge4(K.key + v, lo, msel + v);
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v) msel[v] = ballot_ge(K.key[v], lo);
+    }
+  } else {
+    const int need = k - wave_count_ge<V>(K.key, lo + 1u);  // keys == lo to take, lowest index first
+    int before = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const uint64_t eq = __ballot(K.key[v] == lo);
+      msel[v] = __ballot(K.key[v] > lo || (K.key[v] == lo && before + bits_below(eq) < need));
+      before += __builtin_popcountll(eq);
+    }
+  }
+}
+
+// Expert index of the n-th selected expert in index order (wave-uniform):
+// the v holding it from the mask counts (scalar), then its lane from one
+// ballot.
+template <int V>
+__device__ __forceinline__ int wave_nth_selected(const uint64_t (&msel)[V], int n) {
+  const int lane = threadIdx.x & 63;
+  int pre = 0, vs = 0, r = 0;
+  uint64_t ms = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int c = __builtin_popcountll(msel[v]);
+    const bool here = n >= pre && n < pre + c;
+    vs = here ? v : vs;
+    r = here ? n - pre : r;
+    ms = here ? msel[v] : ms;
+    pre += c;
+  }
+  const uint64_t hit = __ballot(((ms >> lane) & 1ull) && bits_below(ms) == r);
+  return 64 * vs + int(__builtin_ctzll(hit));
+}
+
+// Ranks of the selection.  The k selected go to this wave's LDS slots in
+// index order, each is ranked by counting the entries above it (larger key,
+// or equal key and lower index), and lane j < k returns the rank-j expert,
+// its logit (a -0 logit comes back as +0, which changes no weight) and its
+// position in index order.
+template <int V>
+__device__ __forceinline__ void wave_rank(const WaveKeys<V>& K, const uint64_t (&msel)[V], int k, float& my_val,
+                                          int& my_idx, int& my_slot) {
+  __shared__ uint2 tk_s[16][2][kMaxTopKLds];  // per wave of the workgroup: index order / rank order
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int base = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const uint64_t m = msel[v];
+    if ((m >> lane) & 1ull) tk_s[wv][0][base + bits_below(m)] = uint2{K.key[v], uint32_t(lane + 64 * v)};
+    base += __builtin_popcountll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < k) {
+    const uint2 me = tk_s[wv][0][lane];
+    int rank = 0;
+    for (int i = 0; i < k; ++i) {
+      const uint2 o = tk_s[wv][0][i];
+      rank += (o.x > me.x || (o.x == me.x && i < lane)) ? 1 : 0;
+    }
+    tk_s[wv][1][rank] = uint2{me.x, me.y | (uint32_t(lane) << 16)};  // expert < 2^16, slot in the high half
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint2 out = uint2{0u, 0u};
+  if (lane < k) out = tk_s[wv][1][lane];
+  my_val = key_float(out.x);
+  my_idx = int(out.y & 0xffffu);
+  my_slot = int(out.y >> 16);
+}
+
+// Renormalised softmax weight of rank `lane` (lane < k):
+// exp(l_j - l_0) / sum_{j' < k} exp(l_j' - l_0).
+__device__ __forceinline__ float wave_topk_weight(float my_val, int k) {
   const float top = __shfl(my_val, 0, 64);
   const int lane = threadIdx.x & 63;
   const float p = lane < k ? expf(my_val - top) : 0.0f;
   const float sum = wave_sum(p);
-  my_w = p / sum;
+  return p / sum;
+}
+
+// Lane j < k returns selection j: its expert and weight.  Every caller of
+// the layer's selection goes through these routines, so all paths pick the
+// same experts with the same weight bits.
+template <int V>
+__device__ __forceinline__ void wave_topk_softmax(const float* __restrict__ row, int E, int k, int& my_idx,
+                                                  float& my_w) {
+  WaveKeys<V> K;
+  wave_keys<V>(row, E, K);
+  uint64_t msel[V];
+  wave_select<V>(K, k, msel);
+  float my_val;
+  int my_slot;
+  wave_rank<V>(K, msel, k, my_val, my_idx, my_slot);
+  my_w = wave_topk_weight(my_val, k);
 }
 
 }  // namespace moe

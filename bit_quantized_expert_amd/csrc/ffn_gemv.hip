@@ -153,18 +153,18 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 // MFMA operands: no LDS staging, and they are requested before anything
 // else.  h is written in the permuted column order of the down projection.
 //
-// Slot source.  With `logits` null, slot s of the slot table (standalone
-// expert FFN: h row = the pair's sorted position).  With `logits` set (the
-// fused decode layer), every wave selects the token's top-k itself from the
-// router logits (the shared selection routine, so the experts and weights
-// are those of every other path): slot j < k is the rank-j expert, h row j;
-// slot k is the shared expert.  Workgroup (0, 0) stores the selection.
+// Slot source.  With `sl.logits` null, slot s of the slot table (standalone
+// expert FFN: h row = the pair's sorted position).  With `sl.logits` set (the
+// fused decode layer), every wave finds the token's selected set itself from
+// the router logits (the shared selection routines, so the experts and
+// weights are those of every other path): slot j < k is the j-th selected
+// expert in ascending expert order, h row j; slot k is the shared expert.
+// The ranking and the weights stay off that path: one wave of workgroup
+// (0, 0) computes them while its weight loads are in flight and stores the
+// rank-ordered selection and the rank <-> slot maps.
 // ---------------------------------------------------------------------------
 template <int QBITS, int UNIT, typename XT>
-__global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, const float* __restrict__ logits,
-                                                              int32_t* __restrict__ idx_out,
-                                                              float* __restrict__ w_out,
-                                                              int32_t* __restrict__ header) {
+__global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, Decode1Sel sl) {
   __shared__ float red[4][2][16];
   constexpr int RB = 2;  // rounds per wave per load batch (rounds c and c + 4)
   const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
@@ -189,23 +189,27 @@ __global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, const 
   bool shared;
   int64_t ex;
   int hrow;
-  if (logits) {
+  WaveKeys<8> K;
+  uint64_t sel[8];
+  bool rank_here = false;  // the one wave that also ranks the selection and stores it
+  if (sl.logits) {
     shared = j >= a.k;
     if (blockIdx.x * 16 >= (shared ? a.Is : a.I)) return;
     ex = 0;
     hrow = shared ? 0 : j;
     if (!shared) {
-      int my_idx;
-      float my_w;
-      wave_topk_softmax<8>(logits, a.E, a.k, my_idx, my_w);
-      ex = __shfl(my_idx, j, 64);
-      if (blockIdx.x == 0 && j == 0 && ks == 0) {
-        if (lane < a.k) {
-          idx_out[lane] = my_idx;
-          w_out[lane] = my_w;
-        }
-        if (lane == 0) header[kHdrError] = 0;
+      // one wave selects (the selection's ballot counts run on the CU's one
+      // scalar unit, so four waves would queue behind each other there)
+      __shared__ int s_ex;
+      if (ks == 0) {
+        wave_keys<8>(sl.logits, a.E, K);
+        wave_select<8>(K, a.k, sel);
+        const int e = wave_nth_selected<8>(sel, j);  // slot j: the j-th selected expert in index order
+        if (lane == 0) s_ex = e;
       }
+      __syncthreads();
+      ex = s_ex;
+      rank_here = blockIdx.x == 0 && j == 0 && ks == 0;
     }
   } else {
     const int4 si = a.slots[j];
@@ -238,6 +242,20 @@ __global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, const 
         zero_unit(ug[i]);
         zero_unit(uu[i]);
       }
+    }
+    if (b0 == 0 && rank_here) {
+      // ranks, weights and the slot maps, while this wave's weight loads are in flight
+      float my_val;
+      int my_idx, my_slot;
+      wave_rank<8>(K, sel, a.k, my_val, my_idx, my_slot);
+      const float my_w = wave_topk_weight(my_val, a.k);
+      if (lane < a.k) {
+        sl.idx[lane] = my_idx;
+        sl.w[lane] = my_w;
+        sl.slot_of_rank[lane] = my_slot;
+        sl.slot_expert[my_slot] = my_idx;
+      }
+      if (lane == 0) sl.header[kHdrError] = 0;
     }
     if (b0 > 0) {  // later batches (hidden > 2048): their activations, loaded after the weights
 #pragma unroll
@@ -291,8 +309,9 @@ __global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, const 
 //   out[r] = shared[r] + sum_{j<k} w_j * y_j[r]
 // in the combine's order (shared first, then ranks 0..k-1, one fma each).
 // grid = H / 16, block = 64 * NW: wave w takes slots w, w + NW, ... (slot
-// j < k = rank j, h row j; slot k = shared) and computes 16 output rows of
-// its slot with the same MFMA sequence as the standalone down kernel.  The
+// s < k = expert slot_expert[s], h row s; slot k = shared) and computes 16
+// output rows of its slot with the same MFMA sequence as the standalone down
+// kernel; the combine takes the slots in rank order through slot_of_rank.  The
 // weight loads of a wave's first slot go out first; meanwhile the workgroup
 // copies the h rows of all slots into LDS (their addresses depend on
 // nothing), and the MFMA operands are read from there.  The rows of all
@@ -304,13 +323,13 @@ struct DownSlot {
   int K, n_units, rounds;
 };
 
-// Down weights of slot s of the fused single-token layer (s < k: the rank-s
-// expert; s == k: the shared expert).
+// Down weights of slot s of the fused single-token layer (s < k: the
+// expert slot_expert[s]; s == k: the shared expert).
 template <int UNIT>
-__device__ __forceinline__ DownSlot down_slot(const FfnArgs& a, const int32_t* __restrict__ idx, int s) {
+__device__ __forceinline__ DownSlot down_slot(const FfnArgs& a, const int32_t* __restrict__ slot_expert, int s) {
   const bool shared = s >= a.k;
   const QMat D = shared ? a.sd : a.rd;
-  const int64_t ex = shared ? 0 : idx[s];
+  const int64_t ex = shared ? 0 : slot_expert[s];
   DownSlot r;
   r.K = shared ? a.Is : a.I;
   r.dc = D.codes + ex * D.code_stride;
@@ -321,13 +340,16 @@ __device__ __forceinline__ DownSlot down_slot(const FfnArgs& a, const int32_t* _
 }
 
 template <int QBITS, int UNIT>
-__global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a, const int32_t* __restrict__ idx,
+__global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
+                                                                     const int32_t* __restrict__ slot_expert,
+                                                                     const int32_t* __restrict__ slot_of_rank,
                                                                      const float* __restrict__ w,
                                                                      float* __restrict__ out,
                                                                      float* __restrict__ res, int ldh) {
   extern __shared__ __attribute__((aligned(16))) f16 hs[];  // [n_slots][ldh]
   __shared__ float ys[kMaxTopK + 1][16];
   __shared__ float s_w[kMaxTopK];
+  __shared__ int s_slot[kMaxTopK];
   constexpr int RB = 4;
   const int nw = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -335,12 +357,15 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a, 
   const int H = a.H;
   const int row = blockIdx.x * 16 + n;  // H is a multiple of 32
   const int n_slots = a.k + (a.has_shared ? 1 : 0);
-  if (threadIdx.x < a.k) s_w[threadIdx.x] = w[threadIdx.x];
+  if (threadIdx.x < a.k) {
+    s_w[threadIdx.x] = w[threadIdx.x];
+    s_slot[threadIdx.x] = slot_of_rank[threadIdx.x];
+  }
 
   Unit<QBITS, UNIT> ud[RB];
   DownSlot sl{};
   if (wv < n_slots) {
-    sl = down_slot<UNIT>(a, idx, wv);
+    sl = down_slot<UNIT>(a, slot_expert, wv);
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int u = i * 4 + g;
@@ -376,7 +401,7 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a, 
   const bool a_on = n == 0;  // MFMA row 0 is the token; rows 1..15 are zero
   for (int s = wv; s < n_slots; s += nw) {
     if (s != wv) {
-      sl = down_slot<UNIT>(a, idx, s);
+      sl = down_slot<UNIT>(a, slot_expert, s);
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const int u = i * 4 + g;
@@ -419,7 +444,7 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a, 
   __syncthreads();
   if (threadIdx.x < 16) {
     float v = a.has_shared ? ys[a.k][n] : 0.0f;
-    for (int j = 0; j < a.k; ++j) v = __builtin_fmaf(s_w[j], ys[j][n], v);
+    for (int j = 0; j < a.k; ++j) v = __builtin_fmaf(s_w[j], ys[s_slot[j]][n], v);
     if (out) out[row] = v;
     if (res) res[row] += v;
   }
@@ -765,7 +790,7 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
     if (one) {
       const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
 #define GU(U_, X_) \
-  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 256, 0, stream>>>(a, nullptr, nullptr, nullptr, nullptr)
+  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 256, 0, stream>>>(a, Decode1Sel{})
       if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
       else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
@@ -803,14 +828,14 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases) {
 }
 
 template <int QBITS>
-static hipError_t launch_decode1_q(const FfnArgs& a, const float* logits, int32_t* idx, float* w, int32_t* header,
-                                   float* out, float* res, hipStream_t stream) {
+static hipError_t launch_decode1_q(const FfnArgs& a, const Decode1Sel& sel, float* out, float* res,
+                                   hipStream_t stream) {
   const int slots = a.k + (a.has_shared ? 1 : 0);
   const int max_rows = std::max(a.I, a.has_shared ? a.Is : 0);
   {
     const bool u64 = a.H % 64 == 0;
     const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
-#define GU(U_, X_) gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 256, 0, stream>>>(a, logits, idx, w, header)
+#define GU(U_, X_) gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 256, 0, stream>>>(a, sel)
     if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
     else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
@@ -821,17 +846,19 @@ static hipError_t launch_decode1_q(const FfnArgs& a, const float* logits, int32_
     const dim3 grid(unsigned(a.H / 16));
     const int ldh = std::max(a.I, a.has_shared ? a.Is : 0) + 8;
     const size_t lds = size_t(slots) * ldh * sizeof(_Float16);
-    if (u64) gemv_down_combine_1tok_kernel<QBITS, 64><<<grid, 64 * nw, lds, stream>>>(a, idx, w, out, res, ldh);
-    else gemv_down_combine_1tok_kernel<QBITS, 32><<<grid, 64 * nw, lds, stream>>>(a, idx, w, out, res, ldh);
+#define DC(U_) \
+  gemv_down_combine_1tok_kernel<QBITS, U_><<<grid, 64 * nw, lds, stream>>>(a, sel.slot_expert, sel.slot_of_rank, \
+                                                                          sel.w, out, res, ldh)
+    if (u64) DC(64);
+    else DC(32);
+#undef DC
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode1_ffn(const FfnArgs& a, const float* logits, int32_t* idx, float* w, int32_t* header,
-                              float* out, float* res, hipStream_t stream) {
+hipError_t launch_decode1_ffn(const FfnArgs& a, const Decode1Sel& sel, float* out, float* res, hipStream_t stream) {
   if (a.E > kDecode1MaxExperts || a.T != 1) return hipErrorInvalidValue;
-  return a.qbits == 2 ? launch_decode1_q<2>(a, logits, idx, w, header, out, res, stream)
-                      : launch_decode1_q<3>(a, logits, idx, w, header, out, res, stream);
+  return a.qbits == 2 ? launch_decode1_q<2>(a, sel, out, res, stream) : launch_decode1_q<3>(a, sel, out, res, stream);
 }
 
 }  // namespace moe

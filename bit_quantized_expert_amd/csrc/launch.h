@@ -79,11 +79,19 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases);
 constexpr int kGroupedBM = 128;
 hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases);
 // The fused single-token decode FFN (needs E <= kDecode1MaxExperts): gate/up
-// with the selection made from `logits` in every workgroup (writes idx, w and
-// clears the error word), then down + combine into out and/or res.
+// with the selection made from the router logits in every workgroup, then
+// down + combine into out and/or res.  The selected experts occupy slots in
+// ascending expert order; idx/w are the API's rank-ordered outputs.
 constexpr int kDecode1MaxExperts = 512;
-hipError_t launch_decode1_ffn(const FfnArgs& a, const float* logits, int32_t* idx, float* w, int32_t* header,
-                              float* out, float* res, hipStream_t stream);
+struct Decode1Sel {
+  const float* logits;   // [E] router logits of the token
+  int32_t* idx;          // [k] experts, rank order (written)
+  float* w;              // [k] weights, rank order (written)
+  int32_t* slot_of_rank; // [k] slot of rank r (written)
+  int32_t* slot_expert;  // [k] expert of slot s (written)
+  int32_t* header;       // workspace header: the error word is cleared
+};
+hipError_t launch_decode1_ffn(const FfnArgs& a, const Decode1Sel& sel, float* out, float* res, hipStream_t stream);
 // res[t] -> a[t] = bf16_RNE(res[t] / sqrt(mean(res[t]^2) + 1e-6)) with the
 // reduction order of the combine kernel (so both give the same bits).
 hipError_t launch_residual_rmsnorm(const float* res, int64_t T, int H, uint16_t* next_in, hipStream_t stream);

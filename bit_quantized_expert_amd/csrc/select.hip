@@ -13,6 +13,7 @@
 namespace moe {
 
 constexpr int kSelMaxT = 16;
+static_assert(kMaxTopK <= kMaxTopKLds, "the wave top-k ranks at most kMaxTopKLds entries");
 
 template <int V>
 __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restrict__ logits, int T, int E, int k,

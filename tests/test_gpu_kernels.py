@@ -85,6 +85,42 @@ def test_route_all_equal_logits_tie_rule():
     assert np.allclose(w.cpu().numpy(), 1 / 7, rtol=0, atol=1e-7)
 
 
+@pytest.mark.parametrize("E,k,T", [(40, 7, 1), (40, 7, 16), (512, 10, 1), (512, 10, 16), (512, 32, 1),
+                                   (100, 32, 5), (33, 33 - 1, 16), (8, 8, 3)])
+def test_layer_selection_exact_ties(E, k, T):
+    """Zero router weights and a bias on a coarse grid: the logits are the
+    bias exactly, with many exact ties (at the k-th place too).  The fused
+    layer's selection (single-token and small-batch paths) equals the first k
+    of the oracle's stable sort, and the standalone router's selection, bit
+    for bit (indices and weights)."""
+    from oracle import moe_oracle as O
+    M = _lib()
+    H, I, Is = 64, 32, 32
+    g = torch.Generator().manual_seed(E * 1000 + k * 10 + T)
+    bias = torch.randint(-3, 4, (E,), generator=g).float() * 0.5
+    s = synth.MoEShape(H, I, E, k, Is, 2)
+    arena = M.QArena(E, H, I, 2, "cuda")
+    for m, (r, c) in enumerate(arena.mat_shapes):
+        arena.quantize_from(m, torch.zeros(E, r, c, device="cuda"))
+    sarena = M.QArena(1, H, Is, 2, "cuda")
+    for m, (r, c) in enumerate(sarena.mat_shapes):
+        sarena.quantize_from(m, torch.zeros(1, r, c, device="cuda"))
+    q = M.QLayer(torch.zeros(E, H, dtype=torch.bfloat16, device="cuda"), bias.cuda(), arena, sarena)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16).cuda()
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, device="cuda")
+    out = torch.empty(T, H, device="cuda")
+    M.layer_forward(x, q, s, out=out, topk_idx=idx, topk_w=w, algo="gemv", ws=M.alloc_workspace(s, T, algo="gemv"))
+    idx2 = torch.empty_like(idx)
+    w2 = torch.empty_like(w)
+    M.route(x, q, s, idx2, w2, ws=M.alloc_workspace(s, T))
+    torch.cuda.synchronize()
+    want = O.topk_select(np.tile(bias.numpy().astype(np.float64), (T, 1)), k)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert np.array_equal(idx2.cpu().numpy(), want)
+    assert torch.equal(w, w2)
+
+
 def _permute(M, idx_np, E, k):
     T = idx_np.shape[0]
     s = synth.MoEShape(64, 32, E, k, 0, 2)
