@@ -167,7 +167,7 @@ template <int QBITS, int UNIT, typename XT>
 __global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, Decode1Sel sl) {
   __shared__ float red[4][2][16];
   constexpr int RB = 2;  // rounds per wave per load batch (rounds c and c + 4)
-  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, g = lane >> 4;
   const int j = blockIdx.y;
   const int H = a.H;
@@ -345,22 +345,53 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
                                                                      const int32_t* __restrict__ slot_of_rank,
                                                                      const float* __restrict__ w,
                                                                      float* __restrict__ out,
-                                                                     float* __restrict__ res, int ldh) {
+                                                                     float* __restrict__ res, int ldh,
+                                                                     int nthreads) {
   extern __shared__ __attribute__((aligned(16))) f16 hs[];  // [n_slots][ldh]
   __shared__ float ys[kMaxTopK + 1][16];
   __shared__ float s_w[kMaxTopK];
   __shared__ int s_slot[kMaxTopK];
   constexpr int RB = 4;
-  const int nw = blockDim.x >> 6;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = nthreads >> 6;  // == blockDim.x / 64 (blockDim would be a load from the packet)
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, g = lane >> 4;
   const int H = a.H;
   const int row = blockIdx.x * 16 + n;  // H is a multiple of 32
   const int n_slots = a.k + (a.has_shared ? 1 : 0);
+  // Issue order: the combine's weights and slot map, then the h rows (their
+  // addresses depend on nothing), then the slot's expert id and, once it is
+  // in, the weight loads; the LDS stores come last, so no load waits for
+  // another before it is issued.
+  float w_r = 0.0f;
+  int slot_r = 0;
   if (threadIdx.x < a.k) {
-    s_w[threadIdx.x] = w[threadIdx.x];
-    s_slot[threadIdx.x] = slot_of_rank[threadIdx.x];
+    w_r = w[threadIdx.x];
+    slot_r = slot_of_rank[threadIdx.x];
   }
+  const int ch = ldh / 8;  // 16-byte chunks per LDS row (covers the longest K)
+  const int items = n_slots * ch;
+  constexpr int HB = 4;  // h chunks per thread per batch
+  half8 hv[HB];
+  bool hon[HB];
+  auto load_h = [&](int base) {
+#pragma unroll
+    for (int q = 0; q < HB; ++q) {
+      const int it = base + q * nthreads + int(threadIdx.x);
+      const int s = min(it, items - 1) / ch, c = min(it, items - 1) - s * ch;
+      const int Ks = s >= a.k ? a.Is : a.I;
+      hon[q] = it < items && 8 * c < Ks;
+      const f16* src = s >= a.k ? a.h_shared : a.h_routed + int64_t(s) * Ks;
+      hv[q] = *reinterpret_cast<const half8*>(src + (8 * c < Ks ? 8 * c : 0));  // unconditional (clamped)
+    }
+  };
+  auto store_h = [&](int base) {
+#pragma unroll
+    for (int q = 0; q < HB; ++q) {
+      const int it = base + q * nthreads + int(threadIdx.x);
+      if (hon[q]) *reinterpret_cast<half8*>(hs + it / ch * ldh + 8 * (it % ch)) = hv[q];
+    }
+  };
+  load_h(0);
 
   Unit<QBITS, UNIT> ud[RB];
   DownSlot sl{};
@@ -373,28 +404,14 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
       else zero_unit(ud[i]);
     }
   }
-  // h rows of every slot -> LDS, 16 bytes per item, all loads of a thread first
-  {
-    const int ch = ldh / 8;  // 16-byte chunks per LDS row (covers the longest K)
-    const int items = n_slots * ch;
-    for (int base = 0; base < items; base += 4 * int(blockDim.x)) {
-      half8 v[4];
-      bool on[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int it = base + q * int(blockDim.x) + int(threadIdx.x);
-        const int s = min(it, items - 1) / ch, c = min(it, items - 1) - s * ch;
-        const int Ks = s >= a.k ? a.Is : a.I;
-        on[q] = it < items && 8 * c < Ks;
-        const f16* src = s >= a.k ? a.h_shared : a.h_routed + int64_t(s) * Ks;
-        v[q] = *reinterpret_cast<const half8*>(src + (8 * c < Ks ? 8 * c : 0));  // unconditional (clamped)
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int it = base + q * int(blockDim.x) + int(threadIdx.x);
-        if (on[q]) *reinterpret_cast<half8*>(hs + it / ch * ldh + 8 * (it % ch)) = v[q];
-      }
-    }
+  store_h(0);
+  for (int base = HB * nthreads; base < items; base += HB * nthreads) {  // more than one batch
+    load_h(base);
+    store_h(base);
+  }
+  if (threadIdx.x < a.k) {
+    s_w[threadIdx.x] = w_r;
+    s_slot[threadIdx.x] = slot_r;
   }
   __syncthreads();
 
@@ -410,7 +427,8 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
       }
     }
     const f16* hrow = hs + s * ldh;
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    float4v acc[4] = {};  // one accumulator per round class (round % 4), as in every down kernel
+    static_assert(RB % 4 == 0, "a load batch holds whole round classes");
     for (int r0 = 0; r0 < sl.rounds; r0 += RB) {
       if (r0 > 0) {
 #pragma unroll
@@ -434,19 +452,31 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
             alo = ap[0];
             ahi = ap[1];
           }
-          acc = mfma16(alo, blo, acc);
-          acc = mfma16(ahi, bhi, acc);
+          acc[i & 3] = mfma16(alo, blo, acc[i & 3]);
+          acc[i & 3] = mfma16(ahi, bhi, acc[i & 3]);
         }
       }
     }
-    if (lane < 16) ys[s][n] = acc[0];
+    if (lane < 16) ys[s][n] = ((acc[0][0] + acc[1][0]) + acc[2][0]) + acc[3][0];
   }
   __syncthreads();
   if (threadIdx.x < 16) {
+    const float r_in = res ? res[row] : 0.0f;
     float v = a.has_shared ? ys[a.k][n] : 0.0f;
-    for (int j = 0; j < a.k; ++j) v = __builtin_fmaf(s_w[j], ys[s_slot[j]][n], v);
+    for (int j0 = 0; j0 < a.k; j0 += 8) {  // the LDS reads of 8 ranks at a time, then their fmas in rank order
+      float wj[8], yj[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = min(j0 + q, a.k - 1);
+        wj[q] = s_w[j];
+        yj[q] = ys[s_slot[j]][n];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j0 + q < a.k) v = __builtin_fmaf(wj[q], yj[q], v);
+    }
     if (out) out[row] = v;
-    if (res) res[row] += v;
+    if (res) res[row] = r_in + v;
   }
 }
 
@@ -484,7 +514,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
     const bool a_on = n < mnow;
     const int nr = a_on ? n : 0;  // rows past the tokens read token 0's row (loads are unconditional)
     const f16* hrow = hin + (shared ? int64_t(mc + nr) : int64_t(si.y + mc + nr)) * K;
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    float4v acc[4] = {};  // one accumulator per round class (round % 4)
+    static_assert(RB % 4 == 0, "a load batch holds whole round classes");
     for (int r0 = 0; r0 < rounds; r0 += RB) {
       Unit<QBITS, UNIT> ud[RB];
 #pragma unroll
@@ -514,17 +545,18 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
         for (int d = 0; d < UNIT / 16; ++d) {
           half8 blo, bhi;
           dq_unit_word(ud[i], d, blo, bhi);
-          acc = mfma16(av[i][d][0], blo, acc);
-          acc = mfma16(av[i][d][1], bhi, acc);
+          acc[i & 3] = mfma16(av[i][d][0], blo, acc[i & 3]);
+          acc[i & 3] = mfma16(av[i][d][1], bhi, acc[i & 3]);
         }
       }
     }
+    const float4v y4 = ((acc[0] + acc[1]) + acc[2]) + acc[3];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = 4 * g + j;
       if (m < mnow) {
         const int64_t yr = shared ? int64_t(mc + m) : int64_t(si.y + mc + m);
-        yout[yr * H + row] = acc[j];
+        yout[yr * H + row] = y4[j];
       }
     }
   }
@@ -550,6 +582,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
 template <int QBITS, int UNIT, typename XT, int NW>
 __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) f16 xs[];
+  constexpr int kThreads = 64 * NW;  // the launch's block size (blockDim would be a load)
   constexpr int D = MOE_TP_D;
   static_assert(D % 4 == 0, "the pipeline depth is a multiple of the 4 accumulation classes");
   const int4 si = a.slots[blockIdx.y];
@@ -596,24 +629,24 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
       // the activation loads, then the conversions, each step as one batch
       constexpr int NB = sizeof(XT) == 4 ? 4 : 8;
       const int chunks = H / 16, items = mnow * chunks;
-      for (int base = 0; base < items; base += NB * int(blockDim.x)) {
+      for (int base = 0; base < items; base += NB * kThreads) {
         int64_t tok[NB];
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-          const int it = min(base + q * int(blockDim.x) + int(threadIdx.x), items - 1);
+          const int it = min(base + q * kThreads + int(threadIdx.x), items - 1);
           const int r = it / chunks;
           tok[q] = shared ? int64_t(mc + r) : int64_t(a.sorted_pair[si.y + mc + r] / a.k);
         }
         Raw16<XT> raw[NB];
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-          const int it = min(base + q * int(blockDim.x) + int(threadIdx.x), items - 1);
+          const int it = min(base + q * kThreads + int(threadIdx.x), items - 1);
           const int r = it / chunks, gg = it - r * chunks;
           load_raw16(x + tok[q] * H + gg * 16, raw[q]);
         }
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-          const int it = base + q * int(blockDim.x) + int(threadIdx.x);
+          const int it = base + q * kThreads + int(threadIdx.x);
           if (it < items) {
             const int r = it / chunks, gg = it - r * chunks;
             half8 lo, hi;
@@ -684,6 +717,7 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
 template <int QBITS, int UNIT, int NW>
 __global__ __launch_bounds__(64 * NW) void gemv_down_tp_kernel(FfnArgs a, int ldsw) {
   extern __shared__ __attribute__((aligned(16))) f16 hs[];
+  constexpr int kThreads = 64 * NW;  // the launch's block size (blockDim would be a load)
   constexpr int D = 4;
   const int4 si = a.slots[blockIdx.y];
   const int m_total = si.z;
@@ -721,18 +755,18 @@ __global__ __launch_bounds__(64 * NW) void gemv_down_tp_kernel(FfnArgs a, int ld
       // NB loads in flight per thread before their stores
       constexpr int NB = 8;
       const int chunks = K / 8, items = mnow * chunks;
-      for (int base = 0; base < items; base += NB * int(blockDim.x)) {
+      for (int base = 0; base < items; base += NB * kThreads) {
         half8 v[NB];
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-          const int it = min(base + q * int(blockDim.x) + int(threadIdx.x), items - 1);
+          const int it = min(base + q * kThreads + int(threadIdx.x), items - 1);
           const int r = it / chunks, c8 = it - r * chunks;
           const int64_t hr = shared ? int64_t(mc + r) : int64_t(si.y + mc + r);
           v[q] = *reinterpret_cast<const half8*>(hin + hr * K + c8 * 8);
         }
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-          const int it = base + q * int(blockDim.x) + int(threadIdx.x);
+          const int it = base + q * kThreads + int(threadIdx.x);
           if (it < items) {
             const int r = it / chunks, c8 = it - r * chunks;
             *reinterpret_cast<half8*>(hs + r * ldsw + c8 * 8) = v[q];
@@ -743,7 +777,8 @@ __global__ __launch_bounds__(64 * NW) void gemv_down_tp_kernel(FfnArgs a, int ld
     __syncthreads();
     if (!wave_on) continue;
     const f16* hrow = hs + min(n, mnow - 1) * ldsw;  // see the gate/up kernel: finite, never stored
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    float4v acc[4] = {};  // one accumulator per round class (round % 4): r0 is a multiple of D, D of 4
+    static_assert(D % 4 == 0, "the pipeline depth is a multiple of the 4 accumulation classes");
     for (int r0 = 0; r0 < rounds; r0 += D) {
 #pragma unroll
       for (int i = 0; i < D; ++i) {
@@ -760,17 +795,18 @@ __global__ __launch_bounds__(64 * NW) void gemv_down_tp_kernel(FfnArgs a, int ld
           dq_unit_word(cd, d, blo, bhi);
           const half8* ap = reinterpret_cast<const half8*>(hrow + ua * UNIT + 16 * d);
           const half8 alo = ap[0], ahi = ap[1];
-          acc = mfma16(alo, blo, acc);
-          acc = mfma16(ahi, bhi, acc);
+          acc[i & 3] = mfma16(alo, blo, acc[i & 3]);
+          acc[i & 3] = mfma16(ahi, bhi, acc[i & 3]);
         }
       }
     }
+    const float4v y4 = ((acc[0] + acc[1]) + acc[2]) + acc[3];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = 4 * g + j;
       if (m < mnow) {
         const int64_t yr = shared ? int64_t(mc + m) : int64_t(si.y + mc + m);
-        yout[yr * H + row] = acc[j];
+        yout[yr * H + row] = y4[j];
       }
     }
   }
@@ -848,7 +884,7 @@ static hipError_t launch_decode1_q(const FfnArgs& a, const Decode1Sel& sel, floa
     const size_t lds = size_t(slots) * ldh * sizeof(_Float16);
 #define DC(U_) \
   gemv_down_combine_1tok_kernel<QBITS, U_><<<grid, 64 * nw, lds, stream>>>(a, sel.slot_expert, sel.slot_of_rank, \
-                                                                          sel.w, out, res, ldh)
+                                                                          sel.w, out, res, ldh, 64 * nw)
     if (u64) DC(64);
     else DC(32);
 #undef DC
