@@ -579,6 +579,9 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
 #ifndef MOE_TP_MINW
 #define MOE_TP_MINW 1
 #endif
+#ifndef MOE_TP_EARLY
+#define MOE_TP_EARLY 2
+#endif
 template <int QBITS, int UNIT, typename XT, int NW>
 __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) f16 xs[];
@@ -608,9 +611,34 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
   const XT* x = static_cast<const XT*>(a.x);
   f16* hout = shared ? a.h_shared : a.h_routed;
   const int hw = shared ? a.Is : a.I;
+  // With a token mask in the slot (decode selection), the slot's tokens are
+  // known without a load: the activations are requested before the weights,
+  // so the staging waits for them alone (loads complete in issue order).
+  __shared__ int s_tok[kGemvMaxM];
+  const uint32_t tmask = uint32_t(si.w);
+  if (tmask) {
+    if (threadIdx.x < kGemvMaxM && ((tmask >> threadIdx.x) & 1u))
+      s_tok[__builtin_popcount(tmask & ((1u << threadIdx.x) - 1u))] = int(threadIdx.x);
+    __syncthreads();
+  }
+  constexpr int NB = sizeof(XT) == 4 ? 4 : 8;  // staging items per thread per batch
+  constexpr int NBE = MOE_TP_EARLY;             // items per thread of an early staging (registers held
+                                                // across the weight loads)
+  const int chunks = H / 16;
 
   for (int mc = 0; mc < m_total; mc += kGemvMaxM) {
     const int mnow = min(kGemvMaxM, m_total - mc);
+    const int items = mnow * chunks;
+    const bool early = tmask != 0u && items <= NBE * kThreads;
+    Raw16<XT> raw0[NBE];
+    if (early) {
+#pragma unroll
+      for (int q = 0; q < NBE; ++q) {
+        const int it = min(q * kThreads + int(threadIdx.x), items - 1);
+        const int r = it / chunks, gg = it - r * chunks;
+        load_raw16(x + int64_t(s_tok[r]) * H + gg * 16, raw0[q]);
+      }
+    }
     Unit<QBITS, UNIT> ug[D], uu[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -624,11 +652,22 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
       }
     }
     __syncthreads();
-    {
+    if (early) {
+#pragma unroll
+      for (int q = 0; q < NBE; ++q) {
+        const int it = q * kThreads + int(threadIdx.x);
+        if (it < items) {
+          const int r = it / chunks, gg = it - r * chunks;
+          half8 lo, hi;
+          cvt_raw16(raw0[q], lo, hi);
+          half8* dst = reinterpret_cast<half8*>(xs + r * ldsw + gg * 16);
+          dst[0] = lo;
+          dst[1] = hi;
+        }
+      }
+    } else {
       // stage the tokens: per thread NB items at a time, the token ids, then
       // the activation loads, then the conversions, each step as one batch
-      constexpr int NB = sizeof(XT) == 4 ? 4 : 8;
-      const int chunks = H / 16, items = mnow * chunks;
       for (int base = 0; base < items; base += NB * kThreads) {
         int64_t tok[NB];
 #pragma unroll

@@ -66,7 +66,9 @@ hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared,
                        hipStream_t stream);
 // Decode-layer selection on one workgroup (T <= 16): top-k + softmax weights,
 // permutation and the slot table (int4 {expert or -1 for shared, first sorted
-// position, token count, 0}; empty slots have count 0).
+// position, token count, token mask: bit t set when token t uses the slot};
+// empty slots have count 0).  Slot tables built by launch_plan carry mask 0
+// (tokens then come from sorted_pair).
 hipError_t launch_select_small(const float* logits, int T, int E, int k, int has_shared, int32_t* idx, float* w,
                                int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                                int32_t* header, int4* slots, hipStream_t stream);

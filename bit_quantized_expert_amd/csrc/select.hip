@@ -25,10 +25,14 @@ __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restr
                                                            int32_t* __restrict__ header, int4* __restrict__ slots) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int flag[kMaxExperts];
+  __shared__ uint32_t tmask[kMaxExperts];  // bit t: token t chose the expert
   __shared__ int tmp[16];
   __shared__ int s_idx[kSelMaxT * kMaxTopK];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += 1024) cnt[e] = 0;
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    cnt[e] = 0;
+    tmask[e] = 0u;
+  }
 
   // ---- top-k of token wv (one wave per token)
   if (wv < T) {
@@ -45,7 +49,10 @@ __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restr
 
   // ---- histogram, offsets
   const int P = T * k;
-  for (int p = threadIdx.x; p < P; p += 1024) atomicAdd(&cnt[s_idx[p]], 1);
+  for (int p = threadIdx.x; p < P; p += 1024) {
+    atomicAdd(&cnt[s_idx[p]], 1);
+    atomicOr(&tmask[s_idx[p]], 1u << (p / k));
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 1024) {
     counts[e] = cnt[e];
@@ -55,13 +62,14 @@ __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restr
   for (int e = threadIdx.x; e < E; e += 1024) offsets[e] = cnt[e];
   if (threadIdx.x == 0) offsets[E] = total;
 
-  // ---- stable scatter (P <= 1024: one pair per thread)
+  // ---- stable scatter (P <= 1024: one pair per thread).  A token picks an
+  // expert at most once, so the pairs of expert e before pair (t, j) are
+  // those of the earlier tokens in e's token mask.
   if (threadIdx.x < P) {
     const int p = threadIdx.x;
     const int e = s_idx[p];
-    int before = 0;
-    for (int j = 0; j < p; ++j) before += s_idx[j] == e;
-    const int pos = cnt[e] + before;
+    const int t = p / k;
+    const int pos = cnt[e] + __builtin_popcount(tmask[e] & ((1u << t) - 1u));
     sorted_pair[pos] = p;
     pair_pos[p] = pos;
   }
@@ -70,11 +78,11 @@ __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restr
   const int n_active = block_scan_fast(flag, E, tmp);
   for (int e = threadIdx.x; e < E; e += 1024) {
     const int c = (e + 1 < E ? cnt[e + 1] : total) - cnt[e];
-    if (c > 0) slots[flag[e]] = int4{e, cnt[e], c, 0};
+    if (c > 0) slots[flag[e]] = int4{e, cnt[e], c, int(tmask[e])};
   }
   const int n_valid = n_active + (has_shared ? 1 : 0);
   if (threadIdx.x == 0) {
-    if (has_shared) slots[n_active] = int4{-1, 0, T, 0};
+    if (has_shared) slots[n_active] = int4{-1, 0, T, int((1u << T) - 1u)};
     header[kHdrError] = 0;
     header[kHdrActive] = n_active;
     header[kHdrValid] = n_valid;
