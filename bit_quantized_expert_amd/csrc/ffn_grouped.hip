@@ -29,6 +29,12 @@
 namespace moe {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64, kLDA = kBK + 8;  // row pitch in halves (144 B)
+#ifndef MOE_GROUPED2
+#define MOE_GROUPED2 1
+#endif
+#ifndef MOE_GROUPED2_WAVES
+#define MOE_GROUPED2_WAVES 8
+#endif
 
 // Raw (not yet dequantised) B operand of one thread for one K step.
 struct BRaw {
@@ -282,20 +288,270 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(FfnArgs a, int n_n
   }
 }
 
+// ---------------------------------------------------------------------------
+// Second design: operand traffic per MFMA halved.  A workgroup owns BM = 128
+// rows x 4 waves; each wave a 128 x 64 block (4 x 2 MFMA tiles of 32 x 32),
+// so an A fragment read from LDS feeds two MFMAs and a B fragment four.  The
+// weights never pass through LDS: each wave loads and dequantises its own
+// 64 columns straight into MFMA operands (lane (n, h) of a 32-column set
+// takes 16 code bytes = words 4h .. 4h+3 of the row's 128-weight step; MFMA
+// k-step kk pairs slice kk of lane h = 0 with slice kk of lane h = 1, and
+// the A fragments are read from LDS in the same order).  K advances 128 per
+// step; the activation tile is double-buffered in LDS (fp16, permuted
+// 16-groups), one barrier per step.
+//   gate/up: wave w = gate rows nt*128 + 32w .. +32 and the same up rows;
+//   down   : wave w = output columns nt*256 + 64w .. +64.
+// ---------------------------------------------------------------------------
+constexpr int kBM2 = 128, kBK2 = 128, kLDA2 = kBK2 + 8;  // A row pitch in halves
+
+template <int QBITS>
+struct BRaw2 {
+  uint4v c;        // 16 code bytes: words 4h .. 4h+3
+  uint32_t s;      // two fp16 scales: blocks 2h, 2h + 1
+  uint32_t hb[2];  // 3-bit: high-plane bits of the 64 codes
+};
+
+template <int QBITS>
+__device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, const uint16_t* scales, int rows,
+                                        int K, int row, int step, int h, bool ok) {
+  // blocks of this lane: b0 = 4 * step + 2h and b0 + 1, each zero past K or
+  // past the matrix.  Every load stays inside its row (8-byte code loads,
+  // 2-byte scale loads: rows of K / 4 code bytes are only 8-byte aligned)
+  // and is unconditional from a clamped address.
+  const int nb = K / 32;
+  const int b0 = 4 * step + 2 * h;
+  const bool in0 = ok && b0 < nb, in1 = ok && b0 + 1 < nb;
+  const int rr = in0 ? row : 0, bb0 = in0 ? b0 : 0, bb1 = in1 ? b0 + 1 : bb0;
+  const uint8_t* cr = codes + int64_t(rr) * (K / 4);
+  const uint16_t* sr = scales + int64_t(rr) * nb;
+  const uint2v c0 = *reinterpret_cast<const uint2v*>(cr + bb0 * 8);
+  const uint2v c1 = *reinterpret_cast<const uint2v*>(cr + bb1 * 8);
+  const uint32_t s0 = sr[bb0], s1 = sr[bb1];
+  r.c = uint4v{in0 ? c0[0] : 0u, in0 ? c0[1] : 0u, in1 ? c1[0] : 0u, in1 ? c1[1] : 0u};
+  r.s = (in0 ? s0 : 0u) | ((in1 ? s1 : 0u) << 16);
+  if constexpr (QBITS == 3) {
+    const uint32_t* hp = reinterpret_cast<const uint32_t*>(codes + int64_t(rows) * (K / 4) + int64_t(rr) * (K / 8));
+    const uint32_t h0 = hp[bb0], h1 = hp[bb1];
+    r.hb[0] = in0 ? h0 : 0u;
+    r.hb[1] = in1 ? h1 : 0u;
+  }
+}
+
+// word q (0..3) of a lane's step -> the two permuted k-slices
+template <int QBITS>
+__device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, half8& lo, half8& hi) {
+  const uint32_t sbits = q < 2 ? (r.s & 0xffffu) : (r.s >> 16);
+  const half2v s2 = as_half2(sbits | (sbits << 16));
+  if constexpr (QBITS == 2) {
+    dq2_word(r.c[q], s2, lo, hi);
+  } else {
+    const uint32_t hbits = (r.hb[q >> 1] >> (16 * (q & 1))) & 0xffffu;
+    dq3_word(r.c[q], spread16(hbits), s2, lo, hi);
+  }
+}
+
+template <int QBITS, typename AT, bool GATEUP, int NWV>
+__global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void grouped_gemm2_kernel(FfnArgs a,
+                                                                                                 int n_ntiles) {
+  constexpr int NT = 64 * NWV;              // threads
+  constexpr int AI = kBM2 * (kBK2 / 16) / NT;  // A staging items (16-element groups) per thread
+  __shared__ __attribute__((aligned(16))) f16 As[2][kBM2 * kLDA2];
+
+  // ---- work item (XCD-aware remap over the real items)
+  const int n_tiles = a.header[kHdrTiles];
+  const int total = n_tiles * n_ntiles;
+  const int per = (total + 7) / 8;
+  const int b = blockIdx.x;
+  if (b >= 8 * per) return;
+  const int L = (b % 8) * per + b / 8;
+  if (L >= total) return;
+  const int tile = L / n_ntiles, nt = L - tile * n_ntiles;
+  const int e = a.tile_expert[tile], m0 = a.tile_m0[tile];
+  const bool shared = e < 0;
+  const int lo = shared ? 0 : a.offsets[e];
+  const int m_count = shared ? int(a.T) : a.offsets[e + 1] - lo;
+  const int rows_valid = min(kBM2, m_count - m0);
+  const int H = a.H;
+  const int K = GATEUP ? H : (shared ? a.Is : a.I);
+  const int Nrows = GATEUP ? (shared ? a.Is : a.I) : H;  // rows of each weight matrix
+  const int64_t ex = shared ? 0 : e;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  static_assert(AI >= 1 && AI * NT == kBM2 * (kBK2 / 16), "A staging covers the tile");
+
+  // ---- A sources: thread handles items tid + NT i (i < AI) of the 128 x 8 groups
+  const AT* asrc[AI];
+  int arow[AI], agrp[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int item = tid + NT * i;
+    arow[i] = item >> 3;
+    agrp[i] = item & 7;
+    const int r = min(arow[i], rows_valid - 1);  // rows past the segment read a real row; never stored
+    if constexpr (GATEUP) {
+      const int64_t tok = shared ? int64_t(m0 + r) : int64_t(a.sorted_pair[lo + m0 + r] / a.k);
+      asrc[i] = static_cast<const AT*>(a.x) + tok * H;
+    } else {
+      const f16* hb = shared ? a.h_shared + int64_t(m0 + r) * K : a.h_routed + int64_t(lo + m0 + r) * K;
+      asrc[i] = reinterpret_cast<const AT*>(hb);
+    }
+  }
+  // ---- B sources: two 32-column sets per wave
+  const uint8_t* bc[2];
+  const uint16_t* bsc[2];
+  int brow[2];
+  bool bok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    QMat M;
+    if constexpr (GATEUP) {
+      M = j == 0 ? (shared ? a.sg : a.rg) : (shared ? a.su : a.ru);
+      brow[j] = nt * (32 * NWV) + 32 * wv + n;
+    } else {
+      M = shared ? a.sd : a.rd;
+      brow[j] = nt * (64 * NWV) + 64 * wv + 32 * j + n;
+    }
+    bc[j] = M.codes + ex * M.code_stride;
+    bsc[j] = M.scales + ex * M.scale_stride;
+    bok[j] = brow[j] < Nrows;
+  }
+  const int nsteps = (K + kBK2 - 1) / kBK2;
+
+  using Raw = ARaw<AT>;
+  constexpr int AR = (AI + 1) / 2;  // ARaw holds two groups
+  auto load_a = [&](int step, Raw (&r)[AR]) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      int col = step * kBK2 + agrp[i] * 16;
+      if (col >= K) col = 0;  // K tail: the matching weights are zero
+      load_araw<AT>(asrc[i] + col, r[i >> 1], i & 1);
+    }
+  };
+  auto store_a = [&](const Raw (&r)[AR], f16* buf) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      half8 l8, h8;
+      cvt_araw<AT>(r[i >> 1], i & 1, l8, h8);
+      half8* d = reinterpret_cast<half8*>(buf + arow[i] * kLDA2 + agrp[i] * 16);
+      d[0] = l8;
+      d[1] = h8;
+    }
+  };
+
+  float16v acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  Raw ar[AR];
+  BRaw2<QBITS> bcur[2], bnext[2];
+  load_a(0, ar);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) load_b2<QBITS>(bcur[j], bc[j], bsc[j], Nrows, K, brow[j], 0, h, bok[j]);
+  store_a(ar, As[0]);
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    const int cur = step & 1;
+    const bool more = step + 1 < nsteps;
+    if (more) {
+      load_a(step + 1, ar);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) load_b2<QBITS>(bnext[j], bc[j], bsc[j], Nrows, K, brow[j], step + 1, h, bok[j]);
+    }
+    const f16* Ab = As[cur];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // word q of each lane's step: k-steps 2q (lo) and 2q + 1 (hi)
+      half8 blo[2], bhi[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bcur[j], q, blo[j], bhi[j]);
+#pragma unroll
+      for (int half_ = 0; half_ < 2; ++half_) {
+        half8 af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + 64 * h + 16 * q + 8 * half_);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], half_ ? bhi[j] : blo[j], acc[i][j]);
+      }
+    }
+    if (more) {
+      store_a(ar, As[cur ^ 1]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bcur[j] = bnext[j];
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue.  32 x 32 D layout: lane l holds column l % 32 and rows
+  // 8*(q/4) + 4*(l/32) + q%4, q = 0..15.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+      if (m >= rows_valid) continue;
+      if constexpr (GATEUP) {
+        const int gr = brow[0];
+        if (bok[0]) {
+          const float g = acc[i][0][q], u = acc[i][1][q];
+          const float hv = g / (1.0f + expf(-g)) * u;
+          const int hw = shared ? a.Is : a.I;
+          f16* hout = shared ? a.h_shared + int64_t(m0 + m) * hw : a.h_routed + int64_t(lo + m0 + m) * hw;
+          hout[hcol(gr)] = f16(hv);
+        }
+      } else {
+        float* yrow = shared ? a.shared_out + int64_t(m0 + m) * H : a.y_sorted + int64_t(lo + m0 + m) * H;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (bok[j]) yrow[brow[j]] = acc[i][j][q];
+      }
+    }
+  }
+}
+
 template <int QBITS, typename XT>
 static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases) {
+  // The wide-tile kernel pays off when the segments fill its 128-row tiles:
+  // T * k pairs of at least one tile per expert on average.  Below that
+  // (thin segments, e.g. uniform routing of a few thousand tokens) the
+  // LDS-dequantising kernel's 128 x 128 tiles spread the weights over more
+  // workgroups.
+  const bool wide = MOE_GROUPED2 && a.T * a.k >= int64_t(kBM2) * a.E;
   if (phases & kPhaseGateUp) {
     const int rows = std::max(a.I, a.has_shared ? a.Is : 0);
-    const int nn = (rows + 63) / 64;
-    const int64_t total = max_tiles * nn;
-    const unsigned grid = unsigned((total + 7) / 8 * 8);
-    grouped_gemm_kernel<QBITS, XT, true><<<grid, 256, 0, stream>>>(a, nn);
+    if (wide) {
+      constexpr int W = MOE_GROUPED2_WAVES;
+      const int nn = (rows + 32 * W - 1) / (32 * W);
+      const int64_t total = max_tiles * nn;
+      const unsigned grid = unsigned((total + 7) / 8 * 8);
+      grouped_gemm2_kernel<QBITS, XT, true, W><<<grid, 64 * W, 0, stream>>>(a, nn);
+    } else {
+      const int nn = (rows + 63) / 64;
+      const int64_t total = max_tiles * nn;
+      const unsigned grid = unsigned((total + 7) / 8 * 8);
+      grouped_gemm_kernel<QBITS, XT, true><<<grid, 256, 0, stream>>>(a, nn);
+    }
   }
   if (phases & kPhaseDown) {
-    const int nn = (a.H + kBN - 1) / kBN;
-    const int64_t total = max_tiles * nn;
-    const unsigned grid = unsigned((total + 7) / 8 * 8);
-    grouped_gemm_kernel<QBITS, f16, false><<<grid, 256, 0, stream>>>(a, nn);
+    if (wide) {
+      constexpr int W = MOE_GROUPED2_WAVES;
+      const int nn = (a.H + 64 * W - 1) / (64 * W);
+      const int64_t total = max_tiles * nn;
+      const unsigned grid = unsigned((total + 7) / 8 * 8);
+      grouped_gemm2_kernel<QBITS, f16, false, W><<<grid, 64 * W, 0, stream>>>(a, nn);
+    } else {
+      const int nn = (a.H + kBN - 1) / kBN;
+      const int64_t total = max_tiles * nn;
+      const unsigned grid = unsigned((total + 7) / 8 * 8);
+      grouped_gemm_kernel<QBITS, f16, false><<<grid, 256, 0, stream>>>(a, nn);
+    }
   }
   return hipGetLastError();
 }

@@ -51,6 +51,12 @@ RAGGED = [
     ("g4", 64, 32, 8, 2, 32, 3, 4, torch.float32),
     ("g5", 256, 192, 33, 8, 96, 3, 517, torch.bfloat16),
     ("g6", 192, 320, 7, 2, 128, 2, 1, torch.bfloat16),
+    # segments of at least one 128-row tile per expert on average (the wide-tile kernel),
+    # with odd block counts along K (96 = 3 blocks) and partial column tiles
+    ("w1", 96, 96, 2, 1, 64, 2, 300, torch.bfloat16),
+    ("w2", 160, 96, 3, 2, 32, 3, 400, torch.float32),
+    ("w3", 256, 192, 4, 2, 0, 2, 600, torch.bfloat16),
+    ("w4", 2048, 704, 4, 2, 704, 3, 520, torch.bfloat16),
 ]
 
 
