@@ -501,8 +501,9 @@ def main():
                                "in turn", "global_batch": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gu_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "gemv_gateup_kernel (gate/up dequant-GEMV + SwiGLU, one token, 10 routed + shared "
-                               "expert), launched alone, HIP events on its stream",
+                     "kernel": "gemv_gateup_1tok_kernel<2, 64, unsigned short> (gate/up dequant-GEMV + SwiGLU, one "
+                               "token, 10 routed + shared expert, slot table given), launched alone, HIP "
+                               "events on its stream",
                      "bytes_per_launch": gu_bytes, "avg_us": gu_ms * 1e3,
                      "layer": {"avg_us": layer_ms * 1e3, "bytes": layer_bytes, "GBs": achieved},
                      "down_gemv": {"avg_us": dn_ms * 1e3, "bytes": dn_bytes, "GBs": dn_bytes / dn_ms / 1e6},

@@ -105,6 +105,11 @@ def test_decode16_layer_and_batch_invariance():
         out_t, idx_t, _, _ = _run_layer(M, dl, x[t:t + 1].contiguous())
         assert np.array_equal(idx_t[0], idx_all[t])
         assert np.array_equal(out_t[0], out_all[t]), f"token {t} depends on the rest of the batch"
+    # every batch size of the multi-token kernels: the first T tokens alone
+    for T in range(2, 16):
+        out_T, idx_T, _, _ = _run_layer(M, dl, x[:T].contiguous())
+        assert np.array_equal(idx_T, idx_all[:T])
+        assert np.array_equal(out_T, out_all[:T]), f"batch of {T} differs from the same tokens among 16"
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode16", "decode1"])
