@@ -35,6 +35,9 @@ constexpr int kBM = 128, kBN = 128, kBK = 64, kLDA = kBK + 8;  // row pitch in h
 #ifndef MOE_GROUPED2_WAVES
 #define MOE_GROUPED2_WAVES 8
 #endif
+#ifndef MOE_GROUPED2_PD
+#define MOE_GROUPED2_PD 1
+#endif
 
 // Raw (not yet dequantised) B operand of one thread for one K step.
 struct BRaw {
@@ -350,7 +353,7 @@ __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, half8& lo, h
   }
 }
 
-template <int QBITS, typename AT, bool GATEUP, int NWV>
+template <int QBITS, typename AT, bool GATEUP, int NWV, int PD>
 __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void grouped_gemm2_kernel(FfnArgs a,
                                                                                                  int n_ntiles) {
   constexpr int NT = 64 * NWV;              // threads
@@ -448,45 +451,54 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
+  // B ring: the weights of steps step .. step + PD - 1 are in flight (a
+  // ring of PD register sets; slot p holds steps p, p + PD, ...).  Loads for
+  // steps past K are clamped in load_b2 (zero weights from a valid address).
   Raw ar[AR];
-  BRaw2<QBITS> bcur[2], bnext[2];
+  BRaw2<QBITS> bring[PD][2];
   load_a(0, ar);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) load_b2<QBITS>(bcur[j], bc[j], bsc[j], Nrows, K, brow[j], 0, h, bok[j]);
+  for (int p = 0; p < PD; ++p)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_b2<QBITS>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], p, h, bok[j]);
   store_a(ar, As[0]);
   __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      load_a(step + 1, ar);
+  for (int s0 = 0; s0 < nsteps; s0 += PD) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) load_b2<QBITS>(bnext[j], bc[j], bsc[j], Nrows, K, brow[j], step + 1, h, bok[j]);
-    }
-    const f16* Ab = As[cur];
+    for (int p = 0; p < PD; ++p) {
+      const int step = s0 + p;
+      if (step >= nsteps) break;
+      const int cur = step & 1;
+      const bool more = step + 1 < nsteps;
+      BRaw2<QBITS> bcur[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {  // word q of each lane's step: k-steps 2q (lo) and 2q + 1 (hi)
-      half8 blo[2], bhi[2];
+      for (int j = 0; j < 2; ++j) bcur[j] = bring[p][j];
+      if (more) load_a(step + 1, ar);
+      if (step + PD < nsteps) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bcur[j], q, blo[j], bhi[j]);
-#pragma unroll
-      for (int half_ = 0; half_ < 2; ++half_) {
-        half8 af[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + 64 * h + 16 * q + 8 * half_);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], half_ ? bhi[j] : blo[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) load_b2<QBITS>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], step + PD, h, bok[j]);
       }
-    }
-    if (more) {
-      store_a(ar, As[cur ^ 1]);
+      const f16* Ab = As[cur];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bcur[j] = bnext[j];
+      for (int q = 0; q < 4; ++q) {  // word q of each lane's step: k-steps 2q (lo) and 2q + 1 (hi)
+        half8 blo[2], bhi[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bcur[j], q, blo[j], bhi[j]);
+#pragma unroll
+        for (int half_ = 0; half_ < 2; ++half_) {
+          half8 af[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            af[i] = *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + 64 * h + 16 * q + 8 * half_);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], half_ ? bhi[j] : blo[j], acc[i][j]);
+        }
+      }
+      if (more) store_a(ar, As[cur ^ 1]);
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // ---- epilogue.  32 x 32 D layout: lane l holds column l % 32 and rows
@@ -531,7 +543,7 @@ static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStrea
       const int nn = (rows + 32 * W - 1) / (32 * W);
       const int64_t total = max_tiles * nn;
       const unsigned grid = unsigned((total + 7) / 8 * 8);
-      grouped_gemm2_kernel<QBITS, XT, true, W><<<grid, 64 * W, 0, stream>>>(a, nn);
+      grouped_gemm2_kernel<QBITS, XT, true, W, MOE_GROUPED2_PD><<<grid, 64 * W, 0, stream>>>(a, nn);
     } else {
       const int nn = (rows + 63) / 64;
       const int64_t total = max_tiles * nn;
@@ -545,7 +557,7 @@ static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStrea
       const int nn = (a.H + 64 * W - 1) / (64 * W);
       const int64_t total = max_tiles * nn;
       const unsigned grid = unsigned((total + 7) / 8 * 8);
-      grouped_gemm2_kernel<QBITS, f16, false, W><<<grid, 64 * W, 0, stream>>>(a, nn);
+      grouped_gemm2_kernel<QBITS, f16, false, W, MOE_GROUPED2_PD><<<grid, 64 * W, 0, stream>>>(a, nn);
     } else {
       const int nn = (a.H + kBN - 1) / kBN;
       const int64_t total = max_tiles * nn;

@@ -113,10 +113,17 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const XT* __restrict__
 // ---------------------------------------------------------------------------
 // Router logits on MFMA for bf16 activations and bf16 router weights
 // (v_mfma_f32_16x16x32_bf16: bf16 x bf16 products are exact in fp32).
-// Workgroup = 16 experts x 16 tokens, 8 waves; wave w takes the 32-wide
-// K blocks w, w+8, w+16, ...  Partial tiles are summed through LDS in wave
-// order, so a token's logits never depend on the other tokens.
+//
+// Accumulation order, the same in both MFMA router kernels so that a token's
+// logits are the same bits at every batch size: the 32-wide K blocks fall in
+// 8 classes of ceil(nkb / 8) consecutive blocks; each class is one MFMA chain
+// from zero in increasing block order; the class sums are added 0, 1, ..., 7
+// (S = a0, S = S + a1, ...), then the bias.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int router_class_len(int nkb) { return (nkb + 7) / 8; }
+
+// Few tokens: workgroup = 16 experts x 16 tokens, 8 waves; wave w runs class
+// w and the 8 partial tiles meet in LDS.
 __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
                                                          const uint16_t* __restrict__ w,
                                                          const float* __restrict__ bias, int E,
@@ -126,20 +133,21 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
   const int n = lane & 15, g = lane >> 4;
   const int e0 = blockIdx.x * 16;
   const int64_t t0 = int64_t(blockIdx.y) * 16;
-  const int nkb = H / 32;
+  const int nkb = H / 32, cl = router_class_len(nkb);
+  const int c0 = min(nkb, wv * cl), c1 = min(nkb, c0 + cl);
   const bool b_on = e0 + n < E;
   const bool a_on = t0 + n < T;
   const uint16_t* wrow = w + int64_t(b_on ? e0 + n : 0) * H + 8 * g;
   const uint16_t* xrow = x + (a_on ? t0 + n : 0) * H + 8 * g;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   constexpr int B = 8;  // K blocks per load batch
-  for (int kb0 = wv; kb0 < nkb; kb0 += 8 * B) {
+  for (int kb0 = c0; kb0 < c1; kb0 += B) {
     uint4v bw[B], ax[B];
 #pragma unroll
     for (int i = 0; i < B; ++i) {  // unconditional loads (clamped block, rows clamped above)
-      const int kb = kb0 + 8 * i;
-      const bool in = kb < nkb;
-      const int kbc = in ? kb : 0;
+      const int kb = kb0 + i;
+      const bool in = kb < c1;
+      const int kbc = in ? kb : kb0;
       const uint4v wl = *reinterpret_cast<const uint4v*>(wrow + kbc * 32);
       const uint4v xl = *reinterpret_cast<const uint4v*>(xrow + kbc * 32);
       bw[i] = (in && b_on) ? wl : uint4v{0u, 0u, 0u, 0u};
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
     }
 #pragma unroll
     for (int i = 0; i < B; ++i)
-      if (kb0 + 8 * i < nkb)
+      if (kb0 + i < c1)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ax[i]),
                                                       __builtin_bit_cast(bf16x8, bw[i]), acc, 0, 0, 0);
   }
@@ -170,9 +178,185 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
   }
 }
 
+// Many tokens: a 128-token x 128-expert tile per workgroup, 8 waves of
+// 32 tokens x 64 experts (2 x 4 MFMA blocks of 16 x 16).  The classes run
+// one after another, so a wave keeps two accumulators per output (the class
+// chain and the running sum S) instead of eight.  K advances RK blocks per
+// step (within a class); the workgroup stages each step's activation and
+// weight rows in LDS with row-contiguous 16-byte loads (a wave instruction
+// covers two 256-byte row pieces) and the next step's loads are in flight
+// during the MFMAs.  The logits tile goes out through LDS as whole 512-byte
+// row pieces.  Tiles are handed out so that the expert tiles of one token
+// tile run one after another on one XCD (its activations are read into one
+// L2).
+// ---------------------------------------------------------------------------
+constexpr int kRtT = 128, kRtE = 128;  // tile: tokens x experts
+constexpr int kRtOutPitch = kRtE + 4;   // LDS row pitch of the logits tile in floats
+#ifndef MOE_ROUTER_GEMM_MIN_T
+#define MOE_ROUTER_GEMM_MIN_T 2048
+#endif
+constexpr int64_t kRouterGemmMinT = MOE_ROUTER_GEMM_MIN_T;  // below: router_mfma_kernel's 16 x 16 tiles
+// LDS row pitch of the staged operands in bf16: an odd number of 16-byte
+// units, so the 16 rows of a fragment read hit distinct banks
+template <int RK>
+constexpr int rt_pitch() { return RK * 32 + 8; }
+template <int RK>
+constexpr size_t rt_lds() {
+  return std::max(size_t(kRtT + kRtE) * rt_pitch<RK>() * 2, size_t(kRtT) * kRtOutPitch * 4);
+}
+
+// RK = K blocks (of 32) per step; OCC = waves per SIMD the registers are
+// budgeted for (RK = 2 fits 128 registers, 4 waves: two workgroups per CU;
+// RK = 4 halves the steps and barriers but needs the 256 of 2 waves).
+template <int RK, int OCC>
+__global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
+                                                            const uint16_t* __restrict__ w,
+                                                            const float* __restrict__ bias, int E,
+                                                            float* __restrict__ logits, int n_et, int64_t total) {
+  constexpr int kPitch = rt_pitch<RK>();
+  extern __shared__ __attribute__((aligned(16))) uint16_t rs[];  // [kRtT + kRtE][kPitch] bf16, then the out tile
+  const int64_t per = (total + 7) / 8;
+  const int64_t L = int64_t(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (L >= total) return;
+  const int64_t tt = L / n_et;
+  const int et = int(L - tt * n_et);
+  const int64_t t0 = tt * kRtT;
+  const int e0 = et * kRtE;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int wt = wv >> 1, we = wv & 1;  // wave tile: tokens 32 wt .., experts 64 we ..
+  const int nkb = H / 32, cl = router_class_len(nkb);
+
+  // staging: 16-byte piece p = tid + 512 q (q < NQ) of the step's
+  // (kRtT + kRtE) rows x RK blocks: row p / (4 RK), piece p % (4 RK)
+  // of the row's 64 RK bytes (block piece / 4 of the step, quarter piece % 4)
+  constexpr int NQ = (kRtT + kRtE) * RK * 4 / 512;
+  static_assert(NQ * 512 == (kRtT + kRtE) * RK * 4 && kRtT * RK * 4 == 512 * (NQ / 2),
+                "staging covers the step; the first NQ / 2 pieces of a thread are activation rows");
+  // element offsets from the tile's first activation / weight row (rows
+  // past the end read the last real row; their results are never stored)
+  const uint16_t* xt = x + t0 * H;
+  const uint16_t* wt_ = w + int64_t(e0) * H;
+  const int t_last = int(min(T - t0, int64_t(kRtT))) - 1, e_last = min(E - e0, kRtE) - 1;
+  int off[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int p = tid + 512 * q, row = p / (4 * RK), pc = p % (4 * RK);
+    off[q] = (row < kRtT ? min(row, t_last) : min(row - kRtT, e_last)) * H + pc * 8;
+  }
+  uint4v stg[NQ];
+  // step s of class c covers blocks b .. b + RK - 1 (those at or past the class end are zero)
+  auto load_step = [&](int b, int cend) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int kb = b + (tid + 512 * q) % (4 * RK) / 4;
+      const bool in = kb < cend;
+      const uint16_t* base = q < NQ / 2 ? xt : wt_;  // pieces q < NQ/2 are activation rows
+      const uint4v v = *reinterpret_cast<const uint4v*>(base + off[q] + (in ? b : 0) * 32);  // clamped, unconditional
+      stg[q] = in ? v : uint4v{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_step = [&]() {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int p = tid + 512 * q, row = p / (4 * RK), pc = p % (4 * RK);
+      *reinterpret_cast<uint4v*>(rs + row * kPitch + pc * 8) = stg[q];
+    }
+  };
+
+  float4v S[2][4], acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) S[i][j] = acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+  const int n_cls = (nkb + cl - 1) / cl;  // non-empty classes (an empty class adds +0: S is never -0)
+  // the first step's loads
+  load_step(0, min(nkb, cl));
+  for (int c = 0; c < n_cls; ++c) {
+    const int cb = c * cl, ce = min(nkb, cb + cl);
+    for (int b = cb; b < ce; b += RK) {
+      __syncthreads();  // the previous step's fragments are read
+      store_step();
+      __syncthreads();
+      // the next step's loads (next block group of this class, or the next class's first)
+      {
+        int nb = b + RK, nce = ce;
+        if (nb >= ce) {
+          nb = ce;
+          nce = min(nkb, ce + cl);
+        }
+        if (nb < nkb) load_step(nb, nce);
+      }
+      const int nsub = min(RK, ce - b);
+      for (int k = 0; k < nsub; ++k) {
+        uint4v af[2], bf[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[i] = *reinterpret_cast<const uint4v*>(rs + (32 * wt + 16 * i + n) * kPitch + k * 32 + 8 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bf[j] = *reinterpret_cast<const uint4v*>(rs + (kRtT + 64 * we + 16 * j + n) * kPitch + k * 32 + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                                __builtin_bit_cast(bf16x8, bf[j]), acc[i][j], 0,
+                                                                0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        S[i][j] = c == 0 ? acc[i][j] : S[i][j] + acc[i][j];
+        acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+      }
+  }
+  // logits tile through LDS: S block (i, j) element r = token 32 wt + 16 i + 4 g + r, expert 64 we + 16 j + n
+  __syncthreads();
+  float* os = reinterpret_cast<float*>(rs);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) os[(32 * wt + 16 * i + 4 * g + r) * kRtOutPitch + 64 * we + 16 * j + n] = S[i][j][r];
+  __syncthreads();
+  // 16-byte stores and bias loads when every logits row and the bias are 16-byte aligned
+  const bool vec = E % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
+#pragma unroll
+  for (int q = 0; q < kRtT * kRtE / 4 / 512; ++q) {
+    const int p = tid + 512 * q, row = p >> 5, c4 = (p & 31) * 4;
+    const int64_t t = t0 + row;
+    const int e = e0 + c4;
+    if (t >= T || e >= E) continue;
+    float4v v = *reinterpret_cast<const float4v*>(os + row * kRtOutPitch + c4);
+    if (vec && e + 3 < E) {
+      const float4v bv = bias ? *reinterpret_cast<const float4v*>(bias + e) : float4v{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<float4v*>(logits + t * E + e) = v + bv;
+    } else {
+      for (int u = 0; u < 4 && e + u < E; ++u) logits[t * E + e + u] = v[u] + (bias ? bias[e + u] : 0.0f);
+    }
+  }
+}
+
 hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_t* w, const float* bias, int E,
                               float* logits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  if (T >= kRouterGemmMinT) {
+    const int n_et = (E + kRtE - 1) / kRtE;
+    const int64_t total = (T + kRtT - 1) / kRtT * n_et;
+    const int64_t grid = (total + 7) / 8 * 8;
+    if (total >= 512)  // two resident workgroups per CU have work: the 128-register variant
+      router_gemm_kernel<2, 4><<<unsigned(grid), 512, rt_lds<2>(), stream>>>(x, T, H, w, bias, E, logits, n_et,
+                                                                           total);
+    else
+      router_gemm_kernel<4, 2><<<unsigned(grid), 512, rt_lds<4>(), stream>>>(x, T, H, w, bias, E, logits, n_et,
+                                                                           total);
+    return hipGetLastError();
+  }
   const dim3 grid(unsigned((E + 15) / 16), unsigned((T + 15) / 16));
   router_mfma_kernel<<<grid, 512, 0, stream>>>(x, T, H, w, bias, E, logits);
   return hipGetLastError();

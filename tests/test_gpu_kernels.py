@@ -61,13 +61,44 @@ def _route(M, wl, T, layer=0):
     return logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), ol
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode1", 1), ("decode16", 16), ("decode16", 333)])
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode1", 1), ("decode16", 16), ("decode16", 333),
+                                    ("decode16", 2500), ("prefill", 33000)])
 def test_route_protocol(name, T):
     M = _lib()
     wl = synth.WORKLOADS[name]
     gl, gi, gw, ol = _route(M, wl, T)
     flagged = check_route_protocol(gl, gi, gw, ol, wl.shape.top_k)
     assert len(flagged) <= max(1, T // 100)
+
+
+@pytest.mark.parametrize("H,E,T", [(2048, 512, 2100), (96, 40, 2200), (64, 8, 2050), (4096, 130, 2088),
+                                   (2048, 512, 65600), (64, 8, 70000)])
+def test_router_tiles_match_small_batches(H, E, T):
+    """Logits of T >= 2048 tokens at once (128 x 128 tiles, both step
+    variants) are the same bits as the same tokens routed 16 at a time
+    (16 x 16 tiles): one accumulation order for every batch size, ragged
+    token and expert tiles included.  Large T: a sample of the 16-token
+    chunks, the first and the last among them."""
+    M = _lib()
+    wl = synth.custom("rt", H, 32, E, min(E, 8), 0, 2, T, seed=H + E, act_dtype=torch.bfloat16, zipf_bias=True)
+    s = wl.shape
+    w_r, bias = synth.router(wl, 0, "cuda")
+    x = synth.tokens(wl, "cuda")
+    arena = M.QArena(1, 64, 32, 2, "cuda")
+    q = M.QLayer(w_r, bias, arena, None)
+    big = torch.empty(T, E, device="cuda")
+    M.route(x, q, s, torch.empty(T, s.top_k, dtype=torch.int32, device="cuda"), torch.empty(T, s.top_k, device="cuda"),
+            logits=big)
+    starts = list(range(0, T, 16))
+    if len(starts) > 200:
+        rng = np.random.default_rng(T)
+        starts = sorted({starts[0], starts[-1], *rng.choice(starts, 60, replace=False).tolist()})
+    for t0 in starts:
+        t1 = min(T, t0 + 16)
+        small = torch.empty(t1 - t0, E, device="cuda")
+        M.route(x[t0:t1].contiguous(), q, s, torch.empty(t1 - t0, s.top_k, dtype=torch.int32, device="cuda"),
+                torch.empty(t1 - t0, s.top_k, device="cuda"), logits=small)
+        assert torch.equal(big[t0:t1], small), f"tokens {t0}..{t1 - 1}"
 
 
 def test_route_all_equal_logits_tie_rule():
