@@ -314,9 +314,29 @@ struct BRaw2 {
   uint32_t hb[2];  // 3-bit: high-plane bits of the 64 codes
 };
 
-template <int QBITS>
+// K64: K is a multiple of 64 (even block count per row), so a lane's two
+// blocks are in or out together and its 16 code bytes, 4 scale bytes (and
+// 8 high-plane bytes) are aligned for single loads.
+template <int QBITS, bool K64>
 __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, const uint16_t* scales, int rows,
                                         int K, int row, int step, int h, bool ok) {
+  if constexpr (K64) {
+    const int nb = K / 32;
+    const int b0 = 4 * step + 2 * h;
+    const bool in = ok && b0 < nb;
+    const int rr = in ? row : 0, bb = in ? b0 : 0;
+    const uint4v c = *reinterpret_cast<const uint4v*>(codes + int64_t(rr) * (K / 4) + bb * 8);
+    const uint32_t sv = *reinterpret_cast<const uint32_t*>(scales + int64_t(rr) * nb + bb);
+    r.c = in ? c : uint4v{0u, 0u, 0u, 0u};
+    r.s = in ? sv : 0u;
+    if constexpr (QBITS == 3) {
+      const uint2v hv = *reinterpret_cast<const uint2v*>(codes + int64_t(rows) * (K / 4) + int64_t(rr) * (K / 8) +
+                                                        bb * 4);
+      r.hb[0] = in ? hv[0] : 0u;
+      r.hb[1] = in ? hv[1] : 0u;
+    }
+    return;
+  }
   // blocks of this lane: b0 = 4 * step + 2h and b0 + 1, each zero past K or
   // past the matrix.  Every load stays inside its row (8-byte code loads,
   // 2-byte scale loads: rows of K / 4 code bytes are only 8-byte aligned)
@@ -353,7 +373,7 @@ __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, half8& lo, h
   }
 }
 
-template <int QBITS, typename AT, bool GATEUP, int NWV, int PD>
+template <int QBITS, typename AT, bool GATEUP, int NWV, int PD, bool K64>
 __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void grouped_gemm2_kernel(FfnArgs a,
                                                                                                  int n_ntiles) {
   constexpr int NT = 64 * NWV;              // threads
@@ -460,7 +480,7 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
 #pragma unroll
   for (int p = 0; p < PD; ++p)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) load_b2<QBITS>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], p, h, bok[j]);
+    for (int j = 0; j < 2; ++j) load_b2<QBITS, K64>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], p, h, bok[j]);
   store_a(ar, As[0]);
   __syncthreads();
   for (int s0 = 0; s0 < nsteps; s0 += PD) {
@@ -476,7 +496,8 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
       if (more) load_a(step + 1, ar);
       if (step + PD < nsteps) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) load_b2<QBITS>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], step + PD, h, bok[j]);
+        for (int j = 0; j < 2; ++j) load_b2<QBITS, K64>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], step + PD, h,
+                                                        bok[j]);
       }
       const f16* Ab = As[cur];
 #pragma unroll
@@ -543,7 +564,8 @@ static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStrea
       const int nn = (rows + 32 * W - 1) / (32 * W);
       const int64_t total = max_tiles * nn;
       const unsigned grid = unsigned((total + 7) / 8 * 8);
-      grouped_gemm2_kernel<QBITS, XT, true, W, MOE_GROUPED2_PD><<<grid, 64 * W, 0, stream>>>(a, nn);
+      if (a.H % 64 == 0) grouped_gemm2_kernel<QBITS, XT, true, W, MOE_GROUPED2_PD, true><<<grid, 64 * W, 0, stream>>>(a, nn);
+      else grouped_gemm2_kernel<QBITS, XT, true, W, MOE_GROUPED2_PD, false><<<grid, 64 * W, 0, stream>>>(a, nn);
     } else {
       const int nn = (rows + 63) / 64;
       const int64_t total = max_tiles * nn;
@@ -557,7 +579,10 @@ static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStrea
       const int nn = (a.H + 64 * W - 1) / (64 * W);
       const int64_t total = max_tiles * nn;
       const unsigned grid = unsigned((total + 7) / 8 * 8);
-      grouped_gemm2_kernel<QBITS, f16, false, W, MOE_GROUPED2_PD><<<grid, 64 * W, 0, stream>>>(a, nn);
+      if (a.I % 64 == 0 && (!a.has_shared || a.Is % 64 == 0))
+        grouped_gemm2_kernel<QBITS, f16, false, W, MOE_GROUPED2_PD, true><<<grid, 64 * W, 0, stream>>>(a, nn);
+      else
+        grouped_gemm2_kernel<QBITS, f16, false, W, MOE_GROUPED2_PD, false><<<grid, 64 * W, 0, stream>>>(a, nn);
     } else {
       const int nn = (a.H + kBN - 1) / kBN;
       const int64_t total = max_tiles * nn;
