@@ -163,28 +163,28 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 // (0, 0) computes them while its weight loads are in flight and stores the
 // rank-ordered selection and the rank <-> slot maps.
 // ---------------------------------------------------------------------------
+constexpr int k1tokWaves = 8;  // waves per workgroup of the single-token gate/up kernel
+
 template <int QBITS, int UNIT, typename XT>
-__global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, Decode1Sel sl) {
+__global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnArgs a, Decode1Sel sl) {
+  extern __shared__ __attribute__((aligned(16))) f16 xs1[];  // the token, fp16, permuted 16-groups
   __shared__ float red[4][2][16];
   constexpr int RB = 2;  // rounds per wave per load batch (rounds c and c + 4)
-  const int lane = threadIdx.x & 63, ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  constexpr int NT = 64 * k1tokWaves;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int ks = wv & 3, mat = wv >> 2;  // class ks; matrix 0 = gate, 1 = up
   const int n = lane & 15, g = lane >> 4;
   const int j = blockIdx.y;
   const int H = a.H;
   const int n_units = H / UNIT, rounds = (n_units + 3) / 4;
   const XT* xg = static_cast<const XT*>(a.x);
 
-  // the first batch of activations, independent of the slot: raw loads now
-  // (clamped units, all in flight together), conversion once the weight
-  // loads are out
-  Raw16<XT> xr[RB][UNIT / 16];
-#pragma unroll
-  for (int i = 0; i < RB; ++i) {
-    const int rp = i * 4 + ks, u = rp * 4 + g;
-    const int uc = rp < rounds && u < n_units ? u : 0;
-#pragma unroll
-    for (int d = 0; d < UNIT / 16; ++d) load_raw16(xg + uc * UNIT + 16 * d, xr[i][d]);
-  }
+  // the token's first 16-groups, independent of the slot: raw loads now,
+  // conversion into LDS once the weight loads are out
+  const int ngrp = H / 16;
+  Raw16<XT> xr;
+  const int g0 = min(int(threadIdx.x), ngrp - 1);
+  load_raw16(xg + g0 * 16, xr);
 
   bool shared;
   int64_t ex;
@@ -199,9 +199,9 @@ __global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, Decode
     hrow = shared ? 0 : j;
     if (!shared) {
       // one wave selects (the selection's ballot counts run on the CU's one
-      // scalar unit, so four waves would queue behind each other there)
+      // scalar unit, so several waves would queue behind each other there)
       __shared__ int s_ex;
-      if (ks == 0) {
+      if (wv == 0) {
         wave_keys<8>(sl.logits, a.E, K);
         wave_select<8>(K, a.k, sel);
         const int e = wave_nth_selected<8>(sel, j);  // slot j: the j-th selected expert in index order
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, Decode
       }
       __syncthreads();
       ex = s_ex;
-      rank_here = blockIdx.x == 0 && j == 0 && ks == 0;
+      rank_here = blockIdx.x == 0 && j == 0 && wv == 0;
     }
   } else {
     const int4 si = a.slots[j];
@@ -221,78 +221,77 @@ __global__ __launch_bounds__(256) void gemv_gateup_1tok_kernel(FfnArgs a, Decode
   }
   const int rows = shared ? a.Is : a.I;
   const int row = blockIdx.x * 16 + n;  // rows are multiples of 32: every row of the tile exists
-  const QMat G = shared ? a.sg : a.rg;
-  const QMat U = shared ? a.su : a.ru;
-  const uint8_t* gc = G.codes + ex * G.code_stride;
-  const uint16_t* gs = G.scales + ex * G.scale_stride;
-  const uint8_t* uc = U.codes + ex * U.code_stride;
-  const uint16_t* us = U.scales + ex * U.scale_stride;
+  const QMat M = shared ? (mat == 0 ? a.sg : a.su) : (mat == 0 ? a.rg : a.ru);
+  const uint8_t* wc = M.codes + ex * M.code_stride;
+  const uint16_t* wsc = M.scales + ex * M.scale_stride;
 
-  Unit<QBITS, UNIT> ug[RB], uu[RB];
-  float4v accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  const bool a_on = n == 0;  // MFMA row 0 is the token; rows 1..15 are zero
+  Unit<QBITS, UNIT> uw[RB];
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
   for (int b0 = 0; b0 * 4 < rounds; b0 += RB) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int rp = (b0 + i) * 4 + ks, u = rp * 4 + g;
-      if (rp < rounds && u < n_units) {
-        load_unit(ug[i], gc, gs, rows, H, row, u);
-        load_unit(uu[i], uc, us, rows, H, row, u);
-      } else {
-        zero_unit(ug[i]);
-        zero_unit(uu[i]);
-      }
+      if (rp < rounds && u < n_units) load_unit(uw[i], wc, wsc, rows, H, row, u);
+      else zero_unit(uw[i]);
     }
-    if (b0 == 0 && rank_here) {
-      // ranks, weights and the slot maps, while this wave's weight loads are in flight
-      float my_val;
-      int my_idx, my_slot;
-      wave_rank<8>(K, sel, a.k, my_val, my_idx, my_slot);
-      const float my_w = wave_topk_weight(my_val, a.k);
-      if (lane < a.k) {
-        sl.idx[lane] = my_idx;
-        sl.w[lane] = my_w;
-        sl.slot_of_rank[lane] = my_slot;
-        sl.slot_expert[my_slot] = my_idx;
+    if (b0 == 0) {
+      if (rank_here) {
+        // ranks, weights and the slot maps, while this wave's weight loads are in flight
+        float my_val;
+        int my_idx, my_slot;
+        wave_rank<8>(K, sel, a.k, my_val, my_idx, my_slot);
+        const float my_w = wave_topk_weight(my_val, a.k);
+        if (lane < a.k) {
+          sl.idx[lane] = my_idx;
+          sl.w[lane] = my_w;
+          sl.slot_of_rank[lane] = my_slot;
+          sl.slot_expert[my_slot] = my_idx;
+        }
+        if (lane == 0) sl.header[kHdrError] = 0;
       }
-      if (lane == 0) sl.header[kHdrError] = 0;
-    }
-    if (b0 > 0) {  // later batches (hidden > 2048): their activations, loaded after the weights
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int rp = (b0 + i) * 4 + ks, u = rp * 4 + g;
-        const int ucl = rp < rounds && u < n_units ? u : 0;
-#pragma unroll
-        for (int d = 0; d < UNIT / 16; ++d) load_raw16(xg + ucl * UNIT + 16 * d, xr[i][d]);
+      // the token into LDS (first groups from the early loads, any others now)
+      {
+        half8 lo, hi;
+        cvt_raw16(xr, lo, hi);
+        if (int(threadIdx.x) < ngrp) {
+          half8* dst = reinterpret_cast<half8*>(xs1 + threadIdx.x * 16);
+          dst[0] = lo;
+          dst[1] = hi;
+        }
+        for (int gi = NT + int(threadIdx.x); gi < ngrp; gi += NT) {
+          Raw16<XT> r2;
+          load_raw16(xg + gi * 16, r2);
+          cvt_raw16(r2, lo, hi);
+          half8* dst = reinterpret_cast<half8*>(xs1 + gi * 16);
+          dst[0] = lo;
+          dst[1] = hi;
+        }
       }
+      __syncthreads();
     }
+    // every lane reads the token's fragment (MFMA rows 1..15 repeat row 0;
+    // only row 0 of the result is used)
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int rp = (b0 + i) * 4 + ks;
       if (rp >= rounds) break;
       const int u = rp * 4 + g;
-      const bool on = a_on && u < n_units;
+      const int ua = u < n_units ? u : 0;  // units past K have zero weights
 #pragma unroll
       for (int d = 0; d < UNIT / 16; ++d) {
-        half8 glo, ghi, ulo, uhi, alo = {}, ahi = {};
-        dq_unit_word(ug[i], d, glo, ghi);
-        dq_unit_word(uu[i], d, ulo, uhi);
-        if (on) cvt_raw16(xr[i][d], alo, ahi);
-        accg = mfma16(alo, glo, accg);
-        accg = mfma16(ahi, ghi, accg);
-        accu = mfma16(alo, ulo, accu);
-        accu = mfma16(ahi, uhi, accu);
+        const half8* ap = reinterpret_cast<const half8*>(xs1 + ua * UNIT + 16 * d);
+        half8 wlo, whi;
+        dq_unit_word(uw[i], d, wlo, whi);
+        acc = mfma16(ap[0], wlo, acc);
+        acc = mfma16(ap[1], whi, acc);
       }
     }
   }
-  // row 0 of the result: lanes 0..15, element 0
-  if (ks > 0 && lane < 16) {
-    red[ks][0][n] = accg[0];
-    red[ks][1][n] = accu[0];
-  }
+  // row 0 of the result: lanes 0..15, element 0; the class partials meet in LDS
+  if (wv > 0 && lane < 16) red[ks][mat][n] = acc[0];
   __syncthreads();
-  if (ks == 0 && lane < 16) {
-    float sg = accg[0], su = accu[0];
+  if (wv == 0 && lane < 16) {
+    float sg = acc[0], su = red[0][1][n];
 #pragma unroll
     for (int q = 1; q < 4; ++q) {
       sg += red[q][0][n];
@@ -865,7 +864,7 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
     if (one) {
       const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
 #define GU(U_, X_) \
-  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 256, 0, stream>>>(a, Decode1Sel{})
+  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a, Decode1Sel{})
       if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
       else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
@@ -910,7 +909,7 @@ static hipError_t launch_decode1_q(const FfnArgs& a, const Decode1Sel& sel, floa
   {
     const bool u64 = a.H % 64 == 0;
     const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
-#define GU(U_, X_) gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 256, 0, stream>>>(a, sel)
+#define GU(U_, X_) gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a, sel)
     if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
     else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
