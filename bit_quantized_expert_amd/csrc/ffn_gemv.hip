@@ -581,10 +581,14 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
 #ifndef MOE_TP_EARLY
 #define MOE_TP_EARLY 2
 #endif
+// NW row blocks of 16 per workgroup; waves 0..NW-1 take the gate rows of
+// block wv, waves NW..2NW-1 the up rows (half the dequantisation per wave);
+// the up sums reach the gate waves through LDS for the SwiGLU.
 template <int QBITS, int UNIT, typename XT, int NW>
-__global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(FfnArgs a) {
+__global__ __launch_bounds__(128 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) f16 xs[];
-  constexpr int kThreads = 64 * NW;  // the launch's block size (blockDim would be a load)
+  __shared__ float4v up_x[NW][64];  // the up waves' sums, per lane
+  constexpr int kThreads = 128 * NW;  // the launch's block size (blockDim would be a load)
   constexpr int D = MOE_TP_D;
   static_assert(D % 4 == 0, "the pipeline depth is a multiple of the 4 accumulation classes");
   const int4 si = a.slots[blockIdx.y];
@@ -594,18 +598,16 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
   const int rows = shared ? a.Is : a.I;
   const int row_base = blockIdx.x * 16 * NW;
   if (row_base >= rows) return;
-  const QMat G = shared ? a.sg : a.rg;
-  const QMat U = shared ? a.su : a.ru;
-  const int64_t ex = shared ? 0 : si.x;
-  const uint8_t* gc = G.codes + ex * G.code_stride;
-  const uint16_t* gs = G.scales + ex * G.scale_stride;
-  const uint8_t* uc = U.codes + ex * U.code_stride;
-  const uint16_t* us = U.scales + ex * U.scale_stride;
   const int H = a.H, ldsw = H + 8;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int wr = wv % NW, mat = wv / NW;  // row block, matrix (0 gate, 1 up)
+  const QMat Mq = shared ? (mat == 0 ? a.sg : a.su) : (mat == 0 ? a.rg : a.ru);
+  const int64_t ex = shared ? 0 : si.x;
+  const uint8_t* wc = Mq.codes + ex * Mq.code_stride;
+  const uint16_t* wsc = Mq.scales + ex * Mq.scale_stride;
   const int n = lane & 15, g = lane >> 4;
-  const int row = row_base + wv * 16 + n;
-  const bool wave_on = row_base + wv * 16 < rows;
+  const int row = row_base + wr * 16 + n;
+  const bool wave_on = row_base + wr * 16 < rows;
   const int n_units = H / UNIT, rounds = (n_units + 3) / 4;
   const XT* x = static_cast<const XT*>(a.x);
   f16* hout = shared ? a.h_shared : a.h_routed;
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
       s_tok[__builtin_popcount(tmask & ((1u << threadIdx.x) - 1u))] = int(threadIdx.x);
     __syncthreads();
   }
-  constexpr int NB = sizeof(XT) == 4 ? 4 : 8;  // staging items per thread per batch
+  constexpr int NB = sizeof(XT) == 4 ? 2 : 4;  // staging items per thread per batch
   constexpr int NBE = MOE_TP_EARLY;             // items per thread of an early staging (registers held
                                                 // across the weight loads)
   const int chunks = H / 16;
@@ -638,17 +640,12 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
         load_raw16(x + int64_t(s_tok[r]) * H + gg * 16, raw0[q]);
       }
     }
-    Unit<QBITS, UNIT> ug[D], uu[D];
+    Unit<QBITS, UNIT> uw[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       const int u = i * 4 + g;
-      if (wave_on && i < rounds && u < n_units) {
-        load_unit(ug[i], gc, gs, rows, H, row, u);
-        load_unit(uu[i], uc, us, rows, H, row, u);
-      } else {
-        zero_unit(ug[i]);
-        zero_unit(uu[i]);
-      }
+      if (wave_on && i < rounds && u < n_units) load_unit(uw[i], wc, wsc, rows, H, row, u);
+      else zero_unit(uw[i]);
     }
     __syncthreads();
     if (early) {
@@ -697,9 +694,9 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
       }
     }
     __syncthreads();
-    float4v accg[4], accu[4];
+    float4v acc[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) accg[c] = accu[c] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
     if (wave_on) {
       // Rows past the tokens (and units past K, whose weights are zero) read
       // a real, finite row: MFMA rows are independent and the extra rows of
@@ -710,35 +707,32 @@ __global__ __launch_bounds__(64 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(Ff
         for (int i = 0; i < D; ++i) {
           const int r = r0 + i;
           if (r >= rounds) break;
-          const Unit<QBITS, UNIT> cg = ug[i], cu = uu[i];
+          const Unit<QBITS, UNIT> cw = uw[i];
           const int rn = r + D, un = rn * 4 + g;
-          if (rn < rounds && un < n_units) {
-            load_unit(ug[i], gc, gs, rows, H, row, un);
-            load_unit(uu[i], uc, us, rows, H, row, un);
-          }
+          if (rn < rounds && un < n_units) load_unit(uw[i], wc, wsc, rows, H, row, un);
           const int u = r * 4 + g;
           const int ua = u < n_units ? u : 0;
 #pragma unroll
           for (int d = 0; d < UNIT / 16; ++d) {
-            half8 glo, ghi, ulo, uhi;
-            dq_unit_word(cg, d, glo, ghi);
-            dq_unit_word(cu, d, ulo, uhi);
+            half8 wlo, whi;
+            dq_unit_word(cw, d, wlo, whi);
             const half8* ap = reinterpret_cast<const half8*>(xrow + ua * UNIT + 16 * d);
             const half8 alo = ap[0], ahi = ap[1];
             const int c = i & 3;  // class of round r = r0 + i (r0 is a multiple of D, D of 4)
-            accg[c] = mfma16(alo, glo, accg[c]);
-            accg[c] = mfma16(ahi, ghi, accg[c]);
-            accu[c] = mfma16(alo, ulo, accu[c]);
-            accu[c] = mfma16(ahi, uhi, accu[c]);
+            acc[c] = mfma16(alo, wlo, acc[c]);
+            acc[c] = mfma16(ahi, whi, acc[c]);
           }
         }
       }
-      float4v sg = accg[0], su = accu[0];
+      float4v sum = acc[0];
 #pragma unroll
-      for (int c = 1; c < 4; ++c) {
-        sg += accg[c];
-        su += accu[c];
-      }
+      for (int c = 1; c < 4; ++c) sum += acc[c];
+      if (mat == 1) up_x[wr][lane] = sum;
+      acc[0] = sum;
+    }
+    __syncthreads();  // the up sums are in LDS
+    if (wave_on && mat == 0) {
+      const float4v sg = acc[0], su = up_x[wr][lane];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = 4 * g + j;
@@ -871,7 +865,7 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
     } else {
       const size_t lds = size_t(mrows) * (a.H + 8) * sizeof(f16);
       const dim3 grid(unsigned((max_rows + 16 * NW - 1) / (16 * NW)), unsigned(slots));
-#define GU(U_, X_) gemv_gateup_tp_kernel<QBITS, U_, X_, NW><<<grid, 64 * NW, lds, stream>>>(a)
+#define GU(U_, X_) gemv_gateup_tp_kernel<QBITS, U_, X_, NW><<<grid, 128 * NW, lds, stream>>>(a)
       if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
       else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
