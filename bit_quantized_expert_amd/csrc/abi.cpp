@@ -241,7 +241,7 @@ hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, co
   if (!(flags & MOE_FFN_REUSE_PLAN)) {
     hipError_t e = moe::launch_plan(offsets, s->n_experts, T, a.has_shared, tile_bm, at<int32_t>(ws, W.header),
                                     at<int4>(ws, W.slots), at<int32_t>(ws, W.tile_expert),
-                                    at<int32_t>(ws, W.tile_m0), st);
+                                    at<int32_t>(ws, W.tile_m0), sorted_pair, s->top_k, st);
     if (e != hipSuccess) return e;
   }
   const int phases = (flags & MOE_FFN_SKIP_GATEUP ? 0 : moe::kPhaseGateUp) | (flags & MOE_FFN_SKIP_DOWN ? 0 : moe::kPhaseDown);

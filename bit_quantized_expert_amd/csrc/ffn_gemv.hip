@@ -30,7 +30,8 @@ namespace moe {
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int64_t T,
                                                    int has_shared, int tile_bm, int32_t* __restrict__ header,
                                                    int4* __restrict__ slots, int32_t* __restrict__ tile_expert,
-                                                   int32_t* __restrict__ tile_m0, int n_slots) {
+                                                   int32_t* __restrict__ tile_m0, int n_slots,
+                                                   const int32_t* __restrict__ sorted_pair, int k) {
   __shared__ int flag[kMaxExperts];
   __shared__ int ntile[kMaxExperts];
   __shared__ int tmp[16];
@@ -45,7 +46,21 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += 1024) {
     const int lo = offsets[e];
     const int c = offsets[e + 1] - lo;
-    if (c > 0) slots[flag[e]] = int4{e, lo, c, 0};
+    if (c > 0) {
+      // token mask of the slot for small batches (the GEMV kernels then know
+      // the slot's tokens without reading sorted_pair); 0 = not given.  Pair
+      // ids that are not those of a permutation of T * k pairs cannot make a
+      // correct result; their tokens are clamped into [0, T) so that no
+      // kernel reads outside the activations.
+      uint32_t mask = 0u;
+      if (sorted_pair && T <= kGemvMaxM) {
+        for (int q = lo; q < lo + c; ++q) {
+          const int t = min(max(sorted_pair[q] / k, 0), int(T) - 1);
+          mask |= 1u << t;
+        }
+      }
+      slots[flag[e]] = int4{e, lo, c, int(mask)};
+    }
     if (tile_bm > 0) {
       int pos = ntile[e];
       for (int m0 = 0; m0 < c; m0 += tile_bm, ++pos) {
@@ -55,7 +70,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     }
   }
   const int n_valid = n_active + (has_shared ? 1 : 0);
-  if (threadIdx.x == 0 && has_shared) slots[n_active] = int4{-1, 0, int(T), 0};
+  if (threadIdx.x == 0 && has_shared)
+    slots[n_active] = int4{-1, 0, int(T), sorted_pair && T <= kGemvMaxM ? int((1u << T) - 1u) : 0};
   for (int s = n_valid + threadIdx.x; s < n_slots; s += 1024) slots[s] = int4{0, 0, 0, 0};
   int n_tiles = n_routed_tiles;
   if (tile_bm > 0 && has_shared) {
@@ -75,10 +91,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm, int32_t* header,
-                       int4* slots, int32_t* tile_expert, int32_t* tile_m0, hipStream_t stream) {
+                       int4* slots, int32_t* tile_expert, int32_t* tile_m0, const int32_t* sorted_pair, int k,
+                       hipStream_t stream) {
   const int n_slots = int(std::min<int64_t>(E, T * 32)) + 1;  // covers min(E, T*k) + 1 for every k <= 32
   plan_kernel<<<1, 1024, 0, stream>>>(offsets, E, T, has_shared, tile_bm, header, slots, tile_expert, tile_m0,
-                                      n_slots);
+                                      n_slots, sorted_pair, k);
   return hipGetLastError();
 }
 
@@ -581,6 +598,10 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
 #ifndef MOE_TP_EARLY
 #define MOE_TP_EARLY 2
 #endif
+#ifndef MOE_GEMV_PERS
+#define MOE_GEMV_PERS 1
+#endif
+constexpr int kPersGrid = 512;  // persistent gate/up workgroups (two per CU)
 // NW row blocks of 16 per workgroup; waves 0..NW-1 take the gate rows of
 // block wv, waves NW..2NW-1 the up rows (half the dequantisation per wave);
 // the up sums reach the gate waves through LDS for the SwiGLU.
@@ -746,6 +767,179 @@ __global__ __launch_bounds__(128 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(F
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent gate/up for 2..kGemvMaxM tokens: the same per-row arithmetic as
+// gemv_gateup_tp_kernel (8 waves, 64 rows per work item, gate and up waves,
+// four round classes), but a fixed grid of G workgroups each walks a
+// contiguous run of the (slot, 64-row block) items.  All T tokens are staged
+// in LDS once per workgroup (a slot's MFMA rows pick its tokens through the
+// token mask), and the weight pipeline runs on across items: the next item's
+// slot entry is requested when an item starts and its first D rounds of
+// weights while the current item's last D rounds are computed.  So the
+// first-load latency is paid once per workgroup instead of once per item.
+// Requires H % (16 UNIT) == 0 (whole pipeline groups per item) and Is = I or
+// no shared expert (one item size).
+// ---------------------------------------------------------------------------
+template <int QBITS, int UNIT, typename XT>
+__global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_rb, int G,
+                                                               const int4* __restrict__ slots,
+                                                               const int32_t* __restrict__ header) {
+  // slots / header are a.slots / a.header, read-only here: scalar loads,
+  // which wait on their own counter instead of behind the weight loads
+  constexpr int NW = 4, D = 4, kThreads = 512;
+  extern __shared__ __attribute__((aligned(16))) f16 xs[];  // [T][H + 8]
+  __shared__ float4v up_x[NW][64];
+  const int H = a.H, ldsw = H + 8, T = int(a.T);
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int wr = wv % NW, mat = wv / NW;
+  const int n = lane & 15, g = lane >> 4;
+  const int n_units = H / UNIT, rounds = n_units / 4;  // a multiple of D (host-checked)
+  const int n_items = header[kHdrValid] * n_rb;
+  const int q = n_items / G, rem = n_items - q * G, b = blockIdx.x;
+  const int it0 = b * q + min(b, rem), it1 = it0 + q + (b < rem ? 1 : 0);
+  if (it0 >= it1) return;
+
+  // an item's weight source for this wave (plain values: no aggregate copies)
+  auto make = [&](int it, int4 si, const uint8_t*& wc, const uint16_t*& wsc, int& rows, int& row, bool& on) {
+    const bool shared = si.x < 0;
+    rows = shared ? a.Is : a.I;
+    const int row_base = (it % n_rb) * 16 * NW + wr * 16;
+    on = si.z > 0 && row_base < rows;
+    row = row_base + n;
+    const QMat Mq = shared ? (mat == 0 ? a.sg : a.su) : (mat == 0 ? a.rg : a.ru);
+    const int64_t ex = shared ? 0 : si.x;
+    wc = Mq.codes + ex * Mq.code_stride;
+    wsc = Mq.scales + ex * Mq.scale_stride;
+  };
+
+  int4 si_cur = slots[it0 / n_rb];
+  const uint8_t* c_wc;
+  const uint16_t* c_wsc;
+  int c_rows, c_row;
+  bool c_on;
+  make(it0, si_cur, c_wc, c_wsc, c_rows, c_row, c_on);
+  // Weight loads are unconditional (a wave past its rows reads the last row,
+  // and the prefetch past a workgroup's last item rereads its own weights):
+  // a load under a branch makes the compiler wait for every load in flight.
+  Unit<QBITS, UNIT> uw[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) load_unit(uw[i], c_wc, c_wsc, c_rows, H, min(c_row, c_rows - 1), i * 4 + g);
+  // all T tokens into LDS (fp16, permuted 16-groups)
+  {
+    const XT* x = static_cast<const XT*>(a.x);
+    const int chunks = H / 16, items = T * chunks;
+    constexpr int NB = sizeof(XT) == 4 ? 2 : 4;
+    for (int base = 0; base < items; base += NB * kThreads) {
+      Raw16<XT> raw[NB];
+#pragma unroll
+      for (int k2 = 0; k2 < NB; ++k2) {
+        const int it = min(base + k2 * kThreads + int(threadIdx.x), items - 1);
+        const int r = it / chunks, gg = it - r * chunks;
+        load_raw16(x + int64_t(r) * H + gg * 16, raw[k2]);
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < NB; ++k2) {
+        const int it = base + k2 * kThreads + int(threadIdx.x);
+        if (it < items) {
+          const int r = it / chunks, gg = it - r * chunks;
+          half8 lo, hi;
+          cvt_raw16(raw[k2], lo, hi);
+          half8* dst = reinterpret_cast<half8*>(xs + r * ldsw + gg * 16);
+          dst[0] = lo;
+          dst[1] = hi;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // Nothing is in flight here (the staging waited for every load); saying so
+  // keeps the compiler from assuming a pending staging load at the loop head,
+  // where it would otherwise wait for all loads in flight every item.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  for (int it = it0; it < it1; ++it) {
+    const bool has_next = it + 1 < it1;
+    const int4 si_next = slots[min(it + 1, it1 - 1) / n_rb];  // requested now, read at round rounds - D
+    const bool shared = si_cur.x < 0;
+    const int mnow = si_cur.z;
+    // this lane's MFMA row: the slot's min(n, mnow - 1)-th token
+    // (slot tables for at most kGemvMaxM tokens always carry the mask)
+    int tok = 0;
+    const uint32_t mask = uint32_t(si_cur.w);
+    for (int bit = 0, c = 0; bit < kGemvMaxM; ++bit)
+      if ((mask >> bit) & 1u) {
+        if (c <= n) tok = bit;
+        ++c;
+      }
+    const f16* xrow = xs + tok * ldsw;
+    float4v acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = float4v{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* n_wc = c_wc;
+    const uint16_t* n_wsc = c_wsc;
+    int n_rows = c_rows, n_row = c_row;
+    bool n_on = false;
+    for (int r0 = 0; r0 < rounds; r0 += D) {
+      const bool last_group = r0 + D >= rounds;
+      if (last_group && has_next) make(it + 1, si_next, n_wc, n_wsc, n_rows, n_row, n_on);
+      // the loads of this group: this item's rounds r0 + D .., or the next item's first D
+      const uint8_t* l_wc = last_group ? n_wc : c_wc;
+      const uint16_t* l_wsc = last_group ? n_wsc : c_wsc;
+      const int l_rows = last_group ? n_rows : c_rows;
+      const int l_row = min(last_group ? n_row : c_row, l_rows - 1);
+      const int l_r0 = last_group ? 0 : r0 + D;
+      // Round r is dequantised from ring slot i, then the slot is reloaded
+      // (reloading before the use would need a copy of the slot, and the
+      // copies at the loop edge would wait for the loads just issued).
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        const int r = r0 + i;
+        if (c_on) {
+          const int u = r * 4 + g;
+#pragma unroll
+          for (int d = 0; d < UNIT / 16; ++d) {
+            half8 wlo, whi;
+            dq_unit_word(uw[i], d, wlo, whi);
+            const half8* ap = reinterpret_cast<const half8*>(xrow + u * UNIT + 16 * d);
+            acc[i & 3] = mfma16(ap[0], wlo, acc[i & 3]);
+            acc[i & 3] = mfma16(ap[1], whi, acc[i & 3]);
+          }
+        }
+        load_unit(uw[i], l_wc, l_wsc, l_rows, H, l_row, (l_r0 + i) * 4 + g);
+      }
+    }
+    if (c_on) {
+      float4v sum = acc[0];
+#pragma unroll
+      for (int c = 1; c < 4; ++c) sum += acc[c];
+      if (mat == 1) up_x[wr][lane] = sum;
+      acc[0] = sum;
+    }
+    __syncthreads();  // the up sums are in LDS
+    if (c_on && mat == 0) {
+      const float4v su = up_x[wr][lane];
+      f16* hout = shared ? a.h_shared : a.h_routed;
+      const int hw = shared ? a.Is : a.I;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 4 * g + j;
+        if (m < mnow) {
+          const float hv = silu_f(acc[0][j]) * su[j];
+          const int64_t hr = shared ? int64_t(m) : int64_t(si_cur.y + m);
+          hout[hr * hw + hcol(c_row)] = f16(hv);
+        }
+      }
+    }
+    __syncthreads();  // up_x is free for the next item
+    c_wc = n_wc;
+    c_wsc = n_wsc;
+    c_rows = n_rows;
+    c_row = n_row;
+    c_on = n_on;
+    si_cur = si_next;
+  }
+}
+
 template <int QBITS, int UNIT, int NW>
 __global__ __launch_bounds__(64 * NW) void gemv_down_tp_kernel(FfnArgs a, int ldsw) {
   extern __shared__ __attribute__((aligned(16))) f16 hs[];
@@ -864,11 +1058,23 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
 #undef GU
     } else {
       const size_t lds = size_t(mrows) * (a.H + 8) * sizeof(f16);
-      const dim3 grid(unsigned((max_rows + 16 * NW - 1) / (16 * NW)), unsigned(slots));
+      const bool pers = MOE_GEMV_PERS && a.T <= kGemvMaxM && u64 && a.H % 1024 == 0 &&
+                        (!a.has_shared || a.Is == a.I);
+      if (pers) {
+        const int n_rb = (a.I + 63) / 64;
+        const int G = int(std::min<int64_t>(kPersGrid, int64_t(slots) * n_rb));
+        const size_t lds_p = size_t(a.T) * (a.H + 8) * sizeof(f16);
+        if (a.x_bf16)
+          gemv_gateup_pers_kernel<QBITS, 64, uint16_t><<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header);
+        else
+          gemv_gateup_pers_kernel<QBITS, 64, float><<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header);
+      } else {
+        const dim3 grid(unsigned((max_rows + 16 * NW - 1) / (16 * NW)), unsigned(slots));
 #define GU(U_, X_) gemv_gateup_tp_kernel<QBITS, U_, X_, NW><<<grid, 128 * NW, lds, stream>>>(a)
-      if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
-      else { if (u64) GU(64, float); else GU(32, float); }
+        if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+        else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
+      }
     }
   }
   if (phases & kPhaseDown) {

@@ -60,15 +60,17 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts,
                           int32_t* sorted_pair, int32_t* pair_pos, int32_t* header, int32_t* chunk_hist,
                           hipStream_t stream);
 // Builds the slot table (and, when tile_bm > 0, the grouped-GEMM tile list)
-// from offsets, for the standalone expert FFN.
+// from offsets, for the standalone expert FFN.  With sorted_pair given and
+// T <= kGemvMaxM the slots carry their token masks (else mask 0); the
+// persistent gate/up kernel relies on them.
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm,
                        int32_t* header, int4* slots, int32_t* tile_expert, int32_t* tile_m0,
-                       hipStream_t stream);
+                       const int32_t* sorted_pair, int k, hipStream_t stream);
 // Decode-layer selection on one workgroup (T <= 16): top-k + softmax weights,
 // permutation and the slot table (int4 {expert or -1 for shared, first sorted
 // position, token count, token mask: bit t set when token t uses the slot};
-// empty slots have count 0).  Slot tables built by launch_plan carry mask 0
-// (tokens then come from sorted_pair).
+// empty slots have count 0).  Slot tables built by launch_plan carry the
+// mask for T <= kGemvMaxM (0 otherwise: tokens then come from sorted_pair).
 hipError_t launch_select_small(const float* logits, int T, int E, int k, int has_shared, int32_t* idx, float* w,
                                int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                                int32_t* header, int4* slots, hipStream_t stream);
