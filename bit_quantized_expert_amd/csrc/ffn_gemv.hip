@@ -601,7 +601,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
 #ifndef MOE_GEMV_PERS
 #define MOE_GEMV_PERS 1
 #endif
-constexpr int kPersGrid = 512;  // persistent gate/up workgroups (two per CU)
+constexpr int kPersGrid = 512;       // persistent gate/up workgroups (two per CU)
+constexpr int kPersGridDown = 1024;  // persistent down workgroups (four per CU)
 // NW row blocks of 16 per workgroup; waves 0..NW-1 take the gate rows of
 // block wv, waves NW..2NW-1 the up rows (half the dequantisation per wave);
 // the up sums reach the gate waves through LDS for the SwiGLU.
@@ -1039,6 +1040,140 @@ __global__ __launch_bounds__(64 * NW) void gemv_down_tp_kernel(FfnArgs a, int ld
 }
 
 // ---------------------------------------------------------------------------
+// Persistent down projection for 2..kGemvMaxM tokens: the arithmetic of
+// gemv_down_tp_kernel (16 output rows per wave, four round classes), with a
+// fixed grid walking contiguous runs of (slot, 64-row block) items.  A slot
+// has R = ceil(K / 256) rounds (the whole reduction axis in one ring), so
+// while an item is computed the ring is refilled with the next item's
+// weights (slot entries two items ahead are scalar loads).  The h rows of a
+// slot are staged in LDS when the slot changes.  Requires Is = I (or no
+// shared expert), I % 64 == 0 and ceil(I / 256) == R.
+// ---------------------------------------------------------------------------
+template <int QBITS, int R>
+__global__ __launch_bounds__(256) void gemv_down_pers_kernel(FfnArgs a, int ldsw, int n_rb, int G,
+                                                             const int4* __restrict__ slots,
+                                                             const int32_t* __restrict__ header) {
+  constexpr int NW = 4, UNIT = 64, kThreads = 256;
+  extern __shared__ __attribute__((aligned(16))) f16 hs[];  // [<= kGemvMaxM][ldsw]
+  const int H = a.H, K = a.I;
+  const int n_units = K / UNIT;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int n = lane & 15, g = lane >> 4;
+  const int n_items = header[kHdrValid] * n_rb;
+  const int q = n_items / G, rem = n_items - q * G, b = blockIdx.x;
+  const int it0 = b * q + min(b, rem), it1 = it0 + q + (b < rem ? 1 : 0);
+  if (it0 >= it1) return;
+
+  // item -> this wave's weight rows (loads always go to a real row and unit)
+  auto src = [&](int it, int4 si, const uint8_t*& dc, const uint16_t*& dsc, int& row, bool& on) {
+    const bool shared = si.x < 0;
+    const QMat Dm = shared ? a.sd : a.rd;
+    const int64_t ex = shared ? 0 : si.x;
+    dc = Dm.codes + ex * Dm.code_stride;
+    dsc = Dm.scales + ex * Dm.scale_stride;
+    const int rb = (it % n_rb) * 16 * NW + wv * 16;
+    on = si.z > 0 && rb < H && !(shared && a.shared_out == nullptr);
+    row = min(rb + n, H - 1);
+  };
+  auto load_ring = [&](Unit<QBITS, UNIT> (&ud)[R], const uint8_t* dc, const uint16_t* dsc, int row) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int u = i * 4 + g;
+      load_unit(ud[i], dc, dsc, H, K, row, u < n_units ? u : 0);
+    }
+  };
+
+  int4 si_c = slots[it0 / n_rb];
+  int4 si_n = slots[min(it0 + 1, it1 - 1) / n_rb];
+  const uint8_t* c_dc;
+  const uint16_t* c_dsc;
+  int c_row;
+  bool c_on;
+  src(it0, si_c, c_dc, c_dsc, c_row, c_on);
+  Unit<QBITS, UNIT> ud[R];
+  load_ring(ud, c_dc, c_dsc, c_row);
+  int staged = -1;  // slot index whose h rows are in LDS
+  __builtin_amdgcn_s_waitcnt(0);  // (see the persistent gate/up kernel)
+
+  for (int it = it0; it < it1; ++it) {
+    const int4 si_nn = slots[min(it + 2, it1 - 1) / n_rb];  // two items ahead
+    const int slot = it / n_rb;
+    const bool shared = si_c.x < 0;
+    const int mnow = si_c.z;
+    if (slot != staged) {  // the slot's h rows into LDS (uniform over the workgroup)
+      __syncthreads();
+      const f16* hin = shared ? a.h_shared : a.h_routed;
+      constexpr int NB = 4;
+      const int chunks = K / 8, items = mnow * chunks;
+      for (int base = 0; base < items; base += NB * kThreads) {
+        half8 v[NB];
+#pragma unroll
+        for (int k2 = 0; k2 < NB; ++k2) {
+          const int ii = min(base + k2 * kThreads + int(threadIdx.x), items - 1);
+          const int r = ii / chunks, c8 = ii - r * chunks;
+          const int64_t hr = shared ? int64_t(r) : int64_t(si_c.y + r);
+          v[k2] = *reinterpret_cast<const half8*>(hin + hr * K + c8 * 8);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < NB; ++k2) {
+          const int ii = base + k2 * kThreads + int(threadIdx.x);
+          if (ii < items) {
+            const int r = ii / chunks, c8 = ii - r * chunks;
+            *reinterpret_cast<half8*>(hs + r * ldsw + c8 * 8) = v[k2];
+          }
+        }
+      }
+      __syncthreads();
+      staged = slot;
+    }
+    // the next item's weight source (its slot entry arrived during the previous item)
+    const uint8_t* n_dc;
+    const uint16_t* n_dsc;
+    int n_row;
+    bool n_on;
+    src(min(it + 1, it1 - 1), si_n, n_dc, n_dsc, n_row, n_on);
+    const f16* hrow = hs + min(n, mnow - 1) * ldsw;  // finite, never stored past mnow
+    float4v acc[4] = {};
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int u = i * 4 + g;
+      const bool valid = u < n_units;
+      if (c_on) {
+        const int ua = valid ? u : 0;
+        if (!valid) zero_unit(ud[i]);  // units past K: the zero unit of the other down kernels
+#pragma unroll
+        for (int d = 0; d < UNIT / 16; ++d) {
+          half8 blo, bhi;
+          dq_unit_word(ud[i], d, blo, bhi);
+          const half8* ap = reinterpret_cast<const half8*>(hrow + ua * UNIT + 16 * d);
+          acc[i & 3] = mfma16(ap[0], blo, acc[i & 3]);
+          acc[i & 3] = mfma16(ap[1], bhi, acc[i & 3]);
+        }
+      }
+      load_unit(ud[i], n_dc, n_dsc, H, K, n_row, valid ? u : 0);  // the next item's round i
+    }
+    if (c_on) {
+      const float4v y4 = ((acc[0] + acc[1]) + acc[2]) + acc[3];
+      float* yout = shared ? a.shared_out : a.y_sorted;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = 4 * g + j;
+        if (m < mnow) {
+          const int64_t yr = shared ? int64_t(m) : int64_t(si_c.y + m);
+          yout[yr * H + c_row] = y4[j];
+        }
+      }
+    }
+    si_c = si_n;
+    si_n = si_nn;
+    c_dc = n_dc;
+    c_dsc = n_dsc;
+    c_row = n_row;
+    c_on = n_on;
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int QBITS>
 static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases) {
   constexpr int NW = MOE_TP_NW;
@@ -1088,9 +1223,23 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
       const int kmax = std::max(a.I, a.has_shared ? a.Is : 0);
       const int ldsw = kmax + 8;
       const size_t lds = size_t(mrows) * ldsw * sizeof(f16);
-      const dim3 grid(unsigned((a.H + 16 * NW - 1) / (16 * NW)), unsigned(slots));
-      if (u64) gemv_down_tp_kernel<QBITS, 64, NW><<<grid, 64 * NW, lds, stream>>>(a, ldsw);
-      else gemv_down_tp_kernel<QBITS, 32, NW><<<grid, 64 * NW, lds, stream>>>(a, ldsw);
+      const int rounds = (a.I / 64 + 3) / 4;
+      const bool pers = MOE_GEMV_PERS && a.T <= kGemvMaxM && a.I % 64 == 0 && rounds <= 4 &&
+                        (!a.has_shared || a.Is == a.I);
+      if (pers) {
+        const int n_rb = (a.H + 63) / 64;
+        const int G = int(std::min<int64_t>(kPersGridDown, int64_t(slots) * n_rb));
+#define DP(R_) gemv_down_pers_kernel<QBITS, R_><<<G, 256, lds, stream>>>(a, ldsw, n_rb, G, a.slots, a.header)
+        if (rounds == 1) DP(1);
+        else if (rounds == 2) DP(2);
+        else if (rounds == 3) DP(3);
+        else DP(4);
+#undef DP
+      } else {
+        const dim3 grid(unsigned((a.H + 16 * NW - 1) / (16 * NW)), unsigned(slots));
+        if (u64) gemv_down_tp_kernel<QBITS, 64, NW><<<grid, 64 * NW, lds, stream>>>(a, ldsw);
+        else gemv_down_tp_kernel<QBITS, 32, NW><<<grid, 64 * NW, lds, stream>>>(a, ldsw);
+      }
     }
   }
   return hipGetLastError();
