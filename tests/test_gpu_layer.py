@@ -60,6 +60,15 @@ RAGGED = [
     ("r3", 128, 160, 12, 4, 0, 2, 21, torch.bfloat16),
     ("r4", 64, 32, 8, 2, 32, 3, 4, torch.float32),
     ("r5", 256, 192, 33, 8, 96, 3, 17, torch.bfloat16),
+    # 2..16 tokens touching few experts (reduction split over the waves): 32-weight units, 3-bit
+    # with fp32 tokens, hidden above 2048 (several load batches per class)
+    ("k1", 96, 96, 40, 2, 64, 2, 5, torch.bfloat16),
+    ("k2", 256, 192, 64, 3, 96, 3, 9, torch.float32),
+    ("k3", 2304, 96, 64, 2, 96, 2, 12, torch.bfloat16),
+    # 2..16 tokens touching most experts (persistent gate/up and down kernels)
+    ("p1", 1024, 128, 8, 4, 128, 2, 16, torch.bfloat16),
+    ("p2", 2048, 704, 16, 8, 704, 3, 12, torch.float32),
+    ("p3", 1024, 256, 4, 2, 0, 2, 3, torch.bfloat16),
     # single-token layers (the fused one-token path), 64- and 32-weight units
     ("s1", 96, 96, 5, 3, 64, 2, 1, torch.bfloat16),
     ("s2", 64, 32, 8, 2, 32, 3, 1, torch.float32),
