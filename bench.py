@@ -184,6 +184,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gateup_decode1_traffic.txt")
 TRAFFIC_SOURCES = ("ffn_gemv.hip", "common.h", "launch.h")
 
 
+def source_digest() -> str:
+    """SHA-256 of the kernel sources the traffic counters depend on, with
+    // comments and blank lines removed (a comment edit does not change the
+    code the counters measured)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "bit_quantized_expert_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch of the decode gate/up kernel from the committed
     FETCH_SIZE / WRITE_SIZE counter runs (scaled by the copy-kernel
@@ -196,11 +212,7 @@ def measured_traffic():
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-        h = hashlib.sha256()
-        for f in TRAFFIC_SOURCES:
-            with open(os.path.join(ROOT, "bit_quantized_expert_amd", "csrc", f), "rb") as fh:
-                h.update(fh.read())
-        if h.hexdigest() != kv["source_sha256"]:
+        if source_digest() != kv["source_sha256"]:
             return None
         return (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) + float(kv["write_kib"]) * float(kv["write_scale"])) * 1024
     except (OSError, KeyError, ValueError):

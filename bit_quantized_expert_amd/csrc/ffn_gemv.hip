@@ -158,17 +158,18 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 
 // ---------------------------------------------------------------------------
 // Single-token gate/up + SwiGLU.  grid = (ceil(max_rows / 16), slots),
-// block = 256.
+// block = 512.
 //
 // Unit u of a row (64 or 32 weights) is read in round r' = u / 4 by lane
-// group g = u % 4.  Rounds fall in four classes c = r' % 4: wave c of the
-// workgroup takes the rounds of class c for the workgroup's 16 rows (the
-// reduction axis split four ways: four times more waves for one token), and
-// the partial sums meet in LDS as ((c0 + c1) + c2) + c3 -- the order of the
-// multi-token kernels, so a token's result does not depend on the batch.
-// The activations (always token 0) go straight from global memory into the
-// MFMA operands: no LDS staging, and they are requested before anything
-// else.  h is written in the permuted column order of the down projection.
+// group g = u % 4.  Rounds fall in four classes c = r' % 4: waves 0..3 take
+// the rounds of classes 0..3 of the workgroup's 16 gate rows, waves 4..7 the
+// same for the up rows (the reduction axis split four ways and the two
+// matrices apart: eight waves for one token), and the partial sums meet in
+// LDS as ((c0 + c1) + c2) + c3 -- the order of the multi-token kernels, so a
+// token's result does not depend on the batch.  The token is requested
+// before anything else and converted to fp16 once per workgroup into LDS;
+// every lane reads it as its MFMA row (only row 0 of the result is used).
+// h is written in the permuted column order of the down projection.
 //
 // Slot source.  With `sl.logits` null, slot s of the slot table (standalone
 // expert FFN: h row = the pair's sorted position).  With `sl.logits` set (the
