@@ -773,9 +773,10 @@ __global__ __launch_bounds__(128 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(F
 // Persistent gate/up for 2..kGemvMaxM tokens: the same per-row arithmetic as
 // gemv_gateup_tp_kernel (8 waves, 64 rows per work item, gate and up waves,
 // four round classes), but a fixed grid of G workgroups each walks a
-// contiguous run of the (slot, 64-row block) items.  All T tokens are staged
-// in LDS once per workgroup (a slot's MFMA rows pick its tokens through the
-// token mask), and the weight pipeline runs on across items: the next item's
+// contiguous run of the (slot, 64-row block) items.  The tokens of the
+// workgroup's slots are staged in LDS once (rows indexed by token; a slot's
+// MFMA rows pick its tokens through the token mask), and the weight
+// pipeline runs on across items: the next item's
 // slot entry is requested when an item starts and its first D rounds of
 // weights while the current item's last D rounds are computed.  So the
 // first-load latency is paid once per workgroup instead of once per item.
@@ -826,29 +827,35 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
   Unit<QBITS, UNIT> uw[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) load_unit(uw[i], c_wc, c_wsc, c_rows, H, min(c_row, c_rows - 1), i * 4 + g);
-  // all T tokens into LDS (fp16, permuted 16-groups)
+  // the tokens of this workgroup's slots into LDS (fp16, permuted 16-groups;
+  // row = token id): the union of the slots' token masks
   {
+    uint32_t umask = 0u;
+    for (int sl = it0 / n_rb; sl <= (it1 - 1) / n_rb; ++sl) umask |= uint32_t(slots[sl].w);
     const XT* x = static_cast<const XT*>(a.x);
-    const int chunks = H / 16, items = T * chunks;
+    const int chunks = H / 16, items = __builtin_popcount(umask) * chunks;
     constexpr int NB = sizeof(XT) == 4 ? 2 : 4;
     for (int base = 0; base < items; base += NB * kThreads) {
       Raw16<XT> raw[NB];
+      int dst[NB];
 #pragma unroll
       for (int k2 = 0; k2 < NB; ++k2) {
         const int it = min(base + k2 * kThreads + int(threadIdx.x), items - 1);
         const int r = it / chunks, gg = it - r * chunks;
-        load_raw16(x + int64_t(r) * H + gg * 16, raw[k2]);
+        uint32_t mm = umask;  // token of rank r: the r-th set bit
+        for (int k3 = 0; k3 < r; ++k3) mm &= mm - 1u;
+        const int tok = __builtin_ctz(mm);
+        load_raw16(x + int64_t(tok) * H + gg * 16, raw[k2]);
+        dst[k2] = tok * ldsw + gg * 16;
       }
 #pragma unroll
       for (int k2 = 0; k2 < NB; ++k2) {
-        const int it = base + k2 * kThreads + int(threadIdx.x);
-        if (it < items) {
-          const int r = it / chunks, gg = it - r * chunks;
+        if (base + k2 * kThreads + int(threadIdx.x) < items) {
           half8 lo, hi;
           cvt_raw16(raw[k2], lo, hi);
-          half8* dst = reinterpret_cast<half8*>(xs + r * ldsw + gg * 16);
-          dst[0] = lo;
-          dst[1] = hi;
+          half8* d = reinterpret_cast<half8*>(xs + dst[k2]);
+          d[0] = lo;
+          d[1] = hi;
         }
       }
     }
