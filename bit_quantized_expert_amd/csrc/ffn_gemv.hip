@@ -184,7 +184,9 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 constexpr int k1tokWaves = 8;  // waves per workgroup of the single-token gate/up kernel
 
 template <int QBITS, int UNIT, typename XT>
-__global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnArgs a, Decode1Sel sl) {
+__global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnArgs a, Decode1Sel sl,
+                                                                           const int4* __restrict__ slots) {
+  // slots = a.slots, read-only here: the slot entry is a scalar load
   extern __shared__ __attribute__((aligned(16))) f16 xs1[];  // the token, fp16, permuted 16-groups
   __shared__ float red[4][2][16];
   constexpr int RB = 2;  // rounds per wave per load batch (rounds c and c + 4)
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnAr
       rank_here = blockIdx.x == 0 && j == 0 && wv == 0;
     }
   } else {
-    const int4 si = a.slots[j];
+    const int4 si = slots[j];
     if (si.z == 0) return;
     shared = si.x < 0;
     if (blockIdx.x * 16 >= (shared ? a.Is : a.I)) return;
@@ -245,56 +247,25 @@ __global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnAr
 
   Unit<QBITS, UNIT> uw[RB];
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int b0 = 0; b0 * 4 < rounds; b0 += RB) {
+  // batch b0 (rounds (b0 + i) * 4 + ks): unconditional loads from a clamped
+  // unit (a load under a branch costs a wait for every load in flight)
+  auto issue = [&](int b0) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int rp = (b0 + i) * 4 + ks, u = rp * 4 + g;
-      if (rp < rounds && u < n_units) load_unit(uw[i], wc, wsc, rows, H, row, u);
-      else zero_unit(uw[i]);
+      load_unit(uw[i], wc, wsc, rows, H, row, rp < rounds && u < n_units ? u : 0);
     }
-    if (b0 == 0) {
-      if (rank_here) {
-        // ranks, weights and the slot maps, while this wave's weight loads are in flight
-        float my_val;
-        int my_idx, my_slot;
-        wave_rank<8>(K, sel, a.k, my_val, my_idx, my_slot);
-        const float my_w = wave_topk_weight(my_val, a.k);
-        if (lane < a.k) {
-          sl.idx[lane] = my_idx;
-          sl.w[lane] = my_w;
-          sl.slot_of_rank[lane] = my_slot;
-          sl.slot_expert[my_slot] = my_idx;
-        }
-        if (lane == 0) sl.header[kHdrError] = 0;
-      }
-      // the token into LDS (first groups from the early loads, any others now)
-      {
-        half8 lo, hi;
-        cvt_raw16(xr, lo, hi);
-        if (int(threadIdx.x) < ngrp) {
-          half8* dst = reinterpret_cast<half8*>(xs1 + threadIdx.x * 16);
-          dst[0] = lo;
-          dst[1] = hi;
-        }
-        for (int gi = NT + int(threadIdx.x); gi < ngrp; gi += NT) {
-          Raw16<XT> r2;
-          load_raw16(xg + gi * 16, r2);
-          cvt_raw16(r2, lo, hi);
-          half8* dst = reinterpret_cast<half8*>(xs1 + gi * 16);
-          dst[0] = lo;
-          dst[1] = hi;
-        }
-      }
-      __syncthreads();
-    }
-    // every lane reads the token's fragment (MFMA rows 1..15 repeat row 0;
-    // only row 0 of the result is used)
+  };
+  // every lane reads the token's fragment (MFMA rows 1..15 repeat row 0;
+  // only row 0 of the result is used)
+  auto compute = [&](int b0) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int rp = (b0 + i) * 4 + ks;
       if (rp >= rounds) break;
       const int u = rp * 4 + g;
-      const int ua = u < n_units ? u : 0;  // units past K have zero weights
+      const int ua = u < n_units ? u : 0;
+      if (u >= n_units) zero_unit(uw[i]);  // units past K: zero weights
 #pragma unroll
       for (int d = 0; d < UNIT / 16; ++d) {
         const half8* ap = reinterpret_cast<const half8*>(xs1 + ua * UNIT + 16 * d);
@@ -304,6 +275,46 @@ __global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnAr
         acc = mfma16(ap[1], whi, acc);
       }
     }
+  };
+  issue(0);
+  __builtin_amdgcn_sched_barrier(0);  // the first weight loads go out before anything waits on the token loads
+  if (rank_here) {
+    // ranks, weights and the slot maps, while this wave's weight loads are in flight
+    float my_val;
+    int my_idx, my_slot;
+    wave_rank<8>(K, sel, a.k, my_val, my_idx, my_slot);
+    const float my_w = wave_topk_weight(my_val, a.k);
+    if (lane < a.k) {
+      sl.idx[lane] = my_idx;
+      sl.w[lane] = my_w;
+      sl.slot_of_rank[lane] = my_slot;
+      sl.slot_expert[my_slot] = my_idx;
+    }
+    if (lane == 0) sl.header[kHdrError] = 0;
+  }
+  // the token into LDS (first groups from the early loads, any others now)
+  {
+    half8 lo, hi;
+    cvt_raw16(xr, lo, hi);
+    if (int(threadIdx.x) < ngrp) {
+      half8* dst = reinterpret_cast<half8*>(xs1 + threadIdx.x * 16);
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+    for (int gi = NT + int(threadIdx.x); gi < ngrp; gi += NT) {
+      Raw16<XT> r2;
+      load_raw16(xg + gi * 16, r2);
+      cvt_raw16(r2, lo, hi);
+      half8* dst = reinterpret_cast<half8*>(xs1 + gi * 16);
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+  }
+  __syncthreads();
+  compute(0);
+  for (int b0 = RB; b0 * 4 < rounds; b0 += RB) {  // hidden > 2048: later batches
+    issue(b0);
+    compute(b0);
   }
   // row 0 of the result: lanes 0..15, element 0; the class partials meet in LDS
   if (wv > 0 && lane < 16) red[ks][mat][n] = acc[0];
@@ -1195,7 +1206,8 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
     if (one) {
       const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
 #define GU(U_, X_) \
-  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a, Decode1Sel{})
+  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a, Decode1Sel{}, \
+                                                                                               a.slots)
       if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
       else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
@@ -1266,7 +1278,8 @@ static hipError_t launch_decode1_q(const FfnArgs& a, const Decode1Sel& sel, floa
   {
     const bool u64 = a.H % 64 == 0;
     const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
-#define GU(U_, X_) gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a, sel)
+#define GU(U_, X_) \
+  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a, sel, a.slots)
     if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
     else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
