@@ -422,24 +422,24 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
   load_h(0);
 
   Unit<QBITS, UNIT> ud[RB];
-  DownSlot sl{};
-  if (wv < n_slots) {
-    sl = down_slot<UNIT>(a, slot_expert, wv);
+  // the wave's first slot (a wave past the slots loads the last slot's
+  // weights and never uses them); unconditional loads from clamped units,
+  // units past K are zeroed at use (a load under a branch costs a wait for
+  // every load in flight)
+  DownSlot sl = down_slot<UNIT>(a, slot_expert, min(wv, n_slots - 1));
+  auto issue = [&](int r0) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int u = i * 4 + g;
-      if (i < sl.rounds && u < sl.n_units) load_unit(ud[i], sl.dc, sl.ds, H, sl.K, row, u);
-      else zero_unit(ud[i]);
+      const int u = (r0 + i) * 4 + g;
+      load_unit(ud[i], sl.dc, sl.ds, H, sl.K, row, r0 + i < sl.rounds && u < sl.n_units ? u : 0);
     }
-  }
+  };
+  issue(0);
+  __builtin_amdgcn_sched_barrier(0);
   store_h(0);
   for (int base = HB * nthreads; base < items; base += HB * nthreads) {  // more than one batch
     load_h(base);
     store_h(base);
-  }
-  if (threadIdx.x < a.k) {
-    s_w[threadIdx.x] = w_r;
-    s_slot[threadIdx.x] = slot_r;
   }
   __syncthreads();
 
@@ -447,29 +447,18 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
   for (int s = wv; s < n_slots; s += nw) {
     if (s != wv) {
       sl = down_slot<UNIT>(a, slot_expert, s);
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int u = i * 4 + g;
-        if (i < sl.rounds && u < sl.n_units) load_unit(ud[i], sl.dc, sl.ds, H, sl.K, row, u);
-        else zero_unit(ud[i]);
-      }
+      issue(0);
     }
     const f16* hrow = hs + s * ldh;
     float4v acc[4] = {};  // one accumulator per round class (round % 4), as in every down kernel
     static_assert(RB % 4 == 0, "a load batch holds whole round classes");
     for (int r0 = 0; r0 < sl.rounds; r0 += RB) {
-      if (r0 > 0) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          const int u = (r0 + i) * 4 + g;
-          if (r0 + i < sl.rounds && u < sl.n_units) load_unit(ud[i], sl.dc, sl.ds, H, sl.K, row, u);
-          else zero_unit(ud[i]);
-        }
-      }
+      if (r0 > 0) issue(r0);
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         if (r0 + i >= sl.rounds) break;
         const int u = (r0 + i) * 4 + g;
+        if (u >= sl.n_units) zero_unit(ud[i]);
         const bool on = a_on && u < sl.n_units;
 #pragma unroll
         for (int d = 0; d < UNIT / 16; ++d) {
@@ -486,6 +475,10 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
       }
     }
     if (lane < 16) ys[s][n] = ((acc[0][0] + acc[1][0]) + acc[2][0]) + acc[3][0];
+  }
+  if (threadIdx.x < a.k) {  // (stored here: an earlier store would wait on the loads behind it)
+    s_w[threadIdx.x] = w_r;
+    s_slot[threadIdx.x] = slot_r;
   }
   __syncthreads();
   if (threadIdx.x < 16) {
