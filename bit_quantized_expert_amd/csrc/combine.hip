@@ -35,51 +35,98 @@ __device__ __forceinline__ void rmsnorm_row(const float* __restrict__ res, int H
   }
 }
 
+// CPT float4 columns per thread per pass (all their loads in flight
+// together); with H / 4 <= 256 * CPT the row is one pass and the updated
+// residual stays in registers for the norm.  The pair slots and weights are
+// uniform loads (no LDS staging, no barrier before the row loads).
+template <int CPT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ pos,
                                                      const float* __restrict__ w, const float* __restrict__ shared,
                                                      int H, int k, float* __restrict__ out, float* __restrict__ res,
                                                      uint16_t* __restrict__ next_in) {
   __shared__ float red[4];
-  __shared__ int s_pos[kMaxTopK];
-  __shared__ float s_w[kMaxTopK];
   const int64_t t = blockIdx.x;
-  if (threadIdx.x < k) {
-    s_pos[threadIdx.x] = pos[t * k + threadIdx.x];
-    s_w[threadIdx.x] = w[t * k + threadIdx.x];
-  }
-  __syncthreads();
+  const int32_t* pt = pos + t * k;
+  const float* wt = w + t * k;
   const int H4 = H / 4;
   float ss = 0.0f;
-  for (int c = threadIdx.x; c < H4; c += 256) {
-    // every load unconditional (clamped rows) so that they are in flight together: latency, not
-    // bandwidth, bounds one token.  y has at least T rows, so row t of it stands in for a
-    // missing shared output; out-of-range pairs (p < 0) read row 0 and add 0.
-    const float4v s4 = reinterpret_cast<const float4v*>((shared ? shared : y) + t * H)[c];
-    float4v acc = shared ? s4 : float4v{0.f, 0.f, 0.f, 0.f};
+  float4v rk[CPT];  // the updated residual of a one-pass row
+  for (int c0 = 0; c0 < H4; c0 += 256 * CPT) {
+    // every load unconditional (clamped columns and rows) so that they are in flight together:
+    // latency, not bandwidth, bounds a few tokens.  y has at least T rows, so row t of it stands in
+    // for a missing shared output; out-of-range pairs (p < 0) read row 0 and add 0.
+    int cc[CPT];
+    bool on[CPT];
+    float4v acc[CPT], r[CPT];
+    const float* srow = (shared ? shared : y) + t * H;
+    const float* rrow = (res ? res : y) + t * H;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = c0 + 256 * u + int(threadIdx.x);
+      on[u] = c < H4;
+      cc[u] = on[u] ? c : 0;
+      acc[u] = reinterpret_cast<const float4v*>(srow)[cc[u]];  // zeroed below when there is no shared expert
+      r[u] = reinterpret_cast<const float4v*>(rrow)[cc[u]];    // used only with res
+    }
     for (int j0 = 0; j0 < k; j0 += 8) {
-      float4v v[8];
+      float4v v[8][CPT];
+      int pj[8];
+      float wj[8];
+      // the slots and weights first (uniform loads), then every row load
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int p = j0 + i < k ? s_pos[j0 + i] : -1;
-        const float4v l = reinterpret_cast<const float4v*>(y + int64_t(p >= 0 ? p : 0) * H)[c];
-        v[i] = p >= 0 ? l : float4v{0.f, 0.f, 0.f, 0.f};
+        const int j = min(j0 + i, k - 1);
+        pj[i] = pt[j];
+        wj[i] = wt[j];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int u = 0; u < CPT; ++u)
+          v[i][u] = reinterpret_cast<const float4v*>(y + int64_t(pj[i] >= 0 ? pj[i] : 0) * H)[cc[u]];
+      __builtin_amdgcn_sched_barrier(0);
+      if (j0 == 0 && !shared) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) acc[u] = float4v{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (j0 + i < k)  // pairs of out-of-range ids (p < 0) add 0
+        if (j0 + i < k && pj[i] >= 0)  // pairs of out-of-range ids (p < 0) add 0
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(s_w[j0 + i], v[i][q], acc[q]);
+          for (int u = 0; u < CPT; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[u][q] = __builtin_fmaf(wj[i], v[i][u][q], acc[u][q]);
     }
-    if (out) reinterpret_cast<float4v*>(out + t * H)[c] = acc;
-    if (res) {
-      float4v r = reinterpret_cast<float4v*>(res + t * H)[c];
-      r += acc;
-      reinterpret_cast<float4v*>(res + t * H)[c] = r;
-      ss += sumsq4(r);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      if (!on[u]) continue;
+      if (out) reinterpret_cast<float4v*>(out + t * H)[cc[u]] = acc[u];
+      if (res) {
+        r[u] += acc[u];
+        reinterpret_cast<float4v*>(res + t * H)[cc[u]] = r[u];
+        ss += sumsq4(r[u]);
+        rk[u] = r[u];
+      }
     }
   }
   if (!res || !next_in) return;  // uniform across the workgroup
-  rmsnorm_row(res + t * H, H, ss, red, next_in + t * H);
+  if (H4 > 256 * CPT) {
+    rmsnorm_row(res + t * H, H, ss, red, next_in + t * H);
+    return;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float denom = sqrtf((red[0] + red[1] + red[2] + red[3]) / float(H) + 1e-6f);
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = 256 * u + int(threadIdx.x);
+    if (c >= H4) continue;
+    uint16_t* dst = next_in + t * H + 4 * c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = f32_to_bf16_rne(rk[u][q] / denom);
+  }
 }
 
 __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const float* __restrict__ res, int H,
@@ -102,8 +149,8 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const 
                           const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
                           uint16_t* next_in, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  combine_kernel<<<dim3(unsigned(T)), 256, 0, stream>>>(y_sorted, pair_pos, topk_w, shared_out, H, k, out,
-                                                        residual, next_in);
+  combine_kernel<2><<<dim3(unsigned(T)), 256, 0, stream>>>(y_sorted, pair_pos, topk_w, shared_out, H, k, out,
+                                                           residual, next_in);
   return hipGetLastError();
 }
 
