@@ -24,7 +24,6 @@ __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restr
                                                            int32_t* __restrict__ pair_pos,
                                                            int32_t* __restrict__ header, int4* __restrict__ slots) {
   __shared__ int cnt[kMaxExperts];
-  __shared__ int flag[kMaxExperts];
   __shared__ uint32_t tmask[kMaxExperts];  // bit t: token t chose the expert
   __shared__ int tmp[16];
   __shared__ int s_idx[kSelMaxT * kMaxTopK];
@@ -47,7 +46,9 @@ __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restr
   }
   __syncthreads();
 
-  // ---- histogram, offsets
+  // ---- histogram; then one scan of (count | active << 16): the low half
+  // gives the offsets, the high half the slot of each active expert
+  // (counts <= 1024 and active experts <= 4096, so neither half carries)
   const int P = T * k;
   for (int p = threadIdx.x; p < P; p += 1024) {
     atomicAdd(&cnt[s_idx[p]], 1);
@@ -55,31 +56,34 @@ __global__ __launch_bounds__(1024) void select_small_kernel(const float* __restr
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 1024) {
-    counts[e] = cnt[e];
-    flag[e] = cnt[e] > 0;
+    const int c = cnt[e];
+    counts[e] = c;
+    cnt[e] = c | (c > 0 ? 1 << 16 : 0);
   }
-  const int total = block_scan_fast(cnt, E, tmp);
-  for (int e = threadIdx.x; e < E; e += 1024) offsets[e] = cnt[e];
+  __syncthreads();
+  const int packed_total = block_scan_fast(cnt, E, tmp);
+  const int total = packed_total & 0xffff, n_active = packed_total >> 16;
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    const int off = cnt[e] & 0xffff;
+    offsets[e] = off;
+    const uint32_t m = tmask[e];  // a token picks an expert at most once: count = popcount
+    if (m != 0u) slots[cnt[e] >> 16] = int4{e, off, __builtin_popcount(m), int(m)};
+  }
   if (threadIdx.x == 0) offsets[E] = total;
 
-  // ---- stable scatter (P <= 1024: one pair per thread).  A token picks an
-  // expert at most once, so the pairs of expert e before pair (t, j) are
-  // those of the earlier tokens in e's token mask.
+  // ---- stable scatter (P <= 1024: one pair per thread).  The pairs of
+  // expert e before pair (t, j) are those of the earlier tokens in e's token
+  // mask.
   if (threadIdx.x < P) {
     const int p = threadIdx.x;
     const int e = s_idx[p];
     const int t = p / k;
-    const int pos = cnt[e] + __builtin_popcount(tmask[e] & ((1u << t) - 1u));
+    const int pos = (cnt[e] & 0xffff) + __builtin_popcount(tmask[e] & ((1u << t) - 1u));
     sorted_pair[pos] = p;
     pair_pos[p] = pos;
   }
 
-  // ---- slot table: active experts in ascending id order, then the shared expert
-  const int n_active = block_scan_fast(flag, E, tmp);
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    const int c = (e + 1 < E ? cnt[e + 1] : total) - cnt[e];
-    if (c > 0) slots[flag[e]] = int4{e, cnt[e], c, int(tmask[e])};
-  }
+  // ---- slot table tail: the shared expert after the active ones
   const int n_valid = n_active + (has_shared ? 1 : 0);
   if (threadIdx.x == 0) {
     if (has_shared) slots[n_active] = int4{-1, 0, T, int((1u << T) - 1u)};
