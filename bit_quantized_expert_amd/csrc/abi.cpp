@@ -237,7 +237,7 @@ hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, co
                   const int32_t* offsets, const int32_t* sorted_pair, float* y_sorted, float* shared_out,
                   moe_algo algo, void* ws, const WsLayout& W, hipStream_t st, int flags = 0) {
   moe::FfnArgs a = ffn_args(x, xd, T, L, s, offsets, sorted_pair, y_sorted, shared_out, ws, W);
-  const int tile_bm = algo == MOE_ALGO_GROUPED ? moe::kGroupedBM : 0;
+  const int tile_bm = algo == MOE_ALGO_GROUPED ? moe::grouped_tile_rows(T, s->top_k, s->n_experts) : 0;
   if (!(flags & MOE_FFN_REUSE_PLAN)) {
     hipError_t e = moe::launch_plan(offsets, s->n_experts, T, a.has_shared, tile_bm, at<int32_t>(ws, W.header),
                                     at<int4>(ws, W.slots), at<int32_t>(ws, W.tile_expert),
@@ -246,10 +246,10 @@ hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, co
   }
   const int phases = (flags & MOE_FFN_SKIP_GATEUP ? 0 : moe::kPhaseGateUp) | (flags & MOE_FFN_SKIP_DOWN ? 0 : moe::kPhaseDown);
   if (algo == MOE_ALGO_GROUPED) {
-    const int64_t P = T * s->top_k, BM = moe::kGroupedBM;
+    const int64_t P = T * s->top_k, BM = tile_bm;
     const int64_t max_tiles = (P + BM - 1) / BM + std::min<int64_t>(s->n_experts, P) +
                               (a.has_shared ? (T + BM - 1) / BM : 0);
-    return moe::launch_ffn_grouped(a, max_tiles, st, phases);
+    return moe::launch_ffn_grouped(a, max_tiles, tile_bm, st, phases);
   }
   return moe::launch_ffn_gemv(a, st, phases);
 }

@@ -79,9 +79,11 @@ __device__ __forceinline__ void cvt_araw(const ARaw<AT>& r, int i, half8& lo, ha
 }
 
 // ---------------------------------------------------------------------------
-// The grouped GEMM.  A workgroup owns BM = 128 rows x 8 waves; each wave a
-// 128 x 64 block (4 x 2 MFMA tiles of 32 x 32),
-// so an A fragment read from LDS feeds two MFMAs and a B fragment four.  The
+// The grouped GEMM.  A workgroup owns BM rows (128, or 96 when experts hold
+// few rows each: fewer padding rows per tile) x 8 waves; each wave a
+// BM x 64 block (BM/32 x 2 MFMA tiles of 32 x 32), so an A fragment read
+// from LDS feeds two MFMAs and a B fragment BM/32.  Every output element
+// goes through the same MFMA sequence for either BM.  The
 // weights never pass through LDS: each wave loads and dequantises its own
 // 64 columns straight into MFMA operands (lane (n, h) of a 32-column set
 // takes 16 code bytes = words 4h .. 4h+3 of the row's 128-weight step; MFMA
@@ -92,8 +94,7 @@ __device__ __forceinline__ void cvt_araw(const ARaw<AT>& r, int i, half8& lo, ha
 //   gate/up: wave w = gate rows nt*256 + 32w .. +32 and the same up rows;
 //   down   : wave w = output columns nt*512 + 64w .. +64.
 // ---------------------------------------------------------------------------
-constexpr int kBM2 = 128, kBK2 = 128, kLDA2 = kBK2 + 8;  // A row pitch in halves
-static_assert(kBM2 == kGroupedBM, "the plan's tiles have the GEMM's row count");
+constexpr int kBK2 = 128, kLDA2 = kBK2 + 8;  // A row pitch in halves
 
 template <int QBITS>
 struct BRaw2 {
@@ -164,12 +165,15 @@ __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, half8& lo, h
   }
 }
 
-template <int QBITS, typename AT, bool GATEUP, int NWV, int PD, bool K64>
+template <int QBITS, typename AT, bool GATEUP, int NWV, int PD, bool K64, int BM>
 __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void grouped_gemm2_kernel(FfnArgs a,
                                                                                                  int n_ntiles) {
-  constexpr int NT = 64 * NWV;              // threads
-  constexpr int AI = kBM2 * (kBK2 / 16) / NT;  // A staging items (16-element groups) per thread
-  __shared__ __attribute__((aligned(16))) f16 As[2][kBM2 * kLDA2];
+  static_assert(BM % 32 == 0 && BM <= 128, "whole 32-row MFMA tiles");
+  constexpr int NT = 64 * NWV;                         // threads
+  constexpr int MI = BM / 32;                          // MFMA row tiles per wave
+  constexpr int AITEMS = BM * (kBK2 / 16);             // A staging items (16-element groups) per step
+  constexpr int AI = (AITEMS + NT - 1) / NT;           // per thread (the last may be past the tile)
+  __shared__ __attribute__((aligned(16))) f16 As[2][BM * kLDA2];
 
   // ---- work item (XCD-aware remap over the real items)
   const int n_tiles = a.header[kHdrTiles];
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
   const bool shared = e < 0;
   const int lo = shared ? 0 : a.offsets[e];
   const int m_count = shared ? int(a.T) : a.offsets[e + 1] - lo;
-  const int rows_valid = min(kBM2, m_count - m0);
+  const int rows_valid = min(BM, m_count - m0);
   const int H = a.H;
   const int K = GATEUP ? H : (shared ? a.Is : a.I);
   const int Nrows = GATEUP ? (shared ? a.Is : a.I) : H;  // rows of each weight matrix
@@ -193,14 +197,14 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  static_assert(AI >= 1 && AI * NT == kBM2 * (kBK2 / 16), "A staging covers the tile");
 
-  // ---- A sources: thread handles items tid + NT i (i < AI) of the 128 x 8 groups
+  // ---- A sources: thread handles items tid + NT i (i < AI) of the BM x 8
+  // groups; an item past the tile loads a real row and is never stored
   const AT* asrc[AI];
   int arow[AI], agrp[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int item = tid + NT * i;
+    const int item = min(tid + NT * i, AITEMS - 1);
     arow[i] = item >> 3;
     agrp[i] = item & 7;
     const int r = min(arow[i], rows_valid - 1);  // rows past the segment read a real row; never stored
@@ -246,6 +250,7 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
   auto store_a = [&](const Raw (&r)[AR], f16* buf) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
+      if (AITEMS % NT != 0 && tid + NT * i >= AITEMS) continue;
       half8 l8, h8;
       cvt_araw<AT>(r[i >> 1], i & 1, l8, h8);
       half8* d = reinterpret_cast<half8*>(buf + arow[i] * kLDA2 + agrp[i] * 16);
@@ -254,9 +259,9 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
     }
   };
 
-  float16v acc[4][2];
+  float16v acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -295,12 +300,12 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
         for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bring[p][j], q, blo[j], bhi[j]);
 #pragma unroll
         for (int half_ = 0; half_ < 2; ++half_) {
-          half8 af[4];
+          half8 af[MI];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < MI; ++i)
             af[i] = *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + 64 * h + 16 * q + 8 * half_);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], half_ ? bhi[j] : blo[j], acc[i][j]);
         }
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
   // ---- epilogue.  32 x 32 D layout: lane l holds column l % 32 and rows
   // 8*(q/4) + 4*(l/32) + q%4, q = 0..15.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int m = 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
   }
 }
 
-template <int QBITS, typename XT>
+template <int QBITS, typename XT, int BM>
 static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases) {
   constexpr int W = MOE_GROUPED2_WAVES, PD = MOE_GROUPED2_PD;
   if (phases & kPhaseGateUp) {
@@ -348,28 +353,42 @@ static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStrea
     const int nn = (rows + 32 * W - 1) / (32 * W);
     const int64_t total = max_tiles * nn;
     const unsigned grid = unsigned((total + 7) / 8 * 8);
-    if (a.H % 64 == 0) grouped_gemm2_kernel<QBITS, XT, true, W, PD, true><<<grid, 64 * W, 0, stream>>>(a, nn);
-    else grouped_gemm2_kernel<QBITS, XT, true, W, PD, false><<<grid, 64 * W, 0, stream>>>(a, nn);
+    if (a.H % 64 == 0) grouped_gemm2_kernel<QBITS, XT, true, W, PD, true, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    else grouped_gemm2_kernel<QBITS, XT, true, W, PD, false, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
   }
   if (phases & kPhaseDown) {
     const int nn = (a.H + 64 * W - 1) / (64 * W);
     const int64_t total = max_tiles * nn;
     const unsigned grid = unsigned((total + 7) / 8 * 8);
     if (a.I % 64 == 0 && (!a.has_shared || a.Is % 64 == 0))
-      grouped_gemm2_kernel<QBITS, f16, false, W, PD, true><<<grid, 64 * W, 0, stream>>>(a, nn);
+      grouped_gemm2_kernel<QBITS, f16, false, W, PD, true, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
     else
-      grouped_gemm2_kernel<QBITS, f16, false, W, PD, false><<<grid, 64 * W, 0, stream>>>(a, nn);
+      grouped_gemm2_kernel<QBITS, f16, false, W, PD, false, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases) {
+// Rows per tile: 96 when the routed experts hold at most ~90 rows each on
+// average (then most experts fit one 96-row tile, with fewer padding rows
+// than in a 128-row one), else 128.
+int grouped_tile_rows(int64_t T, int k, int E) {
+  const int64_t P = T * k, active = std::max<int64_t>(1, std::min<int64_t>(E, P));
+  return P <= 90 * active ? 96 : 128;
+}
+
+hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, int bm, hipStream_t stream, int phases) {
   if (a.T == 0) return hipSuccess;
-  if (a.qbits == 2)
-    return a.x_bf16 ? launch_grouped_q<2, uint16_t>(a, max_tiles, stream, phases)
-                    : launch_grouped_q<2, float>(a, max_tiles, stream, phases);
-  return a.x_bf16 ? launch_grouped_q<3, uint16_t>(a, max_tiles, stream, phases)
-                  : launch_grouped_q<3, float>(a, max_tiles, stream, phases);
+  if (bm != 96 && bm != 128) return hipErrorInvalidValue;
+#define GQ(Q_, X_) \
+  return bm == 96 ? launch_grouped_q<Q_, X_, 96>(a, max_tiles, stream, phases) \
+                  : launch_grouped_q<Q_, X_, 128>(a, max_tiles, stream, phases)
+  if (a.qbits == 2) {
+    if (a.x_bf16) GQ(2, uint16_t);
+    GQ(2, float);
+  }
+  if (a.x_bf16) GQ(3, uint16_t);
+  GQ(3, float);
+#undef GQ
 }
 
 }  // namespace moe

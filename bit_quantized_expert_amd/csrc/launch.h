@@ -78,10 +78,11 @@ hipError_t launch_select_small(const float* logits, int T, int E, int k, int has
 // Routed + shared expert FFN on the decode kernels: h then y_sorted / shared_out.
 enum { kPhaseGateUp = 1, kPhaseDown = 2 };
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases);
-// Grouped-GEMM expert FFN over the tile list of launch_plan (tile_bm =
-// kGroupedBM); max_tiles bounds the list for the launch grid.
-constexpr int kGroupedBM = 128;
-hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases);
+// Grouped-GEMM expert FFN over the tile list of launch_plan, built with
+// tile_bm = grouped_tile_rows(T, k, E) (96 or 128) and launched with the same
+// bm; max_tiles bounds the list for the launch grid.
+int grouped_tile_rows(int64_t T, int k, int E);
+hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, int bm, hipStream_t stream, int phases);
 // The fused single-token decode FFN (needs E <= kDecode1MaxExperts): gate/up
 // with the selection made from the router logits in every workgroup, then
 // down + combine into out and/or res.  The selected experts occupy slots in
