@@ -57,6 +57,10 @@ RAGGED = [
     ("w2", 160, 96, 3, 2, 32, 3, 400, torch.float32),
     ("w3", 256, 192, 4, 2, 0, 2, 600, torch.bfloat16),
     ("w4", 2048, 704, 4, 2, 704, 3, 520, torch.bfloat16),
+    # ~90 rows per expert or fewer on average (96-row tiles), Zipf-skewed so that some segments span
+    # several tiles with a ragged last one
+    ("b1", 128, 96, 16, 2, 64, 2, 700, torch.bfloat16),
+    ("b2", 256, 192, 24, 3, 0, 3, 680, torch.float32),
 ]
 
 
