@@ -15,8 +15,8 @@ layers with the residual/RMSNorm/bf16 glue; one 32,768-token prefill layer
 (grouped-GEMM path, MFMA roofline of its gate/up and down kernels); the
 4,096-token 3-bit prefill through a 48-layer stack with uniform routing.
 
-Output: one JSON line (see the keys below).  --gpus N with N > 1 exits: this
-build runs on one GPU.
+Output: one JSON line (see the keys below).  --gpus N with N > 1 exits: the
+benchmark runs on one GPU.
 """
 
 from __future__ import annotations
@@ -373,7 +373,7 @@ def main():
             print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU"}))

@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
-  MOE_ERR_UNSUPPORTED = -2, /* a valid request this build does not handle */
+  MOE_ERR_UNSUPPORTED = -2, /* a valid request the library does not handle */
   MOE_ERR_WORKSPACE = -3,   /* workspace too small; see moe_last_required_workspace */
   MOE_ERR_DEVICE = -4,      /* a HIP call or kernel launch failed */
   MOE_ERR_INDEX = -5        /* an expert id outside [0, E) reached moe_permute */
