@@ -167,7 +167,8 @@ def _permute(M, idx_np, E, k):
 
 @pytest.mark.parametrize("T,E,k,skew", [(1, 512, 10, 0), (16, 512, 10, 1), (37, 9, 3, 0), (204, 512, 10, 1),
                                         (205, 512, 10, 1), (3000, 512, 10, 1), (32768, 512, 10, 1),
-                                        (4096, 512, 10, 0), (500, 1, 1, 0)])
+                                        (4096, 512, 10, 0), (500, 1, 1, 0), (3000, 4096, 32, 1),
+                                        (16, 4096, 32, 0)])
 def test_permute_bit_exact(T, E, k, skew):
     M = _lib()
     rng = np.random.default_rng(T * 7 + E)

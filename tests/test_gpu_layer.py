@@ -75,6 +75,10 @@ RAGGED = [
     ("s3", 128, 160, 12, 4, 0, 2, 1, torch.bfloat16),
     ("s4", 256, 192, 33, 8, 96, 3, 1, torch.bfloat16),
     ("s5", 192, 128, 40, 32, 64, 2, 1, torch.bfloat16),
+    # the largest expert count and top-k the library takes (4096, 32): selection over 64 keys per
+    # lane, one token through the small-batch path
+    ("m1", 64, 32, 4096, 32, 32, 2, 1, torch.bfloat16),
+    ("m2", 64, 32, 4096, 32, 32, 3, 16, torch.bfloat16),
 ]
 
 

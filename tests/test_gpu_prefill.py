@@ -61,6 +61,8 @@ RAGGED = [
     # several tiles with a ragged last one
     ("b1", 128, 96, 16, 2, 64, 2, 700, torch.bfloat16),
     ("b2", 256, 192, 24, 3, 0, 3, 680, torch.float32),
+    # the largest expert count and top-k (4096, 32)
+    ("m3", 64, 32, 4096, 32, 32, 2, 40, torch.bfloat16),
 ]
 
 
