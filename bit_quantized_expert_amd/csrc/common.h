@@ -67,6 +67,62 @@ __device__ __forceinline__ float16v mfma32_bf16(bf16x8 a, bf16x8 b, float16v c) 
 }
 
 // ---------------------------------------------------------------------------
+// Tiled storage of one quantised matrix [rows][K] (K a multiple of 32).
+// Rows go in groups of 16 (the last group of a matrix may be shorter);
+// within a group the K axis is cut into units of 64 weights (two 32-weight
+// blocks), and one unit of the whole group is contiguous, row after row:
+//   low code plane (2 bits per weight): 16 bytes per row and unit,
+//   scales (fp16, one per block):        4 bytes per row and unit,
+//   3-bit high plane (1 bit per weight):  8 bytes per row and unit.
+// When K % 64 == 32 the last unit of a group holds one block (8, 2 and 4
+// bytes per row).  A group occupies the bytes its rows take in row-major
+// order, so buffer sizes, the offset of the high plane (rows * K / 4 bytes)
+// and per-expert strides are those of the row-major layout; only the order
+// within a group differs.  A wave that reads one unit of 16 rows (the GEMV
+// and GEMM weight loads) then reads one 256-byte piece of codes instead of 16
+// separate 16-byte pieces.  Within a block the bits are as in row-major
+// storage: weight i of the block at bits 2i (low plane) and bit i (high).
+// ---------------------------------------------------------------------------
+struct QTile {
+  int64_t g0;  // first row of the row's group
+  int gsz;     // rows in the group
+  int rr;      // row within the group
+};
+
+// rows = rows of the matrix; FULL: every group has 16 rows (rows % 16 == 0).
+template <bool FULL>
+__host__ __device__ __forceinline__ QTile qtile(int64_t row, int64_t rows) {
+  QTile t;
+  t.g0 = row & ~int64_t(15);
+  t.gsz = FULL ? 16 : int(rows - t.g0 < 16 ? rows - t.g0 : 16);
+  t.rr = int(row - t.g0);
+  return t;
+}
+
+// Byte offset (in the low plane) of the 8 code bytes of block blk.
+__host__ __device__ __forceinline__ int64_t qt_code_off(const QTile& t, int K, int blk) {
+  const int nuf = K / 64, u = blk >> 1;
+  const int64_t base = t.g0 * (K / 4);
+  return u < nuf ? base + int64_t(u) * t.gsz * 16 + t.rr * 16 + (blk & 1) * 8
+                 : base + int64_t(nuf) * t.gsz * 16 + t.rr * 8;
+}
+
+// Offset (in fp16 elements) of the scale of block blk.
+__host__ __device__ __forceinline__ int64_t qt_scale_off(const QTile& t, int K, int blk) {
+  const int nuf = K / 64, u = blk >> 1;
+  const int64_t base = t.g0 * (K / 32);
+  return u < nuf ? base + int64_t(u) * t.gsz * 2 + t.rr * 2 + (blk & 1) : base + int64_t(nuf) * t.gsz * 2 + t.rr;
+}
+
+// Byte offset (in the high plane) of the 4 high-plane bytes of block blk.
+__host__ __device__ __forceinline__ int64_t qt_high_off(const QTile& t, int K, int blk) {
+  const int nuf = K / 64, u = blk >> 1;
+  const int64_t base = t.g0 * (K / 8);
+  return u < nuf ? base + int64_t(u) * t.gsz * 8 + t.rr * 8 + (blk & 1) * 4
+                 : base + int64_t(nuf) * t.gsz * 8 + t.rr * 4;
+}
+
+// ---------------------------------------------------------------------------
 // Dequantisation of one 32-bit word of 2-bit codes into fp16 pairs.
 //
 // A word holds 16 codes, code i at bits 2i..2i+1.  Pair i (i = 0..7) is

@@ -108,21 +108,26 @@ struct Unit {
   uint32_t s;             // fp16 scale bits (two for UNIT = 64)
 };
 
+// Unit u of row `row` of a matrix of `rows` rows in the tiled layout of
+// common.h (rows are multiples of 32, so every 16-row group is full; UNIT 64
+// is used only when K % 64 == 0, so its units are whole 64-weight units).
 template <int QBITS, int UNIT>
 __device__ __forceinline__ void load_unit(Unit<QBITS, UNIT>& U, const uint8_t* codes, const uint16_t* scales,
                                           int rows, int K, int row, int u) {
-  const uint8_t* lo = codes + int64_t(row) * (K / 4) + u * (UNIT / 4);
+  const QTile tl = qtile<true>(row, rows);
+  const int blk = UNIT == 64 ? 2 * u : u;
+  const uint8_t* lo = codes + qt_code_off(tl, K, blk);
   if constexpr (UNIT == 64) {
     const uint4v c = *reinterpret_cast<const uint4v*>(lo);
     U.w[0] = c[0]; U.w[1] = c[1]; U.w[2] = c[2]; U.w[3] = c[3];
-    U.s = *reinterpret_cast<const uint32_t*>(scales + int64_t(row) * (K / 32) + u * 2);
+    U.s = *reinterpret_cast<const uint32_t*>(scales + qt_scale_off(tl, K, blk));
   } else {
     const uint2v c = *reinterpret_cast<const uint2v*>(lo);
     U.w[0] = c[0]; U.w[1] = c[1];
-    U.s = scales[int64_t(row) * (K / 32) + u];
+    U.s = scales[qt_scale_off(tl, K, blk)];
   }
   if constexpr (QBITS == 3) {
-    const uint8_t* hp = codes + int64_t(rows) * (K / 4) + int64_t(row) * (K / 8) + u * (UNIT / 8);
+    const uint8_t* hp = codes + int64_t(rows) * (K / 4) + qt_high_off(tl, K, blk);
     if constexpr (UNIT == 64) {
       const uint2v hv = *reinterpret_cast<const uint2v*>(hp);
       U.h[0] = hv[0]; U.h[1] = hv[1];

@@ -115,13 +115,13 @@ __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, c
     const int b0 = 4 * step + 2 * h;
     const bool in = ok && b0 < nb;
     const int rr = in ? row : 0, bb = in ? b0 : 0;
+    const QTile tl = qtile<true>(rr, rows);  // tiled layout (common.h); weight rows are multiples of 32
     // raw values only: a select on a loaded value here would wait for the
     // load; blocks past K are zeroed through their scale at dequantisation
-    r.c = *reinterpret_cast<const uint4v*>(codes + int64_t(rr) * (K / 4) + bb * 8);
-    r.s = *reinterpret_cast<const uint32_t*>(scales + int64_t(rr) * nb + bb);
+    r.c = *reinterpret_cast<const uint4v*>(codes + qt_code_off(tl, K, bb));
+    r.s = *reinterpret_cast<const uint32_t*>(scales + qt_scale_off(tl, K, bb));
     if constexpr (QBITS == 3) {
-      const uint2v hv = *reinterpret_cast<const uint2v*>(codes + int64_t(rows) * (K / 4) + int64_t(rr) * (K / 8) +
-                                                        bb * 4);
+      const uint2v hv = *reinterpret_cast<const uint2v*>(codes + int64_t(rows) * (K / 4) + qt_high_off(tl, K, bb));
       r.hb[0] = hv[0];
       r.hb[1] = hv[1];
     }
@@ -129,24 +129,23 @@ __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, c
     return;
   }
   // blocks of this lane: b0 = 4 * step + 2h and b0 + 1, each zero past K or
-  // past the matrix.  Every load stays inside its row (8-byte code loads,
-  // 2-byte scale loads: rows of K / 4 code bytes are only 8-byte aligned)
-  // and is unconditional from a clamped address.
+  // past the matrix.  One load per block (8 code bytes, one scale: a K with
+  // an odd block count ends in a one-block unit), each unconditional from a
+  // clamped address.
   const int nb = K / 32;
   const int b0 = 4 * step + 2 * h;
   const bool in0 = ok && b0 < nb, in1 = ok && b0 + 1 < nb;
   const int rr = in0 ? row : 0, bb0 = in0 ? b0 : 0, bb1 = in1 ? b0 + 1 : bb0;
-  const uint8_t* cr = codes + int64_t(rr) * (K / 4);
-  const uint16_t* sr = scales + int64_t(rr) * nb;
-  const uint2v c0 = *reinterpret_cast<const uint2v*>(cr + bb0 * 8);
-  const uint2v c1 = *reinterpret_cast<const uint2v*>(cr + bb1 * 8);
-  const uint32_t s0 = sr[bb0], s1 = sr[bb1];
+  const QTile tl = qtile<true>(rr, rows);
+  const uint2v c0 = *reinterpret_cast<const uint2v*>(codes + qt_code_off(tl, K, bb0));
+  const uint2v c1 = *reinterpret_cast<const uint2v*>(codes + qt_code_off(tl, K, bb1));
+  const uint32_t s0 = scales[qt_scale_off(tl, K, bb0)], s1 = scales[qt_scale_off(tl, K, bb1)];
   r.c = uint4v{c0[0], c0[1], c1[0], c1[1]};
   r.s = s0 | (s1 << 16);
   if constexpr (QBITS == 3) {
-    const uint32_t* hp = reinterpret_cast<const uint32_t*>(codes + int64_t(rows) * (K / 4) + int64_t(rr) * (K / 8));
-    r.hb[0] = hp[bb0];
-    r.hb[1] = hp[bb1];
+    const uint8_t* hp = codes + int64_t(rows) * (K / 4);
+    r.hb[0] = *reinterpret_cast<const uint32_t*>(hp + qt_high_off(tl, K, bb0));
+    r.hb[1] = *reinterpret_cast<const uint32_t*>(hp + qt_high_off(tl, K, bb1));
   }
   r.v = (in0 ? 1u : 0u) | (in1 ? 2u : 0u);
 }

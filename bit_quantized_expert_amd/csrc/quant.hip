@@ -1,11 +1,13 @@
 // Block quantiser and dequantiser for the 2-bit / 3-bit expert format.
 //
 // Format: blocks of 32 weights along the reduction axis share one fp16 scale;
-// code c in [-2^(b-1), 2^(b-1)-1] stored offset-binary.  2-bit codes: byte
-// k/4, bits 2*(k%4).  3-bit codes: that low plane, then a high plane with bit
-// 2 of q in byte k/8 at bit k%8.  (The pages say experts are stored and read
-// at 2 bits -- "How Strata runs a 125-billion-parameter model ...", intro and
-// Step 1 byte table; the block layout is this library's own.)
+// code c in [-2^(b-1), 2^(b-1)-1] stored offset-binary.  Within a block,
+// weight i sits at bits 2i of the block's 8 low-plane bytes and (3-bit) at
+// bit i of its 4 high-plane bytes; blocks, scales and high-plane pieces are
+// placed by the tiled layout of common.h (16-row groups, 64-weight units).
+// (The pages say experts are stored and read at 2 bits -- "How Strata runs a
+// 125-billion-parameter model ...", intro and Step 1 byte table; the block
+// layout is this library's own.)
 #include "common.h"
 #include "launch.h"
 
@@ -45,8 +47,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     if (d != 0.0f) c = fminf(fmaxf(__builtin_rintf(__fdiv_rn(v[i], d)), cmin), cmax);
     q[i] = uint32_t(int(c) + off);
   }
+  const QTile tl = qtile<false>(r, rows);
   // a zero scale is stored as +0 whatever the sign of the largest element
-  scales[b] = d == 0.0f ? uint16_t(0) : __builtin_bit_cast(uint16_t, d16);
+  scales[qt_scale_off(tl, cols, j)] = d == 0.0f ? uint16_t(0) : __builtin_bit_cast(uint16_t, d16);
   // low plane: 8 bytes per block
   uint32_t lo0 = 0, lo1 = 0;
 #pragma unroll
@@ -54,13 +57,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     lo0 |= (q[i] & 3u) << (2 * i);
     lo1 |= (q[16 + i] & 3u) << (2 * i);
   }
-  uint2v* dst = reinterpret_cast<uint2v*>(codes + (r * cols + int64_t(j) * kBlock) / 4);
+  uint2v* dst = reinterpret_cast<uint2v*>(codes + qt_code_off(tl, cols, j));
   *dst = uint2v{lo0, lo1};
   if constexpr (QBITS == 3) {
     uint32_t hi = 0;
 #pragma unroll
     for (int i = 0; i < kBlock; ++i) hi |= ((q[i] >> 2) & 1u) << i;
-    uint32_t* hdst = reinterpret_cast<uint32_t*>(codes + rows * cols / 4 + (r * cols + int64_t(j) * kBlock) / 8);
+    uint32_t* hdst = reinterpret_cast<uint32_t*>(codes + rows * cols / 4 + qt_high_off(tl, cols, j));
     *hdst = hi;
   }
 }
@@ -74,11 +77,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t nblk = rows * bpr;
   const int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (b >= nblk) return;
-  const int64_t base = b * kBlock;  // == r * cols + j * 32
-  const uint2v lo = *reinterpret_cast<const uint2v*>(codes + base / 4);
+  const int64_t base = b * kBlock;  // == r * cols + j * 32 (row-major output)
+  const int64_t r = b / bpr;
+  const int j = int(b - r * bpr);
+  const QTile tl = qtile<false>(r, rows);
+  const uint2v lo = *reinterpret_cast<const uint2v*>(codes + qt_code_off(tl, cols, j));
   uint32_t hi = 0;
-  if constexpr (QBITS == 3) hi = *reinterpret_cast<const uint32_t*>(codes + rows * cols / 4 + base / 8);
-  const float s = float(__builtin_bit_cast(f16, scales[b]));
+  if constexpr (QBITS == 3) hi = *reinterpret_cast<const uint32_t*>(codes + rows * cols / 4 + qt_high_off(tl, cols, j));
+  const float s = float(__builtin_bit_cast(f16, scales[qt_scale_off(tl, cols, j)]));
   constexpr int off = 1 << (QBITS - 1);
   float4v* dst = reinterpret_cast<float4v*>(out + base);
 #pragma unroll

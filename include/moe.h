@@ -38,13 +38,30 @@
  *   - blocks of 32 consecutive weights along K share one fp16 scale s;
  *   - code c in [-2^(b-1), 2^(b-1)-1], weight = c * s, stored offset-binary
  *     q = c + 2^(b-1);
- *   - 2-bit codes: row-major [rows][K/4] bytes, weight k of a row in byte
- *     k/4 at bits 2*(k%4)..2*(k%4)+1;
- *   - 3-bit codes: a low plane laid out exactly like the 2-bit codes (low two
- *     bits of q), followed by a high plane [rows][K/8] bytes holding bit 2 of
- *     q for weight k in byte k/8 at bit k%8;
- *   - scales: fp16 bit patterns, row-major [rows][K/32].
+ *   - per block: 8 low-plane bytes (2-bit codes, or the low two bits of
+ *     3-bit ones), weight i of the block at bits 2*(i%4) of byte i/4; with
+ *     3 bits also 4 high-plane bytes, bit 2 of q for weight i at bit i%8 of
+ *     byte i/8; and one fp16 scale (bit pattern);
+ *   - tiled placement: rows go in groups of 16 (the last group may be
+ *     shorter); within a group K is cut into units of 64 weights (two
+ *     blocks), and a unit of the whole group is contiguous, row after row:
+ *     16 low-plane bytes, 2 scales and 8 high-plane bytes per row and unit.
+ *     With K % 64 == 32 a group's last unit is one block (8 bytes, 1 scale,
+ *     4 bytes per row).  Groups follow each other in row order.  So with G0
+ *     the first row of row r's group, n its size, j = r - G0, u = blk / 2
+ *     and U = K / 64 full units, block blk of row r has
+ *       low-plane bytes at  G0*K/4  + (u < U ? u*n*16 + j*16 + (blk%2)*8
+ *                                             : U*n*16 + j*8),
+ *       its scale at fp16 index  G0*K/32 + (u < U ? u*n*2 + j*2 + blk%2
+ *                                                  : U*n*2 + j),
+ *       high-plane bytes at  G0*K/8 + (u < U ? u*n*8 + j*8 + (blk%2)*4
+ *                                              : U*n*8 + j*4)
+ *     within the high plane, which follows the low plane (rows*K/4 bytes);
+ *   - buffer sizes are those of dense row-major planes: rows*K/4 (+ rows*K/8)
+ *     code bytes and rows*K/32 scales; an arena's per-expert strides count
+ *     those bytes.
  * Expert matrices: gate [I][H], up [I][H] (K = H) and down [H][I] (K = I).
+ * The expert kernels read one unit of 16 rows as one contiguous piece.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -121,3 +121,39 @@ def check_route_protocol(gpu_logits, gpu_idx, gpu_w, oracle_logits, k):
         gap = np.abs(ol[t, gi[t]] - ol[t, oi[t]])
         assert np.all(gap <= TIE_TAU), f"token {t}: index swap outside the tie band (gap {gap.max():.3e})"
     return flagged
+
+
+def tile_quantised(codes: np.ndarray, scales: np.ndarray, rows: int, K: int, qbits: int):
+    """Row-major codes / scales (the oracle's quantiser: low plane [rows][K/4],
+    3-bit high plane [rows][K/8] after it, scales [rows][K/32]) rearranged
+    into the library's tiled storage: rows in groups of 16 (the last group
+    may be shorter), each 64-weight unit (two blocks) of a whole group
+    contiguous, row after row -- 16 low-plane bytes, 2 scales and 8
+    high-plane bytes per row and unit; with K % 64 == 32 the last unit of a
+    group is one block (8 bytes, 1 scale, 4 bytes per row)."""
+    nb, nuf = K // 32, K // 64
+    lo = np.asarray(codes[: rows * K // 4]).reshape(rows, K // 4)
+    sc = np.asarray(scales).reshape(rows, nb)
+    out_lo = np.zeros(rows * K // 4, np.uint8)
+    out_sc = np.zeros(rows * nb, np.uint16)
+    hi = np.asarray(codes[rows * K // 4:]).reshape(rows, K // 8) if qbits == 3 else None
+    out_hi = np.zeros(rows * K // 8, np.uint8) if qbits == 3 else None
+    for r in range(rows):
+        g0 = r - r % 16
+        gsz, rr = min(16, rows - g0), r - g0
+        for b in range(nb):
+            u = b // 2
+            if u < nuf:
+                co = g0 * (K // 4) + u * gsz * 16 + rr * 16 + (b % 2) * 8
+                so = g0 * nb + u * gsz * 2 + rr * 2 + b % 2
+                ho = g0 * (K // 8) + u * gsz * 8 + rr * 8 + (b % 2) * 4
+            else:
+                co = g0 * (K // 4) + nuf * gsz * 16 + rr * 8
+                so = g0 * nb + nuf * gsz * 2 + rr
+                ho = g0 * (K // 8) + nuf * gsz * 8 + rr * 4
+            out_lo[co:co + 8] = lo[r, 8 * b:8 * b + 8]
+            out_sc[so] = sc[r, b]
+            if qbits == 3:
+                out_hi[ho:ho + 4] = hi[r, 4 * b:4 * b + 4]
+    out_codes = out_lo if qbits == 2 else np.concatenate([out_lo, out_hi])
+    return out_codes, out_sc

@@ -102,3 +102,38 @@ def test_validation_before_any_device_call():
     assert lib.moe_permute(fake, 4096, ctypes.byref(s), fake, fake, fake, fake, fake, 16, None) \
         == L.MOE_ERR_WORKSPACE
     assert lib.moe_read_error(None, 0, None) == L.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("rows,K,qbits", [(3, 32, 2), (17, 96, 3), (40, 64, 2), (33, 160, 3), (64, 704, 2)])
+def test_tiled_layout_is_a_permutation(rows, K, qbits):
+    """The tiled storage of the quantised matrices (as the tests restate it)
+    moves every byte of the row-major layout to a distinct place, so it keeps
+    the buffer sizes: tiling distinct byte values gives every value once."""
+    import numpy as np
+    from tests.helpers import tile_quantised
+    n_codes, n_scales = rows * K * qbits // 8, rows * K // 32
+    codes = np.arange(n_codes, dtype=np.int64)
+    scales = np.arange(n_scales, dtype=np.int64)
+    # distinct labels instead of bytes: run the mapping on int64 arrays of positions
+    tc, ts = _tile_positions(codes, scales, rows, K, qbits, tile_quantised)
+    assert sorted(tc.tolist()) == list(range(n_codes))
+    assert sorted(ts.tolist()) == list(range(n_scales))
+    # a one-group matrix with K a multiple of 64 keeps each row's 16-byte units in row order
+    if rows <= 16 and K % 64 == 0:
+        first_unit = tc[:16 * rows].reshape(rows, 16)
+        assert np.array_equal(first_unit, np.arange(16)[None, :] + (K // 4) * np.arange(rows)[:, None])
+
+
+def _tile_positions(codes, scales, rows, K, qbits, tile):
+    """tile() on position labels: the helper copies values, so labels that fit
+    its dtypes (uint8 bytes / uint16 scales) are tiled in chunks of 256 / 65536."""
+    import numpy as np
+    out_c = np.zeros_like(codes)
+    out_s = np.zeros_like(scales)
+    for shift in range(0, 64, 8):  # byte-plane by byte-plane of the labels
+        c8 = ((codes >> shift) & 0xFF).astype(np.uint8)
+        s16 = ((scales >> shift) & 0xFF).astype(np.uint16)
+        tc, ts = tile(c8, s16, rows, K, qbits)
+        out_c |= tc.astype(np.int64) << shift
+        out_s |= ts.astype(np.int64) << shift
+    return out_c, out_s

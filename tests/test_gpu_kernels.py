@@ -8,7 +8,7 @@ import torch
 
 from oracle import moe_oracle as O
 from bit_quantized_expert_amd import synth
-from tests.helpers import check_route_protocol
+from tests.helpers import check_route_protocol, tile_quantised
 
 pytestmark = pytest.mark.gpu
 
@@ -37,10 +37,11 @@ def test_quantize_and_dequant_bit_exact(qbits, rows, k):
     scales = torch.empty(rows * k // 32, dtype=torch.int16, device="cuda")
     M.quantize(w.cuda(), qbits, codes, scales)
     want_codes, want_scales = O.quantize(w.numpy(), qbits)
-    assert np.array_equal(codes.cpu().numpy(), want_codes)
-    assert np.array_equal(scales.cpu().numpy().view(np.uint16).reshape(rows, k // 32), want_scales)
+    tiled_codes, tiled_scales = tile_quantised(want_codes, want_scales, rows, k, qbits)
+    assert np.array_equal(codes.cpu().numpy(), tiled_codes)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), tiled_scales)
     out = torch.empty(rows, k, dtype=torch.float32, device="cuda")
-    M.dequant(codes, scales, rows, k, qbits, out)
+    M.dequant(codes, scales, rows, k, qbits, out)  # the library's (tiled) storage in, the plain matrix out
     want = O.dequant(want_codes, want_scales, rows, k, qbits)
     assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
 
