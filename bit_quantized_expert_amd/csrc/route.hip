@@ -122,8 +122,13 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const XT* __restrict__
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int router_class_len(int nkb) { return (nkb + 7) / 8; }
 
-// Few tokens: workgroup = 16 experts x 16 tokens, 8 waves; wave w runs class
-// w and the 8 partial tiles meet in LDS.
+// Few tokens: workgroup = EPW experts x 16 tokens on one 16 x 16 MFMA tile,
+// 8 waves; wave w runs class w and the 8 partial tiles meet in LDS.  With
+// EPW < 16 (a handful of tokens: the MFMA work is negligible, the weight
+// rows are spread over more CUs) MFMA columns EPW..15 repeat real rows (the
+// same addresses, no extra traffic) and are zeroed; every logit goes through
+// the same MFMA sequence whatever EPW is.
+template <int EPW>
 __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
                                                          const uint16_t* __restrict__ w,
                                                          const float* __restrict__ bias, int E,
@@ -131,13 +136,14 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
   __shared__ float red[8][4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int e0 = blockIdx.x * 16;
+  const int e0 = blockIdx.x * EPW;
   const int64_t t0 = int64_t(blockIdx.y) * 16;
   const int nkb = H / 32, cl = router_class_len(nkb);
   const int c0 = min(nkb, wv * cl), c1 = min(nkb, c0 + cl);
-  const bool b_on = e0 + n < E;
+  const int er = e0 + (EPW == 16 ? n : n % EPW);
+  const bool b_on = (EPW == 16 || n < EPW) && er < E;
   const bool a_on = t0 + n < T;
-  const uint16_t* wrow = w + int64_t(b_on ? e0 + n : 0) * H + 8 * g;
+  const uint16_t* wrow = w + int64_t(er < E ? er : 0) * H + 8 * g;
   const uint16_t* xrow = x + (a_on ? t0 + n : 0) * H + 8 * g;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   constexpr int B = 8;  // K blocks per load batch
@@ -170,11 +176,11 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] += red[q][j][lane];
   if (!b_on) return;
-  const float b = bias ? bias[e0 + n] : 0.0f;
+  const float b = bias ? bias[er] : 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t t = t0 + 4 * g + j;
-    if (t < T) logits[t * E + e0 + n] = acc[j] + b;
+    if (t < T) logits[t * E + er] = acc[j] + b;
   }
 }
 
@@ -195,7 +201,10 @@ constexpr int kRtOutPitch = kRtE + 4;   // LDS row pitch of the logits tile in f
 #ifndef MOE_ROUTER_GEMM_MIN_T
 #define MOE_ROUTER_GEMM_MIN_T 2048
 #endif
-constexpr int64_t kRouterGemmMinT = MOE_ROUTER_GEMM_MIN_T;  // below: router_mfma_kernel's 16 x 16 tiles
+constexpr int64_t kRouterGemmMinT = MOE_ROUTER_GEMM_MIN_T;
+#ifndef MOE_ROUTER_SMALL_EPW
+#define MOE_ROUTER_SMALL_EPW 2  // experts per workgroup of the router at <= 16 tokens (one workgroup per CU at 512 experts)
+#endif  // below: router_mfma_kernel's 16 x 16 tiles
 // LDS row pitch of the staged operands in bf16: an odd number of 16-byte
 // units, so the 16 rows of a fragment read hit distinct banks
 template <int RK>
@@ -357,8 +366,13 @@ hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_
                                                                            total);
     return hipGetLastError();
   }
-  const dim3 grid(unsigned((E + 15) / 16), unsigned((T + 15) / 16));
-  router_mfma_kernel<<<grid, 512, 0, stream>>>(x, T, H, w, bias, E, logits);
+  if (T <= 16) {
+    constexpr int EPW = MOE_ROUTER_SMALL_EPW;
+    router_mfma_kernel<EPW><<<dim3(unsigned((E + EPW - 1) / EPW)), 512, 0, stream>>>(x, T, H, w, bias, E, logits);
+  } else {
+    const dim3 grid(unsigned((E + 15) / 16), unsigned((T + 15) / 16));
+    router_mfma_kernel<16><<<grid, 512, 0, stream>>>(x, T, H, w, bias, E, logits);
+  }
   return hipGetLastError();
 }
 
