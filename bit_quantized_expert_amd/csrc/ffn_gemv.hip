@@ -341,14 +341,20 @@ __global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnAr
 // expert, combined inside the workgroup (the fused decode layer):
 //   out[r] = shared[r] + sum_{j<k} w_j * y_j[r]
 // in the combine's order (shared first, then ranks 0..k-1, one fma each).
-// grid = H / 16, block = 64 * NW: wave w takes slots w, w + NW, ... (slot
-// s < k = expert slot_expert[s], h row s; slot k = shared) and computes 16
-// output rows of its slot with the same MFMA sequence as the standalone down
-// kernel; the combine takes the slots in rank order through slot_of_rank.  The
-// weight loads of a wave's first slot go out first; meanwhile the workgroup
-// copies the h rows of all slots into LDS (their addresses depend on
-// nothing), and the MFMA operands are read from there.  The rows of all
-// slots meet in LDS for the combine.
+// grid = H / 8: a workgroup owns 8 output rows of every slot (slot s < k =
+// expert slot_expert[s], h row s; slot k = shared).  With one token the MFMA
+// rows are free, so one MFMA serves two slots: B columns 0..7 are the 8 rows
+// of slot s0 and columns 8..15 those of slot s1, A row 0 is h of s0 and A
+// row 1 h of s1, and C[0][0..7], C[1][8..15] are the two slots' outputs
+// (the other elements are not used).  Every output element goes through the
+// same MFMA sequence as in the other down kernels, so the bits are the same,
+// and every lane's dequantisation is used: 256 workgroups (all CUs) share
+// the work that 128 did with 16 rows of one slot per MFMA.  Wave w takes
+// pairs w, w + NW, ...: pair p < ceil(k/2) = slots (2p, 2p+1), then the
+// shared expert alone (pairs mix no K).  The weight loads of a wave's first
+// pair go out first; meanwhile the workgroup copies the h rows of all slots
+// into LDS (their addresses depend on nothing), and the MFMA operands are
+// read from there.  The rows of all slots meet in LDS for the combine.
 // ---------------------------------------------------------------------------
 struct DownSlot {
   const uint8_t* dc;
@@ -372,28 +378,33 @@ __device__ __forceinline__ DownSlot down_slot(const FfnArgs& a, const int32_t* _
   return r;
 }
 
+constexpr int kDcRows = 8;  // output rows per workgroup of the single-token down + combine
+
 template <int QBITS, int UNIT>
-__global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
-                                                                     const int32_t* __restrict__ slot_expert,
-                                                                     const int32_t* __restrict__ slot_of_rank,
-                                                                     const float* __restrict__ w,
-                                                                     float* __restrict__ out,
-                                                                     float* __restrict__ res, int ldh,
-                                                                     int nthreads) {
+__global__ __launch_bounds__(1024) void gemv_down_combine_1tok_kernel(FfnArgs a,
+                                                                      const int32_t* __restrict__ slot_expert,
+                                                                      const int32_t* __restrict__ slot_of_rank,
+                                                                      const float* __restrict__ w,
+                                                                      float* __restrict__ out,
+                                                                      float* __restrict__ res, int ldh,
+                                                                      int nthreads) {
   extern __shared__ __attribute__((aligned(16))) f16 hs[];  // [n_slots][ldh]
-  __shared__ float ys[kMaxTopK + 1][16];
+  __shared__ float ys[kMaxTopK + 1][kDcRows];
   __shared__ float s_w[kMaxTopK];
   __shared__ int s_slot[kMaxTopK];
   constexpr int RB = 4;
   const int nw = nthreads >> 6;  // == blockDim.x / 64 (blockDim would be a load from the packet)
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, g = lane >> 4;
+  const int half = n >> 3;  // B columns 0..7: first slot of the pair, 8..15: second
   const int H = a.H;
-  const int row = blockIdx.x * 16 + n;  // H is a multiple of 32
+  const int row = blockIdx.x * kDcRows + (n & 7);  // H is a multiple of 32
   const int n_slots = a.k + (a.has_shared ? 1 : 0);
+  const int n_rp = (a.k + 1) / 2;                        // pairs of routed slots
+  const int n_pairs = n_rp + (a.has_shared ? 1 : 0);   // then the shared slot alone
   // Issue order: the combine's weights and slot map, then the h rows (their
-  // addresses depend on nothing), then the slot's expert id and, once it is
-  // in, the weight loads; the LDS stores come last, so no load waits for
+  // addresses depend on nothing), then the slots' expert ids and, once they
+  // are in, the weight loads; the LDS stores come last, so no load waits for
   // another before it is issued.
   float w_r = 0.0f;
   int slot_r = 0;
@@ -426,17 +437,37 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
   };
   load_h(0);
 
+  // pair p: its two slots (the second is -1 when there is none)
+  auto pair_slots = [&](int p, int& s0, int& s1) {
+    s0 = p < n_rp ? 2 * p : a.k;
+    s1 = p < n_rp && 2 * p + 1 < a.k ? 2 * p + 1 : -1;
+  };
   Unit<QBITS, UNIT> ud[RB];
-  // the wave's first slot (a wave past the slots loads the last slot's
-  // weights and never uses them); unconditional loads from clamped units,
-  // units past K are zeroed at use (a load under a branch costs a wait for
-  // every load in flight)
-  DownSlot sl = down_slot<UNIT>(a, slot_expert, min(wv, n_slots - 1));
+  int s0, s1;
+  const uint8_t* dc;
+  const uint16_t* ds;
+  int K, n_units, rounds;
+  // this lane's weight rows: slot s0 for columns 0..7, s1 for 8..15 (a
+  // missing s1 reads s0's rows, whose columns are not used)
+  auto set_pair = [&](int p) {
+    pair_slots(p, s0, s1);
+    const DownSlot d0 = down_slot<UNIT>(a, slot_expert, s0);
+    const DownSlot d1 = down_slot<UNIT>(a, slot_expert, s1 >= 0 ? s1 : s0);
+    dc = half ? d1.dc : d0.dc;
+    ds = half ? d1.ds : d0.ds;
+    K = d0.K;  // both slots of a pair have the same K
+    n_units = d0.n_units;
+    rounds = d0.rounds;
+  };
+  // unconditional loads from clamped units (a wave past the pairs loads the
+  // last pair's weights and never uses them); units past K are zeroed at use
+  // (a load under a branch costs a wait for every load in flight)
+  set_pair(min(wv, n_pairs - 1));
   auto issue = [&](int r0) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int u = (r0 + i) * 4 + g;
-      load_unit(ud[i], sl.dc, sl.ds, H, sl.K, row, r0 + i < sl.rounds && u < sl.n_units ? u : 0);
+      load_unit(ud[i], dc, ds, H, K, row, r0 + i < rounds && u < n_units ? u : 0);
     }
   };
   issue(0);
@@ -448,61 +479,66 @@ __global__ __launch_bounds__(768) void gemv_down_combine_1tok_kernel(FfnArgs a,
   }
   __syncthreads();
 
-  const bool a_on = n == 0;  // MFMA row 0 is the token; rows 1..15 are zero
-  for (int s = wv; s < n_slots; s += nw) {
-    if (s != wv) {
-      sl = down_slot<UNIT>(a, slot_expert, s);
+  for (int p = wv; p < n_pairs; p += nw) {
+    if (p != wv) {
+      set_pair(p);
       issue(0);
     }
-    const f16* hrow = hs + s * ldh;
+    // A row 0 = h of s0 (lanes n = 0), row 1 = h of s1 (lanes n = 1); the
+    // other rows repeat s0 (their outputs are not used)
+    const f16* hrow = hs + (n == 1 && s1 >= 0 ? s1 : s0) * ldh;
     float4v acc[4] = {};  // one accumulator per round class (round % 4), as in every down kernel
     static_assert(RB % 4 == 0, "a load batch holds whole round classes");
-    for (int r0 = 0; r0 < sl.rounds; r0 += RB) {
+    for (int r0 = 0; r0 < rounds; r0 += RB) {
       if (r0 > 0) issue(r0);
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
-        if (r0 + i >= sl.rounds) break;
+        if (r0 + i >= rounds) break;
         const int u = (r0 + i) * 4 + g;
-        if (u >= sl.n_units) zero_unit(ud[i]);
-        const bool on = a_on && u < sl.n_units;
+        const int ua = u < n_units ? u : 0;
+        if (u >= n_units) zero_unit(ud[i]);
 #pragma unroll
         for (int d = 0; d < UNIT / 16; ++d) {
-          half8 blo, bhi, alo = {}, ahi = {};
+          half8 blo, bhi;
           dq_unit_word(ud[i], d, blo, bhi);
-          if (on) {
-            const half8* ap = reinterpret_cast<const half8*>(hrow + u * UNIT + 16 * d);
-            alo = ap[0];
-            ahi = ap[1];
-          }
-          acc[i & 3] = mfma16(alo, blo, acc[i & 3]);
-          acc[i & 3] = mfma16(ahi, bhi, acc[i & 3]);
+          const half8* ap = reinterpret_cast<const half8*>(hrow + ua * UNIT + 16 * d);
+          acc[i & 3] = mfma16(ap[0], blo, acc[i & 3]);
+          acc[i & 3] = mfma16(ap[1], bhi, acc[i & 3]);
         }
       }
     }
-    if (lane < 16) ys[s][n] = ((acc[0][0] + acc[1][0]) + acc[2][0]) + acc[3][0];
+    // lane n (g = 0) holds C[0][n] in element 0 and C[1][n] in element 1
+    if (lane < 16) {
+      const int e = half;
+      const float y = ((acc[0][e] + acc[1][e]) + acc[2][e]) + acc[3][e];
+      const int s = half ? s1 : s0;
+      if (s >= 0) ys[s][n & 7] = y;
+    }
   }
   if (threadIdx.x < a.k) {  // (stored here: an earlier store would wait on the loads behind it)
     s_w[threadIdx.x] = w_r;
     s_slot[threadIdx.x] = slot_r;
   }
   __syncthreads();
-  if (threadIdx.x < 16) {
-    const float r_in = res ? res[row] : 0.0f;
-    float v = a.has_shared ? ys[a.k][n] : 0.0f;
+  if (threadIdx.x < kDcRows) {
+    const int t = threadIdx.x;
+    const int orow = blockIdx.x * kDcRows + t;
+    const float r_in = res ? res[orow] : 0.0f;
+    float v = a.has_shared ? ys[a.k][t] : 0.0f;
     for (int j0 = 0; j0 < a.k; j0 += 8) {  // the LDS reads of 8 ranks at a time, then their fmas in rank order
       float wj[8], yj[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int j = min(j0 + q, a.k - 1);
         wj[q] = s_w[j];
-        yj[q] = ys[s_slot[j]][n];
+        yj[q] = ys[s_slot[j]][t];
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         if (j0 + q < a.k) v = __builtin_fmaf(wj[q], yj[q], v);
     }
-    if (out) out[row] = v;
-    if (res) res[row] = r_in + v;
+    if (out) out[orow] = v;
+    if (res) res[orow] = r_in + v;
   }
 }
 
@@ -1284,8 +1320,9 @@ static hipError_t launch_decode1_q(const FfnArgs& a, const Decode1Sel& sel, floa
   }
   {
     const bool u64 = a.I % 64 == 0 && (!a.has_shared || a.Is % 64 == 0);
-    const int nw = std::min(slots, 12);  // within the kernel's 768-thread bound
-    const dim3 grid(unsigned(a.H / 16));
+    const int pairs = (a.k + 1) / 2 + (a.has_shared ? 1 : 0);
+    const int nw = std::min(pairs, 16);  // within the kernel's 1024-thread bound
+    const dim3 grid(unsigned(a.H / kDcRows));
     const int ldh = std::max(a.I, a.has_shared ? a.Is : 0) + 8;
     const size_t lds = size_t(slots) * ldh * sizeof(_Float16);
 #define DC(U_) \
