@@ -14,6 +14,48 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
+// Stable placement of one batch of up to 1024 pairs (one per thread of a
+// 1024-thread workgroup, pair order = thread order).  base[e] is the next
+// free position of expert e and is advanced past the batch's pairs.
+//   - Lanes of a wave holding the same expert find each other with one
+//     ballot per bit of the expert index; a pair's rank is the number of
+//     those lanes below it.
+//   - The 16 waves then take turns in order: wave w reads base[e], places its
+//     pairs at base[e] + rank, and the group's highest lane advances base[e]
+//     (its read of the same word is an earlier instruction of the same wave).
+// Returns the pair's position, or -1 for e < 0 (an id outside [0, E)).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int stable_place_1024(int e, int nbits, int* base) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint64_t same = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    same &= bit ? bal : ~bal;
+  }
+  const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
+  const bool last = (same >> lane) == 1ull;  // no higher lane of the group
+  const int cnt = __builtin_popcountll(same);
+  int pos = -1;
+  for (int w = 0; w < 16; ++w) {
+    if (wv == w && e >= 0) {
+      const int b = base[e];
+      pos = b + rank;
+      if (last) base[e] = b + cnt;
+    }
+    __syncthreads();
+  }
+  return pos;
+}
+
+// bits of an expert index below E
+__host__ __device__ __forceinline__ int expert_bits(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+// ---------------------------------------------------------------------------
 // Single-workgroup permutation for small batches (P <= kSmallPairs).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ idx, int P, int E,
@@ -24,7 +66,6 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __re
                                                             int32_t* __restrict__ header) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int tmp[1024];
-  __shared__ int s_e[1024];
   __shared__ int err;
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
@@ -45,36 +86,17 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __re
   }
   __syncthreads();
   // stable scatter, 1024 pairs at a time; cnt[e] is the running base
+  const int nbits = expert_bits(E);
   for (int p0 = 0; p0 < P; p0 += 1024) {
     const int p = p0 + tid;
-    const int n = min(1024, P - p0);
     int e = -1;
     if (p < P) {
       e = idx[p];
       if (e < 0 || e >= E) e = -1;
     }
-    s_e[tid] = e;
-    __syncthreads();
-    int before = 0, after = 0;
-    if (e >= 0) {
-      for (int j = 0; j < n; ++j) {
-        const int o = s_e[j];
-        before += (j < tid && o == e);
-        after += (j > tid && o == e);
-      }
-    }
-    int base = 0;
-    if (e >= 0) base = cnt[e];
-    __syncthreads();
-    if (e >= 0) {
-      const int pos = base + before;
-      sorted_pair[pos] = p;
-      pair_pos[p] = pos;
-      if (after == 0) cnt[e] = pos + 1;
-    } else if (p < P) {
-      pair_pos[p] = -1;
-    }
-    __syncthreads();
+    const int pos = stable_place_1024(e, nbits, cnt);
+    if (pos >= 0) sorted_pair[pos] = p;
+    if (p < P) pair_pos[p] = pos;
   }
 }
 
@@ -151,50 +173,26 @@ __global__ __launch_bounds__(1024) void offsets_scan_kernel(const int32_t* __res
   if (threadIdx.x == 0) offsets[E] = total;
 }
 
-__global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
-                                                             const int32_t* __restrict__ chunk_hist,
-                                                             const int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ sorted_pair,
-                                                             int32_t* __restrict__ pair_pos) {
+__global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                              const int32_t* __restrict__ chunk_hist,
+                                                              const int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_pair,
+                                                              int32_t* __restrict__ pair_pos) {
+  static_assert(kPermChunk == 1024, "one pair per thread");
   __shared__ int base[kMaxExperts];
-  __shared__ int s_e[256];
   const int tid = threadIdx.x;
   const int32_t* row = chunk_hist + int64_t(blockIdx.x) * (E + 1);
-  for (int e = tid; e < E; e += 256) base[e] = offsets[e] + row[e];
-  __syncthreads();
-  const int64_t c0 = int64_t(blockIdx.x) * kPermChunk;
-  for (int i0 = 0; i0 < kPermChunk; i0 += 256) {
-    const int64_t p = c0 + i0 + tid;
-    const int n = int(min<int64_t>(256, P - (c0 + i0)));
-    if (n <= 0) break;
-    int e = -1;
-    if (p < P) {
-      e = idx[p];
-      if (e < 0 || e >= E) e = -1;
-    }
-    s_e[tid] = e;
-    __syncthreads();
-    int before = 0, after = 0;
-    if (e >= 0) {
-      for (int j = 0; j < n; ++j) {
-        const int o = s_e[j];
-        before += (j < tid && o == e);
-        after += (j > tid && o == e);
-      }
-    }
-    int b = 0;
-    if (e >= 0) b = base[e];
-    __syncthreads();
-    if (e >= 0) {
-      const int pos = b + before;
-      sorted_pair[pos] = int32_t(p);
-      pair_pos[p] = pos;
-      if (after == 0) base[e] = pos + 1;
-    } else if (p < P) {
-      pair_pos[p] = -1;
-    }
-    __syncthreads();
+  const int64_t p = int64_t(blockIdx.x) * kPermChunk + tid;
+  int e = -1;
+  if (p < P) {
+    e = idx[p];
+    if (e < 0 || e >= E) e = -1;
   }
+  for (int i = tid; i < E; i += 1024) base[i] = offsets[i] + row[i];
+  __syncthreads();
+  const int pos = stable_place_1024(e, expert_bits(E), base);
+  if (pos >= 0) sorted_pair[pos] = int32_t(p);
+  if (p < P) pair_pos[p] = pos;
 }
 
 hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts, int32_t* offsets,
@@ -209,7 +207,7 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts,
   permute_hist_kernel<<<n_chunks, 256, 0, stream>>>(idx, P, E, chunk_hist);
   permute_colscan_kernel<<<(E + 1 + 63) / 64, 1024, 0, stream>>>(chunk_hist, n_chunks, E, counts, header);
   offsets_scan_kernel<<<1, 1024, 0, stream>>>(counts, E, offsets);
-  permute_scatter_kernel<<<n_chunks, 256, 0, stream>>>(idx, P, E, chunk_hist, offsets, sorted_pair, pair_pos);
+  permute_scatter_kernel<<<n_chunks, 1024, 0, stream>>>(idx, P, E, chunk_hist, offsets, sorted_pair, pair_pos);
   return hipGetLastError();
 }
 

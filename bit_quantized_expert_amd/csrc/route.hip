@@ -254,15 +254,17 @@ __global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* _
     off[q] = (row < kRtT ? min(row, t_last) : min(row - kRtT, e_last)) * H + pc * 8;
   }
   uint4v stg[NQ];
-  // step s of class c covers blocks b .. b + RK - 1 (those at or past the class end are zero)
+  // step s of class c covers blocks b .. b + RK - 1; pieces of blocks at or
+  // past the class end (or past K) read block 0 of their row instead and
+  // are never read back (the MFMA loop stops at the class end).  The raw
+  // loaded values go straight to the stores: a select on them would make
+  // the loads wait here instead of under the step's MFMAs.
   auto load_step = [&](int b, int cend) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int kb = b + (tid + 512 * q) % (4 * RK) / 4;
-      const bool in = kb < cend;
       const uint16_t* base = q < NQ / 2 ? xt : wt_;  // pieces q < NQ/2 are activation rows
-      const uint4v v = *reinterpret_cast<const uint4v*>(base + off[q] + (in ? b : 0) * 32);  // clamped, unconditional
-      stg[q] = in ? v : uint4v{0u, 0u, 0u, 0u};
+      stg[q] = *reinterpret_cast<const uint4v*>(base + off[q] + (kb < cend ? b : 0) * 32);  // clamped, unconditional
     }
   };
   auto store_step = [&]() {
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* _
           nb = ce;
           nce = min(nkb, ce + cl);
         }
-        if (nb < nkb) load_step(nb, nce);
+        load_step(nb < nkb ? nb : 0, nb < nkb ? nce : 0);  // after the last step: unused loads of block 0
       }
       const int nsub = min(RK, ce - b);
       for (int k = 0; k < nsub; ++k) {
@@ -378,7 +380,10 @@ hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_
 
 // ---------------------------------------------------------------------------
 // Top-k with ties to the lower expert index, then softmax over the selected
-// logits.  One wave per token; lane l holds experts l, l+64, l+128, ...
+// logits.  One wave per token, through the wave selection routines of
+// common.h (the k-th largest key by bisection on ballot counts, then the
+// ranking), so every path of the library selects the same experts with the
+// same weight bits.
 // ---------------------------------------------------------------------------
 template <int V>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
@@ -386,49 +391,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float val[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int e = lane + 64 * v;
-    val[v] = e < E ? logits[t * E + e] : -INFINITY;
-  }
-  uint64_t taken = 0;
-#pragma unroll
-  for (int v = 0; v < V; ++v)
-    if (lane + 64 * v >= E) taken |= 1ull << v;
-  float my_val = 0.0f;  // lane j keeps the j-th selection
-  int my_idx = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      if (!((taken >> v) & 1ull) && (bi == INT_MAX || val[v] > bv)) {
-        bv = val[v];
-        bi = lane + 64 * v;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (oi != INT_MAX && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi != INT_MAX && (bi & 63) == lane) taken |= 1ull << (bi >> 6);
-    if (lane == j) {
-      my_val = bv;
-      my_idx = bi;
-    }
-  }
-  const float top = __shfl(my_val, 0, 64);
-  const float p = lane < k ? expf(my_val - top) : 0.0f;
-  const float sum = wave_sum(p);
+  int my_idx;
+  float my_w;
+  wave_topk_softmax<V>(logits + t * E, E, k, my_idx, my_w);
   if (lane < k) {
     idx_out[t * k + lane] = my_idx;
-    w_out[t * k + lane] = p / sum;
+    w_out[t * k + lane] = my_w;
   }
 }
 
