@@ -38,8 +38,10 @@ __device__ __forceinline__ void rmsnorm_row(const float* __restrict__ res, int H
 // CPT float4 columns per thread per pass (all their loads in flight
 // together); with H / 4 <= 256 * CPT the row is one pass and the updated
 // residual stays in registers for the norm.  The pair slots and weights are
-// uniform loads (no LDS staging, no barrier before the row loads).
-template <int CPT>
+// uniform loads (no LDS staging, no barrier before the row loads).  JG pairs
+// are loaded per group (the launch picks JG >= k where it can, so no row is
+// loaded twice); RES: a residual row is read (only then).
+template <int CPT, int JG, bool RES>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ pos,
                                                      const float* __restrict__ w, const float* __restrict__ shared,
                                                      int H, int k, float* __restrict__ out, float* __restrict__ res,
@@ -59,29 +61,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     bool on[CPT];
     float4v acc[CPT], r[CPT];
     const float* srow = (shared ? shared : y) + t * H;
-    const float* rrow = (res ? res : y) + t * H;
+    const float* rrow = RES ? res + t * H : nullptr;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = c0 + 256 * u + int(threadIdx.x);
       on[u] = c < H4;
       cc[u] = on[u] ? c : 0;
       acc[u] = reinterpret_cast<const float4v*>(srow)[cc[u]];  // zeroed below when there is no shared expert
-      r[u] = reinterpret_cast<const float4v*>(rrow)[cc[u]];    // used only with res
+      if constexpr (RES) r[u] = reinterpret_cast<const float4v*>(rrow)[cc[u]];
     }
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      float4v v[8][CPT];
-      int pj[8];
-      float wj[8];
+    for (int j0 = 0; j0 < k; j0 += JG) {
+      float4v v[JG][CPT];
+      int pj[JG];
+      float wj[JG];
       // the slots and weights first (uniform loads), then every row load
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < JG; ++i) {
         const int j = min(j0 + i, k - 1);
         pj[i] = pt[j];
         wj[i] = wt[j];
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < JG; ++i)
 #pragma unroll
         for (int u = 0; u < CPT; ++u)
           v[i][u] = reinterpret_cast<const float4v*>(y + int64_t(pj[i] >= 0 ? pj[i] : 0) * H)[cc[u]];
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         for (int u = 0; u < CPT; ++u) acc[u] = float4v{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < JG; ++i)
         if (j0 + i < k && pj[i] >= 0)  // pairs of out-of-range ids (p < 0) add 0
 #pragma unroll
           for (int u = 0; u < CPT; ++u)
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int u = 0; u < CPT; ++u) {
       if (!on[u]) continue;
       if (out) reinterpret_cast<float4v*>(out + t * H)[cc[u]] = acc[u];
-      if (res) {
+      if constexpr (RES) {
         r[u] += acc[u];
         reinterpret_cast<float4v*>(res + t * H)[cc[u]] = r[u];
         ss += sumsq4(r[u]);
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
     }
   }
-  if (!res || !next_in) return;  // uniform across the workgroup
+  if (!RES || !next_in) return;  // uniform across the workgroup
   if (H4 > 256 * CPT) {
     rmsnorm_row(res + t * H, H, ss, red, next_in + t * H);
     return;
@@ -149,8 +151,17 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const 
                           const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
                           uint16_t* next_in, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  combine_kernel<2><<<dim3(unsigned(T)), 256, 0, stream>>>(y_sorted, pair_pos, topk_w, shared_out, H, k, out,
-                                                           residual, next_in);
+  const dim3 grid = dim3(unsigned(T));
+#define CB(JG_)                                                                                               \
+  (residual ? combine_kernel<2, JG_, true><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, shared_out, H, \
+                                                                     k, out, residual, next_in)                 \
+            : combine_kernel<2, JG_, false><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, shared_out, H, \
+                                                                      k, out, residual, next_in))
+  if (k <= 4) CB(4);
+  else if (k <= 8) CB(8);
+  else if (k <= 10) CB(10);
+  else CB(16);
+#undef CB
   return hipGetLastError();
 }
 

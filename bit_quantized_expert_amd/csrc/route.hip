@@ -216,8 +216,11 @@ constexpr size_t rt_lds() {
 
 // RK = K blocks (of 32) per step; OCC = waves per SIMD the registers are
 // budgeted for (RK = 2 fits 128 registers, 4 waves: two workgroups per CU;
-// RK = 4 halves the steps and barriers but needs the 256 of 2 waves).
-template <int RK, int OCC>
+// RK = 4 halves the steps and barriers but needs the 256 of 2 waves); PD =
+// steps whose loads are in flight during a step's MFMAs (register sets of
+// the staging ring: 2 fit beside RK = 4 in 256 registers, 1 beside RK = 2 in
+// 128, where the second workgroup of the CU covers the latency).
+template <int RK, int OCC, int PD>
 __global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
                                                             const uint16_t* __restrict__ w,
                                                             const float* __restrict__ bias, int E,
@@ -253,25 +256,36 @@ __global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* _
     const int p = tid + 512 * q, row = p / (4 * RK), pc = p % (4 * RK);
     off[q] = (row < kRtT ? min(row, t_last) : min(row - kRtT, e_last)) * H + pc * 8;
   }
-  uint4v stg[NQ];
-  // step s of class c covers blocks b .. b + RK - 1; pieces of blocks at or
-  // past the class end (or past K) read block 0 of their row instead and
-  // are never read back (the MFMA loop stops at the class end).  The raw
-  // loaded values go straight to the stores: a select on them would make
-  // the loads wait here instead of under the step's MFMAs.
-  auto load_step = [&](int b, int cend) {
+  // Steps: class c has sp = ceil(cl / RK) steps, step i of the tile is step
+  // i % sp of class i / sp and covers blocks b .. b + RK - 1 of it.  A ring
+  // of PD register sets keeps the loads of steps i + 1 .. i + PD in flight
+  // during step i's MFMAs.
+  const int sp = (cl + RK - 1) / RK;
+  const int n_cls = (nkb + cl - 1) / cl;  // non-empty classes (an empty class adds +0: S is never -0)
+  const int n_steps = n_cls * sp;
+  auto step_b = [&](int i) { return (i / sp) * cl + (i % sp) * RK; };
+  auto step_end = [&](int i) { return min(nkb, (i / sp) * cl + cl); };
+  uint4v stg[PD][NQ];
+  // pieces of blocks at or past the class end (or of a step past the last)
+  // read block 0 of their row instead and are never read back (the MFMA loop
+  // stops at the class end).  The raw loaded values go straight to the LDS
+  // stores: a select on them would make the loads wait here instead of under
+  // the MFMAs.
+  auto load_step = [&](uint4v (&st)[NQ], int i) {
+    const bool real = i < n_steps;
+    const int b = real ? step_b(i) : 0, cend = real ? step_end(i) : 0;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int kb = b + (tid + 512 * q) % (4 * RK) / 4;
       const uint16_t* base = q < NQ / 2 ? xt : wt_;  // pieces q < NQ/2 are activation rows
-      stg[q] = *reinterpret_cast<const uint4v*>(base + off[q] + (kb < cend ? b : 0) * 32);  // clamped, unconditional
+      st[q] = *reinterpret_cast<const uint4v*>(base + off[q] + (kb < cend ? b : 0) * 32);  // clamped, unconditional
     }
   };
-  auto store_step = [&]() {
+  auto store_step = [&](const uint4v (&st)[NQ]) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int p = tid + 512 * q, row = p / (4 * RK), pc = p % (4 * RK);
-      *reinterpret_cast<uint4v*>(rs + row * kPitch + pc * 8) = stg[q];
+      *reinterpret_cast<uint4v*>(rs + row * kPitch + pc * 8) = st[q];
     }
   };
 
@@ -280,49 +294,46 @@ __global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* _
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) S[i][j] = acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
-  const int n_cls = (nkb + cl - 1) / cl;  // non-empty classes (an empty class adds +0: S is never -0)
-  // the first step's loads
-  load_step(0, min(nkb, cl));
-  for (int c = 0; c < n_cls; ++c) {
-    const int cb = c * cl, ce = min(nkb, cb + cl);
-    for (int b = cb; b < ce; b += RK) {
-      __syncthreads();  // the previous step's fragments are read
-      store_step();
-      __syncthreads();
-      // the next step's loads (next block group of this class, or the next class's first)
-      {
-        int nb = b + RK, nce = ce;
-        if (nb >= ce) {
-          nb = ce;
-          nce = min(nkb, ce + cl);
-        }
-        load_step(nb < nkb ? nb : 0, nb < nkb ? nce : 0);  // after the last step: unused loads of block 0
-      }
-      const int nsub = min(RK, ce - b);
-      for (int k = 0; k < nsub; ++k) {
-        uint4v af[2], bf[4];
+  auto run_step = [&](uint4v (&st)[NQ], int i) {
+    __syncthreads();  // the previous step's fragments are read
+    store_step(st);
+    __syncthreads();
+    load_step(st, i + PD);  // the ring slot is free again: step i + PD's loads
+    const int b = step_b(i), nsub = min(RK, step_end(i) - b);
+    for (int k = 0; k < nsub; ++k) {
+      uint4v af[2], bf[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = *reinterpret_cast<const uint4v*>(rs + (32 * wt + 16 * i + n) * kPitch + k * 32 + 8 * g);
+      for (int i2 = 0; i2 < 2; ++i2)
+        af[i2] = *reinterpret_cast<const uint4v*>(rs + (32 * wt + 16 * i2 + n) * kPitch + k * 32 + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = *reinterpret_cast<const uint4v*>(rs + (kRtT + 64 * we + 16 * j + n) * kPitch + k * 32 + 8 * g);
+#pragma unroll
+      for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bf[j] = *reinterpret_cast<const uint4v*>(rs + (kRtT + 64 * we + 16 * j + n) * kPitch + k * 32 + 8 * g);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
-                                                                __builtin_bit_cast(bf16x8, bf[j]), acc[i][j], 0,
-                                                                0, 0);
-      }
+          acc[i2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i2]),
+                                                               __builtin_bit_cast(bf16x8, bf[j]), acc[i2][j], 0, 0, 0);
     }
+    if (i % sp == sp - 1) {  // the class is done: S += its chain
+      const int c = i / sp;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        S[i][j] = c == 0 ? acc[i][j] : S[i][j] + acc[i][j];
-        acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
-      }
+        for (int j = 0; j < 4; ++j) {
+          S[i2][j] = c == 0 ? acc[i2][j] : S[i2][j] + acc[i2][j];
+          acc[i2][j] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < PD; ++p) load_step(stg[p], p);
+  // whole ring turns: a step past the last one stages block 0 and runs no
+  // MFMA (its class fold adds +0), and every turn issues and waits for the
+  // ring slots in the same order, so the compiler's wait counts stay exact
+  for (int i = 0; i < n_steps; i += PD) {
+#pragma unroll
+    for (int p = 0; p < PD; ++p) run_step(stg[p], i + p);
   }
   // logits tile through LDS: S block (i, j) element r = token 32 wt + 16 i + 4 g + r, expert 64 we + 16 j + n
   __syncthreads();
@@ -361,10 +372,10 @@ hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_
     const int64_t total = (T + kRtT - 1) / kRtT * n_et;
     const int64_t grid = (total + 7) / 8 * 8;
     if (total >= 512)  // two resident workgroups per CU have work: the 128-register variant
-      router_gemm_kernel<2, 4><<<unsigned(grid), 512, rt_lds<2>(), stream>>>(x, T, H, w, bias, E, logits, n_et,
+      router_gemm_kernel<2, 4, 1><<<unsigned(grid), 512, rt_lds<2>(), stream>>>(x, T, H, w, bias, E, logits, n_et,
                                                                            total);
     else
-      router_gemm_kernel<4, 2><<<unsigned(grid), 512, rt_lds<4>(), stream>>>(x, T, H, w, bias, E, logits, n_et,
+      router_gemm_kernel<4, 2, 2><<<unsigned(grid), 512, rt_lds<4>(), stream>>>(x, T, H, w, bias, E, logits, n_et,
                                                                            total);
     return hipGetLastError();
   }
