@@ -40,12 +40,34 @@ __device__ __forceinline__ void rmsnorm_row(const float* __restrict__ res, int H
 // residual stays in registers for the norm.  The pair slots and weights are
 // uniform loads (no LDS staging, no barrier before the row loads).  JG pairs
 // are loaded per group (the launch picks JG >= k where it can, so no row is
-// loaded twice); RES: a residual row is read (only then).
-template <int CPT, int JG, bool RES>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ pos,
-                                                     const float* __restrict__ w, const float* __restrict__ shared,
-                                                     int H, int k, float* __restrict__ out, float* __restrict__ res,
-                                                     uint16_t* __restrict__ next_in) {
+// loaded twice); RES: a residual row is read (only then).  YT: the expert
+// rows are fp32, or fp16 (the grouped-GEMM layer, where these rows are most
+// of the layer's memory traffic); the sum is fp32 either way.  shared points
+// at [T][H] fp32 rows: the shared expert's output when has_shared, else any
+// readable rows (their values are replaced by 0; they may be out or res, so
+// the pointer is not restrict).
+template <typename YT>
+struct YRow;
+template <>
+struct YRow<float> {
+  typedef float4v raw;
+  static __device__ __forceinline__ float4v cvt(float4v v) { return v; }
+};
+template <>
+struct YRow<f16> {
+  typedef uint2v raw;  // four fp16
+  static __device__ __forceinline__ float4v cvt(uint2v v) {
+    const half2v a = as_half2(v[0]), b = as_half2(v[1]);
+    return float4v{float(a[0]), float(a[1]), float(b[0]), float(b[1])};
+  }
+};
+
+template <int CPT, int JG, bool RES, typename YT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ pos,
+                                                     const float* __restrict__ w, const float* shared,
+                                                     int has_shared, int H, int k, float* __restrict__ out,
+                                                     float* __restrict__ res, uint16_t* __restrict__ next_in) {
+  typedef typename YRow<YT>::raw Raw;
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const int32_t* pt = pos + t * k;
@@ -55,12 +77,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float4v rk[CPT];  // the updated residual of a one-pass row
   for (int c0 = 0; c0 < H4; c0 += 256 * CPT) {
     // every load unconditional (clamped columns and rows) so that they are in flight together:
-    // latency, not bandwidth, bounds a few tokens.  y has at least T rows, so row t of it stands in
-    // for a missing shared output; out-of-range pairs (p < 0) read row 0 and add 0.
+    // latency, not bandwidth, bounds a few tokens.  Out-of-range pairs (p < 0) read row 0 and add 0.
     int cc[CPT];
     bool on[CPT];
     float4v acc[CPT], r[CPT];
-    const float* srow = (shared ? shared : y) + t * H;
+    const float* srow = shared + t * H;
     const float* rrow = RES ? res + t * H : nullptr;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
@@ -71,7 +92,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       if constexpr (RES) r[u] = reinterpret_cast<const float4v*>(rrow)[cc[u]];
     }
     for (int j0 = 0; j0 < k; j0 += JG) {
-      float4v v[JG][CPT];
+      Raw v[JG][CPT];
       int pj[JG];
       float wj[JG];
       // the slots and weights first (uniform loads), then every row load
@@ -86,9 +107,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       for (int i = 0; i < JG; ++i)
 #pragma unroll
         for (int u = 0; u < CPT; ++u)
-          v[i][u] = reinterpret_cast<const float4v*>(y + int64_t(pj[i] >= 0 ? pj[i] : 0) * H)[cc[u]];
+          v[i][u] = reinterpret_cast<const Raw*>(y + int64_t(pj[i] >= 0 ? pj[i] : 0) * H)[cc[u]];
       __builtin_amdgcn_sched_barrier(0);
-      if (j0 == 0 && !shared) {
+      if (j0 == 0 && !has_shared) {
 #pragma unroll
         for (int u = 0; u < CPT; ++u) acc[u] = float4v{0.f, 0.f, 0.f, 0.f};
       }
@@ -96,9 +117,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       for (int i = 0; i < JG; ++i)
         if (j0 + i < k && pj[i] >= 0)  // pairs of out-of-range ids (p < 0) add 0
 #pragma unroll
-          for (int u = 0; u < CPT; ++u)
+          for (int u = 0; u < CPT; ++u) {
+            const float4v vf = YRow<YT>::cvt(v[i][u]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[u][q] = __builtin_fmaf(wj[i], v[i][u][q], acc[u][q]);
+            for (int q = 0; q < 4; ++q) acc[u][q] = __builtin_fmaf(wj[i], vf[q], acc[u][q]);
+          }
     }
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
@@ -147,22 +170,38 @@ hipError_t launch_residual_rmsnorm(const float* res, int64_t T, int H, uint16_t*
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
-                          const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
-                          uint16_t* next_in, hipStream_t stream) {
+template <typename YT>
+static hipError_t launch_combine_t(const YT* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                                   const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
+                                   uint16_t* next_in, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const dim3 grid = dim3(unsigned(T));
-#define CB(JG_)                                                                                               \
-  (residual ? combine_kernel<2, JG_, true><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, shared_out, H, \
-                                                                     k, out, residual, next_in)                 \
-            : combine_kernel<2, JG_, false><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, shared_out, H, \
-                                                                      k, out, residual, next_in))
+  // rows standing in for a missing shared output: out or residual ([T][H] fp32, one is non-null)
+  const float* sh = shared_out ? shared_out : (out ? out : residual);
+  const int has_sh = shared_out != nullptr;
+#define CB(JG_)                                                                                              \
+  (residual ? combine_kernel<2, JG_, true, YT><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, sh, has_sh, \
+                                                                         H, k, out, residual, next_in)          \
+            : combine_kernel<2, JG_, false, YT><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, sh, has_sh, \
+                                                                          H, k, out, residual, next_in))
   if (k <= 4) CB(4);
   else if (k <= 8) CB(8);
   else if (k <= 10) CB(10);
   else CB(16);
 #undef CB
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                          const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
+                          uint16_t* next_in, hipStream_t stream) {
+  return launch_combine_t<float>(y_sorted, pair_pos, topk_w, shared_out, T, H, k, out, residual, next_in, stream);
+}
+
+hipError_t launch_combine_f16y(const _Float16* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                               const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
+                               uint16_t* next_in, hipStream_t stream) {
+  return launch_combine_t<f16>(y_sorted, pair_pos, topk_w, shared_out, T, H, k, out, residual, next_in, stream);
 }
 
 }  // namespace moe

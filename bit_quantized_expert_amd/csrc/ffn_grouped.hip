@@ -10,7 +10,8 @@
 //
 //   gate/up : [BM x H] activations x [H x 256 gate + 256 up rows] -> SwiGLU
 //             epilogue -> h (fp16, the permuted column order of the GEMV path)
-//   down    : [BM x I] h x [I x 512 down rows] -> y_sorted / shared_out (fp32)
+//   down    : [BM x I] h x [I x 512 down rows] -> y_sorted / shared_out (fp32;
+//             routed rows in fp16 when the caller asks for y_sorted_h)
 //
 // The activations keep the permuted 16-group k order the dequantiser
 // produces (pairs (i, i+8)), so codes unpack straight into their slots.  The
@@ -334,6 +335,11 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
           f16* hout = shared ? a.h_shared + int64_t(m0 + m) * hw : a.h_routed + int64_t(lo + m0 + m) * hw;
           hout[hcol(gr)] = f16(hv);
         }
+      } else if (!shared && a.y_sorted_h) {  // routed rows in fp16
+        f16* yrow = a.y_sorted_h + int64_t(lo + m0 + m) * H;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (bok[j]) yrow[brow[j]] = f16(acc[i][j][q]);
       } else {
         float* yrow = shared ? a.shared_out + int64_t(m0 + m) * H : a.y_sorted + int64_t(lo + m0 + m) * H;
 #pragma unroll

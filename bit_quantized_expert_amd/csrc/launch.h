@@ -42,6 +42,8 @@ struct FfnArgs {
                                //   permuted within groups of 16 (MFMA operand order)
   _Float16* h_shared;          // [T][Is]
   float* y_sorted;             // [P][H]
+  _Float16* y_sorted_h;        // grouped GEMM: when non-null, the routed down output
+                               //   goes here in fp16 instead of y_sorted
   float* shared_out;           // [T][H] or null
 };
 
@@ -103,5 +105,9 @@ hipError_t launch_residual_rmsnorm(const float* res, int64_t T, int H, uint16_t*
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                           const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
                           uint16_t* next_in, hipStream_t stream);
+// The same combine over fp16 expert rows (the grouped-GEMM layer's y_sorted_h).
+hipError_t launch_combine_f16y(const _Float16* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                               const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
+                               uint16_t* next_in, hipStream_t stream);
 
 }  // namespace moe
