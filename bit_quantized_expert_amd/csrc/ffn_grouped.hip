@@ -26,8 +26,13 @@
 
 namespace moe {
 
+// Waves per workgroup: 8 (BM x 512 tiles, one workgroup per CU) with 128-row
+// tiles; 4 (BM x 256, two workgroups per CU, so that one's prologue and
+// epilogue overlap the other's MFMAs) with the 96-row tiles of short segments
+// (measured on the 3-bit 4,096-token layer: gate/up -2%, down -8%; with
+// 128-row tiles 4 waves were no faster).
 #ifndef MOE_GROUPED2_WAVES
-#define MOE_GROUPED2_WAVES 8
+#define MOE_GROUPED2_WAVES(BM) ((BM) == 96 ? 4 : 8)
 #endif
 #ifndef MOE_GROUPED2_PD
 #define MOE_GROUPED2_PD 1
@@ -105,15 +110,20 @@ struct BRaw2 {
   uint32_t v;      // bit b: block 2h + b exists (else its scale reads as 0 in dq_b2)
 };
 
-// K64: K is a multiple of 64 (even block count per row), so a lane's two
+// KM >= 1: K is a multiple of 64 (even block count per row), so a lane's two
 // blocks are in or out together and its 16 code bytes, 4 scale bytes (and
 // 8 high-plane bytes) are aligned for single loads.
-template <int QBITS, bool K64>
+// A half step (K % 128 == 64, the last step: blocks 4 step and 4 step + 1
+// only) is loaded by both lanes of a column from the first block: lane h then
+// dequantises block 4 step + h alone (dq_b2 with sel), and the step runs half
+// the MFMAs.
+template <int QBITS, int KM>
 __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, const uint16_t* scales, int rows,
                                         int K, int row, int step, int h, bool ok) {
-  if constexpr (K64) {
+  if constexpr (KM >= 1) {
     const int nb = K / 32;
-    const int b0 = 4 * step + 2 * h;
+    const bool half_step = KM == 2 && 4 * step + 2 >= nb;  // only blocks 4 step, 4 step + 1 (K % 128 == 64)
+    const int b0 = 4 * step + (half_step ? 0 : 2 * h);
     const bool in = ok && b0 < nb;
     const int rr = in ? row : 0, bb = in ? b0 : 0;
     const QTile tl = qtile<true>(rr, rows);  // tiled layout (common.h); weight rows are multiples of 32
@@ -151,21 +161,28 @@ __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, c
   r.v = (in0 ? 1u : 0u) | (in1 ? 2u : 0u);
 }
 
-// word q (0..3) of a lane's step -> the two permuted k-slices
+// word q (0..3) of a lane's step -> the two permuted k-slices.  sel (half
+// steps, lane h = 1, q < 2): word q of the second block instead (block
+// 4 step + 1).
 template <int QBITS>
-__device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, half8& lo, half8& hi) {
-  const uint32_t sraw = q < 2 ? (r.s & 0xffffu) : (r.s >> 16);
+__device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, half8& lo, half8& hi) {
+  const bool second = q >= 2 || sel;  // the lane's second block
+  const uint32_t sraw = second ? (r.s >> 16) : (r.s & 0xffffu);
   const uint32_t sbits = (r.v >> (q >> 1)) & 1u ? sraw : 0u;  // blocks past K: scale 0, weights 0
   const half2v s2 = as_half2(sbits | (sbits << 16));
+  const uint32_t w = q < 2 && sel ? r.c[q + 2] : r.c[q];
   if constexpr (QBITS == 2) {
-    dq2_word(r.c[q], s2, lo, hi);
+    dq2_word(w, s2, lo, hi);
   } else {
-    const uint32_t hbits = (r.hb[q >> 1] >> (16 * (q & 1))) & 0xffffu;
-    dq3_word(r.c[q], spread16(hbits), s2, lo, hi);
+    const uint32_t hbits = (r.hb[second ? 1 : 0] >> (16 * (q & 1))) & 0xffffu;
+    dq3_word(w, spread16(hbits), s2, lo, hi);
   }
 }
 
-template <int QBITS, typename AT, bool GATEUP, int NWV, int PD, bool K64, int BM>
+// KM: 0 = any K (a multiple of 32), 1 = K a multiple of 64, 2 = K a multiple
+// of 64 that may end in a half step (K % 128 == 64; the checks and selects of
+// half steps cost VALU in every step, so only this instantiation has them).
+template <int QBITS, typename AT, bool GATEUP, int NWV, int PD, int KM, int BM>
 __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void grouped_gemm2_kernel(FfnArgs a,
                                                                                                  int n_ntiles) {
   static_assert(BM % 32 == 0 && BM <= 128, "whole 32-row MFMA tiles");
@@ -279,7 +296,7 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
 #pragma unroll
   for (int p = 0; p < PD; ++p)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) load_b2<QBITS, K64>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], p, h, bok[j]);
+    for (int j = 0; j < 2; ++j) load_b2<QBITS, KM>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], p, h, bok[j]);
   store_a(ar, As[0]);
   __syncthreads();
   for (int s0 = 0; s0 < nsteps; s0 += PD) {
@@ -293,17 +310,23 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
       // (the scheduler would otherwise sink them to their use)
       __builtin_amdgcn_sched_barrier(0);
       const f16* Ab = As[cur];
+      // half step (K % 128 == 64, the last step): lane h holds block 4 step + h, A columns
+      // 32h .. 32h + 31, and words 2, 3 (k-steps 4 .. 7) are not run
+      const bool half_step = KM == 2 && 4 * step + 2 >= K / 32;
+      const bool sel = half_step && h;
+      const int acol = (half_step ? 32 : 64) * h;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // word q of each lane's step: k-steps 2q (lo) and 2q + 1 (hi)
+        if (q >= 2 && half_step) break;
         half8 blo[2], bhi[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bring[p][j], q, blo[j], bhi[j]);
+        for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bring[p][j], q, sel, blo[j], bhi[j]);
 #pragma unroll
         for (int half_ = 0; half_ < 2; ++half_) {
           half8 af[MI];
 #pragma unroll
           for (int i = 0; i < MI; ++i)
-            af[i] = *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + 64 * h + 16 * q + 8 * half_);
+            af[i] = *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + acol + 16 * q + 8 * half_);
 #pragma unroll
           for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -312,7 +335,7 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        load_b2<QBITS, K64>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], step + PD, h, bok[j]);
+        load_b2<QBITS, KM>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], step + PD, h, bok[j]);
       store_a(ar, As[cur ^ 1]);  // (after the last step: a buffer nobody reads any more)
       __syncthreads();
     }
@@ -352,23 +375,28 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
 
 template <int QBITS, typename XT, int BM>
 static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases) {
-  constexpr int W = MOE_GROUPED2_WAVES, PD = MOE_GROUPED2_PD;
+  constexpr int W = MOE_GROUPED2_WAVES(BM), PD = MOE_GROUPED2_PD;
   if (phases & kPhaseGateUp) {
     const int rows = std::max(a.I, a.has_shared ? a.Is : 0);
     const int nn = (rows + 32 * W - 1) / (32 * W);
     const int64_t total = max_tiles * nn;
     const unsigned grid = unsigned((total + 7) / 8 * 8);
-    if (a.H % 64 == 0) grouped_gemm2_kernel<QBITS, XT, true, W, PD, true, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
-    else grouped_gemm2_kernel<QBITS, XT, true, W, PD, false, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    if (a.H % 128 == 0) grouped_gemm2_kernel<QBITS, XT, true, W, PD, 1, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    else if (a.H % 64 == 0) grouped_gemm2_kernel<QBITS, XT, true, W, PD, 2, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    else grouped_gemm2_kernel<QBITS, XT, true, W, PD, 0, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
   }
   if (phases & kPhaseDown) {
     const int nn = (a.H + 64 * W - 1) / (64 * W);
     const int64_t total = max_tiles * nn;
     const unsigned grid = unsigned((total + 7) / 8 * 8);
-    if (a.I % 64 == 0 && (!a.has_shared || a.Is % 64 == 0))
-      grouped_gemm2_kernel<QBITS, f16, false, W, PD, true, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    const bool k64 = a.I % 64 == 0 && (!a.has_shared || a.Is % 64 == 0);
+    const bool k128 = a.I % 128 == 0 && (!a.has_shared || a.Is % 128 == 0);
+    if (k128)
+      grouped_gemm2_kernel<QBITS, f16, false, W, PD, 1, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    else if (k64)
+      grouped_gemm2_kernel<QBITS, f16, false, W, PD, 2, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
     else
-      grouped_gemm2_kernel<QBITS, f16, false, W, PD, false, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+      grouped_gemm2_kernel<QBITS, f16, false, W, PD, 0, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
   }
   return hipGetLastError();
 }

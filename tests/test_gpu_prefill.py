@@ -61,6 +61,11 @@ RAGGED = [
     # several tiles with a ragged last one
     ("b1", 128, 96, 16, 2, 64, 2, 700, torch.bfloat16),
     ("b2", 256, 192, 24, 3, 0, 3, 680, torch.float32),
+    # K a multiple of 128 in both projections (no half step), and hidden % 128 == 64 (a half
+    # step in gate/up)
+    ("k1", 128, 256, 6, 2, 128, 2, 300, torch.bfloat16),
+    ("k2", 256, 128, 9, 3, 0, 3, 333, torch.float32),
+    ("k3", 320, 128, 5, 2, 256, 3, 250, torch.bfloat16),
     # the largest expert count and top-k (4096, 32)
     ("m3", 64, 32, 4096, 32, 32, 2, 40, torch.bfloat16),
 ]
