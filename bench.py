@@ -228,6 +228,51 @@ def ffn_flops(s, T) -> tuple[int, int]:
     return gu, dn
 
 
+def decode_stack_bench(wl, s, layers, dev, log, steps):
+    """wl.tokens tokens through the resident layers as a stack (residual +
+    RMSNorm + bf16 glue between layers), captured as one HIP graph; the
+    algorithmic bytes count each layer's distinct experts once."""
+    T, L = wl.tokens, len(layers)
+    r = torch.empty(T, s.hidden, device=dev)
+    a = torch.empty(T, s.hidden, dtype=torch.bfloat16, device=dev)
+    x0 = synth.tokens(wl, dev).float()
+    ws = M.alloc_workspace(s, T, device=dev)
+    idx = torch.empty(L, T, s.top_k, dtype=torch.int32, device=dev)
+
+    def stack_pass():
+        r.copy_(x0)
+        M.rmsnorm_bf16(r, a)
+        for l in range(L):
+            M.layer_forward(a, layers[l], s, residual=r, next_in=a, topk_idx=idx[l], ws=ws)
+
+    stack_pass()
+    torch.cuda.synchronize()
+    r_eager = r.clone()
+    uniq = [int(torch.unique(idx[l]).numel()) for l in range(L)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stack_pass()
+    g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(r, r_eager):
+        raise SystemExit(f"{wl.name} stack graph replay differs from the eager stack")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    router_bytes = s.n_experts * s.hidden * 2
+    nbytes = sum(u * expert_bytes(s) + shared_bytes(s) + router_bytes for u in uniq)
+    log(f"{wl.name} stack: {ms:.3f} ms/step, {T / ms * 1e3:.0f} tok/s, {nbytes / ms / 1e6:.0f} GB/s, "
+        f"unique experts/layer {np.mean(uniq):.1f}")
+    return {"tokens": T, "tokens_per_s": T / ms * 1e3, "ms_per_step": ms, "layers": L,
+            "achieved_GBs": nbytes / ms / 1e6, "hbm_frac": nbytes / ms / 1e6 / HBM_PEAK_GBS,
+            "unique_experts_per_layer": float(np.mean(uniq))}
+
+
 def prefill_bench(wl, layer, dev, log, reps=5):
     """One prefill layer (T tokens through route, permute, grouped-GEMM FFN,
     combine), and the grouped gate/up and down kernels launched alone."""
@@ -447,41 +492,10 @@ def main():
     # kernel streams all 512 experts (+ the shared one) of a layer
     probe = probe_gemv(s, layers, dev, log)
 
-    # secondary: 16-token decode through the 48-layer stack, also as one graph
-    T16 = 16
-    r = torch.empty(T16, s.hidden, device=dev)
-    a = torch.empty(T16, s.hidden, dtype=torch.bfloat16, device=dev)
-    x16 = synth.tokens(synth.WORKLOADS["decode16"], dev).float()
-    ws16 = M.alloc_workspace(s, T16, device=dev)
-    idx16 = torch.empty(L, T16, s.top_k, dtype=torch.int32, device=dev)
-
-    def stack_pass():
-        r.copy_(x16)
-        M.rmsnorm_bf16(r, a)
-        for l in range(L):
-            M.layer_forward(a, layers[l], s, residual=r, next_in=a, topk_idx=idx16[l], ws=ws16)
-
-    stack_pass()
-    torch.cuda.synchronize()
-    r_eager = r.clone()
-    uniq = [int(torch.unique(idx16[l]).numel()) for l in range(L)]
-    g16 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g16):
-        stack_pass()
-    g16.replay()
-    torch.cuda.synchronize()
-    if not torch.equal(r, r_eager):
-        raise SystemExit("stack graph replay differs from the eager stack")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.stack_steps):
-        g16.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    stack_ms = e0.elapsed_time(e1) / args.stack_steps
-    stack_bytes = sum(u * expert_bytes(s) + shared_bytes(s) + router_bytes for u in uniq)
-    log(f"decode16 stack: {stack_ms:.3f} ms/step, {T16 / stack_ms * 1e3:.0f} tok/s, "
-        f"{stack_bytes / stack_ms / 1e6:.0f} GB/s, unique experts/layer {np.mean(uniq):.1f}")
+    # secondary: 16-token decode, and the 4-token verify window (the token plus three drafts),
+    # through the 48-layer stack, each as one graph
+    stack16 = decode_stack_bench(synth.WORKLOADS["decode16"], s, layers, dev, log, args.stack_steps)
+    stack4 = decode_stack_bench(synth.WORKLOADS["verify4"], s, layers, dev, log, args.stack_steps)
 
     # secondary: prefill workloads on the grouped-GEMM path
     prefill = prefill_bench(synth.WORKLOADS["prefill"], layers[0], dev, log)
@@ -522,10 +536,7 @@ def main():
                      "probe": probe},
         "cpu_baseline": cpu,
         "secondary": {"prefill32k_layer": prefill, "prefill3_4k_stack": prefill3,
-                      "decode16_stack": {"tokens_per_s": T16 / stack_ms * 1e3, "ms_per_step": stack_ms,
-                                         "layers": args.layers, "achieved_GBs": stack_bytes / stack_ms / 1e6,
-                                         "hbm_frac": stack_bytes / stack_ms / 1e6 / HBM_PEAK_GBS,
-                                         "unique_experts_per_layer": float(np.mean(uniq))}},
+                      "decode16_stack": stack16, "verify4_stack": stack4},
     }
     print(json.dumps(res), flush=True)
 

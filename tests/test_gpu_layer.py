@@ -199,15 +199,16 @@ def test_zero_tokens_is_a_noop():
     M.layer_forward(x, dl.q, dl.s, out=out, ws=None)
 
 
-def test_decode16_stack_teacher_forced():
-    """Three stacked layers of the 16-token decode workload through the fused
-    residual + RMSNorm + bf16 glue.  Each layer is checked against the oracle
+@pytest.mark.parametrize("name", ["decode16", "verify4"])
+def test_decode_stack_teacher_forced(name):
+    """Three stacked layers of the 16-token decode workload (and of the
+    4-token verify window) through the fused residual + RMSNorm + bf16 glue.  Each layer is checked against the oracle
     fed the GPU's own bf16 activation (teacher forcing); the residual update is
     exact fp32 addition; the next activation matches the oracle's RMSNorm +
     bf16 rounding of the GPU residual except at rounding boundaries."""
     from oracle import moe_oracle as O
     M = _M()
-    wl = synth.WORKLOADS["decode16"]
+    wl = synth.WORKLOADS[name]
     s = wl.shape
     T = wl.tokens
     x0 = synth.tokens(wl, "cuda").float()
