@@ -11,6 +11,7 @@
 
 #include "../../include/moe.h"
 #include "launch.h"
+#include "select.h"
 
 namespace {
 
@@ -162,10 +163,18 @@ moe::QMat qmat(const moe_qweights& q, int m) { return moe::QMat{q.codes[m], q.sc
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-moe_algo pick_algo(const moe_options* o, int64_t T) {
+moe_algo pick_algo(const moe_options* o, int64_t T, const moe_shape* s) {
   const moe_algo a = o ? o->ffn_algo : MOE_ALGO_AUTO;
   if (a != MOE_ALGO_AUTO) return a;
-  return T <= 16 ? MOE_ALGO_GEMV : MOE_ALGO_GROUPED;
+  return T <= 16 && moe::gemv_lds_ok(T, s->hidden, s->inter, s->shared_inter) ? MOE_ALGO_GEMV : MOE_ALGO_GROUPED;
+}
+
+int check_algo(moe_algo algo, int64_t T, const moe_shape* s) {
+  if (algo == MOE_ALGO_GEMV && !moe::gemv_lds_ok(T, s->hidden, s->inter, s->shared_inter))
+    return fail(MOE_ERR_UNSUPPORTED, "the GEMV kernels stage min(T, 16) token rows of hidden=%d and inter=%d in LDS, "
+                "which does not fit at T=%lld; use MOE_ALGO_GROUPED", s->hidden, std::max(s->inter, s->shared_inter),
+                (long long)T);
+  return MOE_OK;
 }
 
 int check_opts(const moe_options* o, bool ffn_flags_ok = false) {
@@ -274,12 +283,20 @@ hipError_t fused_decode(const void* x, moe_dtype xd, int64_t T, const moe_layer*
   int32_t* pair_pos = at<int32_t>(ws, W.pair_pos);
   float* y = at<float>(ws, W.y_sorted);
   float* s_out = s->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;
-  e = moe::launch_select_small(logits, int(T), s->n_experts, s->top_k, s_out != nullptr, idx, w,
-                               at<int32_t>(ws, W.counts), offsets, sorted_pair, pair_pos, at<int32_t>(ws, W.header),
-                               at<int4>(ws, W.slots), st);
-  if (e != hipSuccess) return e;
   moe::FfnArgs a = ffn_args(x, xd, T, L, s, offsets, sorted_pair, y, s_out, ws, W);
-  e = moe::launch_ffn_gemv(a, st, moe::kPhaseGateUp | moe::kPhaseDown);
+  const moe::SelOut so{logits, idx, w, at<int32_t>(ws, W.counts), offsets, sorted_pair, pair_pos,
+                       at<int32_t>(ws, W.header), at<int4>(ws, W.slots)};
+  // the gate/up kernel makes the selection itself where it can, else a selection launch first
+  e = moe::launch_gateup_select(a, so, st);
+  if (e == hipErrorNotSupported) {
+    e = moe::launch_select_small(logits, int(T), s->n_experts, s->top_k, s_out != nullptr, idx, w,
+                                 at<int32_t>(ws, W.counts), offsets, sorted_pair, pair_pos,
+                                 at<int32_t>(ws, W.header), at<int4>(ws, W.slots), st);
+    if (e != hipSuccess) return e;
+    e = moe::launch_ffn_gemv(a, st, moe::kPhaseGateUp);
+  }
+  if (e != hipSuccess) return e;
+  e = moe::launch_ffn_gemv(a, st, moe::kPhaseDown);
   if (e != hipSuccess) return e;
   return moe::launch_combine(y, pair_pos, w, s_out, T, s->hidden, s->top_k, out, residual, next_in, st);
 }
@@ -388,8 +405,10 @@ int moe_expert_ffn(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer*
       return fail(MOE_ERR_INVALID_ARG, "x, y_sorted and shared_out must be 16-byte aligned");
     const WsLayout W = ws_layout(*shape, T);
     if (int r = check_ws(workspace, workspace_bytes, W.end_ffn)) return r;
-    return device_status(do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y_sorted, shared_out,
-                                pick_algo(opts, T), workspace, W, as_stream(stream), opts ? opts->flags : 0),
+    const moe_algo algo = pick_algo(opts, T, shape);
+    if (int r = check_algo(algo, T, shape)) return r;
+    return device_status(do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y_sorted, shared_out, algo,
+                                workspace, W, as_stream(stream), opts ? opts->flags : 0),
                          "moe_expert_ffn");
   } catch (...) {
     return fail(MOE_ERR_DEVICE, "moe_expert_ffn: unexpected exception");
@@ -437,7 +456,8 @@ int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_lay
     void* ws = workspace;
     int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, W.topk_idx);
     float* w = topk_w ? topk_w : at<float>(ws, W.topk_w);
-    const moe_algo algo = pick_algo(opts, T);
+    const moe_algo algo = pick_algo(opts, T, shape);
+    if (int r = check_algo(algo, T, shape)) return r;
     if (decode1_ok(T, shape, algo))
       return device_status(decode1(x, x_dtype, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st),
                            "moe_layer_forward");

@@ -348,12 +348,14 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive scan of vals[0..n) in LDS by a 1024-thread workgroup with two
+// Exclusive scan of vals[0..n) in LDS by an NT-thread workgroup with two
 // barriers: each wave scans a contiguous run, then the wave totals.  `tmp`
-// holds 16 ints.  Returns the total.  n <= 4096.
+// holds NT / 64 ints.  Returns the total.  n <= 4 NT.
+template <int NT = 1024>
 __device__ inline int block_scan_fast(int* vals, int n, int* tmp) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int per = (n + 1023) / 1024;  // values per thread, <= 4
+  const int per = (n + NT - 1) / NT;  // values per thread, <= 4
   int local[4], s = 0;
   for (int i = 0; i < per; ++i) {
     const int idx = threadIdx.x * per + i;
@@ -364,7 +366,7 @@ __device__ inline int block_scan_fast(int* vals, int n, int* tmp) {
   if (lane == 63) tmp[wv] = incl;
   __syncthreads();
   int base = 0, total = 0;
-  for (int w = 0; w < 16; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int t = tmp[w];
     base += w < wv ? t : 0;
     total += t;
@@ -541,38 +543,47 @@ __device__ __forceinline__ int wave_nth_selected(const uint64_t (&msel)[V], int 
 // or equal key and lower index), and lane j < k returns the rank-j expert,
 // its logit (a -0 logit comes back as +0, which changes no weight) and its
 // position in index order.
+// tk: this wave's LDS scratch (index order / rank order).
 template <int V>
-__device__ __forceinline__ void wave_rank(const WaveKeys<V>& K, const uint64_t (&msel)[V], int k, float& my_val,
-                                          int& my_idx, int& my_slot) {
-  __shared__ uint2 tk_s[16][2][kMaxTopKLds];  // per wave of the workgroup: index order / rank order
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+__device__ __forceinline__ void wave_rank_s(const WaveKeys<V>& K, const uint64_t (&msel)[V], int k,
+                                            uint2 (&tk)[2][kMaxTopKLds], float& my_val, int& my_idx,
+                                            int& my_slot) {
+  const int lane = threadIdx.x & 63;
   int base = 0;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const uint64_t m = msel[v];
-    if ((m >> lane) & 1ull) tk_s[wv][0][base + bits_below(m)] = uint2{K.key[v], uint32_t(lane + 64 * v)};
+    if ((m >> lane) & 1ull) tk[0][base + bits_below(m)] = uint2{K.key[v], uint32_t(lane + 64 * v)};
     base += __builtin_popcountll(m);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < k) {
-    const uint2 me = tk_s[wv][0][lane];
+    const uint2 me = tk[0][lane];
     int rank = 0;
     for (int i = 0; i < k; ++i) {
-      const uint2 o = tk_s[wv][0][i];
+      const uint2 o = tk[0][i];
       rank += (o.x > me.x || (o.x == me.x && i < lane)) ? 1 : 0;
     }
-    tk_s[wv][1][rank] = uint2{me.x, me.y | (uint32_t(lane) << 16)};  // expert < 2^16, slot in the high half
+    tk[1][rank] = uint2{me.x, me.y | (uint32_t(lane) << 16)};  // expert < 2^16, slot in the high half
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   uint2 out = uint2{0u, 0u};
-  if (lane < k) out = tk_s[wv][1][lane];
+  if (lane < k) out = tk[1][lane];
   my_val = key_float(out.x);
   my_idx = int(out.y & 0xffffu);
   my_slot = int(out.y >> 16);
+}
+
+// The same with a scratch of the workgroup's (at most 16) waves.
+template <int V>
+__device__ __forceinline__ void wave_rank(const WaveKeys<V>& K, const uint64_t (&msel)[V], int k, float& my_val,
+                                          int& my_idx, int& my_slot) {
+  __shared__ uint2 tk_s[16][2][kMaxTopKLds];
+  wave_rank_s<V>(K, msel, k, tk_s[threadIdx.x >> 6], my_val, my_idx, my_slot);
 }
 
 // Renormalised softmax weight of rank `lane` (lane < k):

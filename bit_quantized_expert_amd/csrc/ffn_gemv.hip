@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace moe {
 
@@ -828,21 +829,94 @@ __global__ __launch_bounds__(128 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(F
 // Requires H % (16 UNIT) == 0 (whole pipeline groups per item) and Is = I or
 // no shared expert (one item size).
 // ---------------------------------------------------------------------------
-template <int QBITS, int UNIT, typename XT>
+//
+// SEL: the selection is made here, from the router logits, by every
+// workgroup (the experts of each token, the slot table in LDS); the last
+// workgroup also writes it out (topk_idx / topk_w, the permutation, the slot table and
+// header for the down kernel and the combine).  E <= kSelPersMaxExperts.
+// Otherwise the slot table and header come from a selection launch.
+constexpr int kSelPersMaxExperts = 512;
+
+template <int QBITS, int UNIT, typename XT, bool SEL>
 __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_rb, int G,
                                                                const int4* __restrict__ slots,
-                                                               const int32_t* __restrict__ header) {
+                                                               const int32_t* __restrict__ header, SelOut so) {
   // slots / header are a.slots / a.header, read-only here: scalar loads,
   // which wait on their own counter instead of behind the weight loads
   constexpr int NW = 4, D = 4, kThreads = 512;
   extern __shared__ __attribute__((aligned(16))) f16 xs[];  // [T][H + 8]
-  __shared__ float4v up_x[NW][64];
+  // the up sums of the item loop; before it, the ranking scratch of the selection
+  __shared__ union {
+    float4v up_x[NW][64];
+    SelRankLds tk[8];
+  } ux;
+  float4v(&up_x)[NW][64] = ux.up_x;
+  __shared__ SelLds<SEL ? kSelPersMaxExperts : 1, SEL ? 8 : 1> sel;
   const int H = a.H, ldsw = H + 8, T = int(a.T);
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int wr = wv % NW, mat = wv / NW;
   const int n = lane & 15, g = lane >> 4;
   const int n_units = H / UNIT, rounds = n_units / 4;  // a multiple of D (host-checked)
-  const int n_items = header[kHdrValid] * n_rb;
+  // Token staging into LDS (fp16, permuted 16-groups; row = token id):
+  // item i of a pass is chunk i % chunks of the (i / chunks)-th token of umask.
+  const XT* xsrc = static_cast<const XT*>(a.x);
+  const int chunks = H / 16;
+  constexpr int NB = sizeof(XT) == 4 ? 2 : 4;
+  auto stage_load = [&](uint32_t umask, int items, int base, Raw16<XT>(&raw)[NB], int(&dst)[NB]) {
+#pragma unroll
+    for (int k2 = 0; k2 < NB; ++k2) {
+      const int it = min(base + k2 * kThreads + int(threadIdx.x), items - 1);
+      const int r = it / chunks, gg = it - r * chunks;
+      uint32_t mm = umask;  // token of rank r: the r-th set bit
+      for (int k3 = 0; k3 < r; ++k3) mm &= mm - 1u;
+      const int tok = __builtin_ctz(mm);
+      load_raw16(xsrc + int64_t(tok) * H + gg * 16, raw[k2]);
+      dst[k2] = tok * ldsw + gg * 16;
+    }
+  };
+  auto stage_store = [&](int items, int base, const Raw16<XT>(&raw)[NB], const int(&dst)[NB]) {
+#pragma unroll
+    for (int k2 = 0; k2 < NB; ++k2) {
+      if (base + k2 * kThreads + int(threadIdx.x) < items) {
+        half8 lo, hi;
+        cvt_raw16(raw[k2], lo, hi);
+        half8* d = reinterpret_cast<half8*>(xs + dst[k2]);
+        d[0] = lo;
+        d[1] = hi;
+      }
+    }
+  };
+  // SEL: every token is staged, and the first pass's loads are issued before
+  // the selection (they do not depend on it), so their latency is hidden
+  Raw16<XT> raw0[NB];
+  int dst0[NB];
+  if constexpr (SEL) stage_load(uint32_t((1ull << T) - 1u), T * chunks, 0, raw0, dst0);
+
+  int n_active = 0, n_valid;
+  if constexpr (SEL) {
+    // the last workgroup writes the selection out: it has the fewest items
+    // (none when there are fewer items than workgroups), so the ranks and
+    // writes stay off the other workgroups' path
+    n_active = select_in_workgroup<kSelPersMaxExperts / 64, 8, kSelPersMaxExperts>(
+        so, T, a.E, a.k, a.has_shared, sel, ux.tk, blockIdx.x == gridDim.x - 1);
+    n_valid = n_active + (a.has_shared ? 1 : 0);
+  } else {
+    n_valid = header[kHdrValid];
+  }
+  // slot s of the table: {expert or -1 (shared), first sorted position, tokens, token mask}
+  auto slot_at = [&](int s) -> int4 {
+    if constexpr (SEL) {
+      if (s < n_active) {
+        const int e = sel.slot_e[s];
+        const uint32_t m = sel.tmask[e];
+        return int4{e, sel.cnt[e] & 0xffff, __builtin_popcount(m), int(m)};
+      }
+      return s == n_active && a.has_shared ? int4{-1, 0, T, int((1u << T) - 1u)} : int4{0, 0, 0, 0};
+    } else {
+      return slots[s];
+    }
+  };
+  const int n_items = n_valid * n_rb;
   const int q = n_items / G, rem = n_items - q * G, b = blockIdx.x;
   const int it0 = b * q + min(b, rem), it1 = it0 + q + (b < rem ? 1 : 0);
   if (it0 >= it1) return;
@@ -860,7 +934,7 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
     wsc = Mq.scales + ex * Mq.scale_stride;
   };
 
-  int4 si_cur = slots[it0 / n_rb];
+  int4 si_cur = slot_at(it0 / n_rb);
   const uint8_t* c_wc;
   const uint16_t* c_wsc;
   int c_rows, c_row;
@@ -872,37 +946,24 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
   Unit<QBITS, UNIT> uw[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) load_unit(uw[i], c_wc, c_wsc, c_rows, H, min(c_row, c_rows - 1), i * 4 + g);
-  // the tokens of this workgroup's slots into LDS (fp16, permuted 16-groups;
-  // row = token id): the union of the slots' token masks
+  // the tokens into LDS: with SEL all of them (the first pass is loaded),
+  // else the union of the workgroup's slots' token masks
   {
-    uint32_t umask = 0u;
-    for (int sl = it0 / n_rb; sl <= (it1 - 1) / n_rb; ++sl) umask |= uint32_t(slots[sl].w);
-    const XT* x = static_cast<const XT*>(a.x);
-    const int chunks = H / 16, items = __builtin_popcount(umask) * chunks;
-    constexpr int NB = sizeof(XT) == 4 ? 2 : 4;
-    for (int base = 0; base < items; base += NB * kThreads) {
+    uint32_t umask = uint32_t((1ull << T) - 1u);
+    int base0 = 0;
+    if constexpr (SEL) {
+      stage_store(T * chunks, 0, raw0, dst0);
+      base0 = NB * kThreads;
+    } else {
+      umask = 0u;
+      for (int sl = it0 / n_rb; sl <= (it1 - 1) / n_rb; ++sl) umask |= uint32_t(slot_at(sl).w);
+    }
+    const int items = __builtin_popcount(umask) * chunks;
+    for (int base = base0; base < items; base += NB * kThreads) {
       Raw16<XT> raw[NB];
       int dst[NB];
-#pragma unroll
-      for (int k2 = 0; k2 < NB; ++k2) {
-        const int it = min(base + k2 * kThreads + int(threadIdx.x), items - 1);
-        const int r = it / chunks, gg = it - r * chunks;
-        uint32_t mm = umask;  // token of rank r: the r-th set bit
-        for (int k3 = 0; k3 < r; ++k3) mm &= mm - 1u;
-        const int tok = __builtin_ctz(mm);
-        load_raw16(x + int64_t(tok) * H + gg * 16, raw[k2]);
-        dst[k2] = tok * ldsw + gg * 16;
-      }
-#pragma unroll
-      for (int k2 = 0; k2 < NB; ++k2) {
-        if (base + k2 * kThreads + int(threadIdx.x) < items) {
-          half8 lo, hi;
-          cvt_raw16(raw[k2], lo, hi);
-          half8* d = reinterpret_cast<half8*>(xs + dst[k2]);
-          d[0] = lo;
-          d[1] = hi;
-        }
-      }
+      stage_load(umask, items, base, raw, dst);
+      stage_store(items, base, raw, dst);
     }
   }
   __syncthreads();
@@ -913,7 +974,7 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
 
   for (int it = it0; it < it1; ++it) {
     const bool has_next = it + 1 < it1;
-    const int4 si_next = slots[min(it + 1, it1 - 1) / n_rb];  // requested now, read at round rounds - D
+    const int4 si_next = slot_at(min(it + 1, it1 - 1) / n_rb);  // requested now, read at round rounds - D
     const bool shared = si_cur.x < 0;
     const int mnow = si_cur.z;
     // this lane's MFMA row: the slot's min(n, mnow - 1)-th token
@@ -1254,9 +1315,11 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
         const int G = int(std::min<int64_t>(kPersGrid, int64_t(slots) * n_rb));
         const size_t lds_p = size_t(a.T) * (a.H + 8) * sizeof(f16);
         if (a.x_bf16)
-          gemv_gateup_pers_kernel<QBITS, 64, uint16_t><<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header);
+          gemv_gateup_pers_kernel<QBITS, 64, uint16_t, false>
+              <<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header, SelOut{});
         else
-          gemv_gateup_pers_kernel<QBITS, 64, float><<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header);
+          gemv_gateup_pers_kernel<QBITS, 64, float, false>
+              <<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header, SelOut{});
       } else {
         const dim3 grid(unsigned((max_rows + 16 * NW - 1) / (16 * NW)), unsigned(slots));
 #define GU(U_, X_) gemv_gateup_tp_kernel<QBITS, U_, X_, NW><<<grid, 128 * NW, lds, stream>>>(a)
@@ -1297,6 +1360,39 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
     }
   }
   return hipGetLastError();
+}
+
+// The persistent gate/up kernel with the selection made inside it (see
+// gemv_gateup_pers_kernel), for a 2..16-token layer whose shape the kernel
+// takes; hipErrorNotSupported otherwise (then the caller launches the
+// selection kernel and launch_ffn_gemv).
+hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t stream) {
+  const int64_t P = a.T * a.k;
+  const size_t lds_p = size_t(a.T) * (a.H + 8) * sizeof(f16);
+  const bool ok = MOE_GEMV_PERS && a.T >= 2 && a.T <= kGemvMaxM && a.H % 1024 == 0 &&
+                  (!a.has_shared || a.Is == a.I) && a.E <= kSelPersMaxExperts && P <= 1024 &&
+                  lds_p + 16384 <= kLdsBytes;
+  if (!ok) return hipErrorNotSupported;
+  const int slots = int(std::min<int64_t>(a.E, P)) + (a.has_shared ? 1 : 0);
+  const int n_rb = (a.I + 63) / 64;
+  const int G = int(std::min<int64_t>(kPersGrid, int64_t(slots) * n_rb));
+#define GS(Q_, X_) gemv_gateup_pers_kernel<Q_, 64, X_, true><<<G, 512, lds_p, stream>>>(a, n_rb, G, nullptr, nullptr, so)
+  if (a.qbits == 2) {
+    if (a.x_bf16) GS(2, uint16_t);
+    else GS(2, float);
+  } else {
+    if (a.x_bf16) GS(3, uint16_t);
+    else GS(3, float);
+  }
+#undef GS
+  return hipGetLastError();
+}
+
+bool gemv_lds_ok(int64_t T, int H, int I, int Is) {
+  if (T <= 1) return true;
+  const size_t m = size_t(std::min<int64_t>(T, kGemvMaxM));
+  const size_t kmax = size_t(std::max(I, Is));
+  return m * (H + 8) * sizeof(f16) + 16384 <= kLdsBytes && m * (kmax + 8) * sizeof(f16) + 16384 <= kLdsBytes;
 }
 
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases) {

@@ -12,6 +12,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kSmallPairs = 2048;   // single-workgroup permutation up to this many pairs
 constexpr int kPermChunk = 1024;    // pairs per workgroup in the multi-workgroup permutation
 constexpr int kGemvMaxM = 16;       // tokens per MFMA tile in the decode kernels
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of a CU (the most one workgroup can have)
 
 // Workspace header (int32 words at the start of the workspace).
 enum HeaderWord { kHdrError = 0, kHdrActive = 1, kHdrTiles = 2, kHdrValid = 3, kHdrWords = 64 };
@@ -80,6 +81,13 @@ hipError_t launch_select_small(const float* logits, int T, int E, int k, int has
 // Routed + shared expert FFN on the decode kernels: h then y_sorted / shared_out.
 enum { kPhaseGateUp = 1, kPhaseDown = 2 };
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases);
+// The decode kernels stage up to 16 tokens of H (gate/up) or max(I, Is)
+// (down) fp16 values per row in LDS: whether that fits for T tokens.
+bool gemv_lds_ok(int64_t T, int H, int I, int Is);
+// 2..16-token gate/up with the selection made in the kernel (select.h),
+// when the shape allows it (else hipErrorNotSupported, nothing launched).
+struct SelOut;
+hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t stream);
 // Grouped-GEMM expert FFN over the tile list of launch_plan, built with
 // tile_bm = grouped_tile_rows(T, k, E) (96 or 128) and launched with the same
 // bm; max_tiles bounds the list for the launch grid.
