@@ -102,6 +102,17 @@ def test_validation_before_any_device_call():
     assert lib.moe_permute(fake, 4096, ctypes.byref(s), fake, fake, fake, fake, fake, 16, None) \
         == L.MOE_ERR_WORKSPACE
     assert lib.moe_read_error(None, 0, None) == L.MOE_ERR_INVALID_ARG
+    # the GEMV kernels stage up to 16 token rows of `hidden` in LDS: asked for explicitly where that
+    # does not fit (hidden 8192 at 16 tokens), the call is refused before any device work
+    big = _shape(hidden=8192)
+    lay_big = _layer_struct()
+    for q in (lay_big.experts, lay_big.shared):
+        q.code_stride = 3 * 704 * 8192 // 4
+        q.scale_stride = 3 * 704 * 8192 // 32
+    o_gemv = L.Options(1, 0)
+    assert lib.moe_layer_forward(fake, 1, 16, ctypes.byref(lay_big), ctypes.byref(big), fake, None, None, None, None,
+                                 ctypes.byref(o_gemv), fake, 1 << 40, None) == L.MOE_ERR_UNSUPPORTED
+    assert "LDS" in L.last_error_detail()
 
 
 @pytest.mark.parametrize("rows,K,qbits", [(3, 32, 2), (17, 96, 3), (40, 64, 2), (33, 160, 3), (64, 704, 2)])
