@@ -54,6 +54,12 @@ import numpy as np
 #   3-bit: planar.  First a low plane laid out exactly like the 2-bit codes
 #          (low two bits of q), then a high plane [rows][K/8] bytes with bit 2
 #          of q for weight k in byte k//8 at bit k%8.
+#   4-bit: planar.  The low plane as for 3-bit, then a second plane in the
+#          same 2-bit layout holding bits 2..3 of q ([rows][K/4] bytes).  The
+#          pages' quantisation ladder tops out at a 4-bit file ("Strata serves
+#          a 125B MoE at 94 tokens/s ...", section "Quality is a sizing
+#          decision"; "How Strata runs a 125-billion-parameter model ...",
+#          benchmark table, the R9700 row); they give no bit layout for it.
 #   scales: fp16 [rows][K/32], row-major.
 # ---------------------------------------------------------------------------
 
@@ -74,8 +80,8 @@ def matrix_code_bytes(rows: int, k: int, qbits: int) -> int:
 
 
 def _check_shape(rows: int, k: int, qbits: int) -> None:
-    if qbits not in (2, 3):
-        raise ValueError(f"qbits must be 2 or 3, got {qbits}")
+    if qbits not in (2, 3, 4):
+        raise ValueError(f"qbits must be 2, 3 or 4, got {qbits}")
     if k % BLOCK != 0:
         raise ValueError(f"K={k} must be a multiple of {BLOCK}")
     if rows < 0:
@@ -87,10 +93,15 @@ def pack_codes(q: np.ndarray, qbits: int) -> np.ndarray:
     q = np.asarray(q, dtype=np.uint8)
     rows, k = q.shape
     _check_shape(rows, k, qbits)
-    lo = (q & 3).reshape(rows, k // 4, 4).astype(np.uint16)
-    lo_bytes = (lo[..., 0] | (lo[..., 1] << 2) | (lo[..., 2] << 4) | (lo[..., 3] << 6)).astype(np.uint8)
+    def plane2(v):  # two bits per weight, four weights per byte, weight k at bits 2 (k % 4)
+        v = v.reshape(rows, k // 4, 4).astype(np.uint16)
+        return (v[..., 0] | (v[..., 1] << 2) | (v[..., 2] << 4) | (v[..., 3] << 6)).astype(np.uint8)
+
+    lo_bytes = plane2(q & 3)
     if qbits == 2:
         return lo_bytes.reshape(-1)
+    if qbits == 4:
+        return np.concatenate([lo_bytes.reshape(-1), plane2((q >> 2) & 3).reshape(-1)])
     hi = ((q >> 2) & 1).reshape(rows, k // 8, 8).astype(np.uint16)
     hi_bytes = np.zeros((rows, k // 8), dtype=np.uint16)
     for bit in range(8):
@@ -103,10 +114,16 @@ def unpack_codes(codes: np.ndarray, rows: int, k: int, qbits: int) -> np.ndarray
     _check_shape(rows, k, qbits)
     codes = np.asarray(codes, dtype=np.uint8).reshape(-1)
     n_lo = rows * k // 4
-    lo_bytes = codes[:n_lo].reshape(rows, k // 4)
-    lo = np.stack([(lo_bytes >> (2 * i)) & 3 for i in range(4)], axis=-1).reshape(rows, k)
+
+    def plane2(b):
+        b = b.reshape(rows, k // 4)
+        return np.stack([(b >> (2 * i)) & 3 for i in range(4)], axis=-1).reshape(rows, k)
+
+    lo = plane2(codes[:n_lo])
     if qbits == 2:
         return lo.astype(np.uint8)
+    if qbits == 4:
+        return (lo | (plane2(codes[n_lo:2 * n_lo]) << 2)).astype(np.uint8)
     hi_bytes = codes[n_lo:n_lo + rows * k // 8].reshape(rows, k // 8)
     hi = np.stack([(hi_bytes >> i) & 1 for i in range(8)], axis=-1).reshape(rows, k)
     return (lo | (hi << 2)).astype(np.uint8)

@@ -44,6 +44,9 @@ def _py_code(codes: bytes, rows, k, qbits, r, c):
     if qbits == 3:
         hi_byte = codes[rows * k // 4 + r * (k // 8) + c // 8]
         q |= ((hi_byte >> (c % 8)) & 1) << 2
+    if qbits == 4:
+        hi_byte = codes[rows * k // 4 + r * (k // 4) + c // 4]
+        q |= ((hi_byte >> (2 * (c % 4))) & 3) << 2
     return q
 
 
@@ -97,7 +100,7 @@ def _tiny_layer(seed=0, hidden=64, inter=32, n_experts=8, shared_inter=32, qbits
 
 # ---------------------------------------------------------------- format
 
-@pytest.mark.parametrize("qbits", [2, 3])
+@pytest.mark.parametrize("qbits", [2, 3, 4])
 def test_quant_block_hand_example(qbits):
     g = _read_kv(os.path.join(GOLDEN, "quant_block.txt"))
     w = np.zeros((1, 32), dtype=np.float32)
@@ -114,7 +117,7 @@ def test_quant_block_hand_example(qbits):
     assert list(deq) == [c * s for c in want_c]
 
 
-@pytest.mark.parametrize("qbits", [2, 3])
+@pytest.mark.parametrize("qbits", [2, 3, 4])
 def test_pack_unpack_bit_layout_brute_force(qbits):
     rng = np.random.default_rng(1)
     rows, k = 5, 96
@@ -133,7 +136,7 @@ def test_pack_unpack_bit_layout_brute_force(qbits):
             assert un[r, c] == _py_code(bytes(rnd), rows, k, qbits, r, c)
 
 
-@pytest.mark.parametrize("qbits", [2, 3])
+@pytest.mark.parametrize("qbits", [2, 3, 4])
 def test_dequant_closed_form_brute_force(qbits):
     rng = np.random.default_rng(2)
     rows, k = 3, 64
@@ -144,7 +147,7 @@ def test_dequant_closed_form_brute_force(qbits):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("qbits", [2, 3])
+@pytest.mark.parametrize("qbits", [2, 3, 4])
 def test_quantize_properties(qbits):
     rng = np.random.default_rng(3)
     rows, k = 64, 256
@@ -294,17 +297,18 @@ def test_combine_one_hot_and_linear():
     assert np.allclose(b, 2 * a, rtol=1e-14, atol=0)
 
 
-def test_layer_brute_force_tiny():
+@pytest.mark.parametrize("qbits", [2, 4])
+def test_layer_brute_force_tiny(qbits):
     """Whole layer on the tiny workload shape versus pure-Python loops that
     re-derive every step from the definition (bit extraction, loops, sort,
     math.exp) -- relative error <= 1e-12."""
-    w_r, b, experts, shared = _tiny_layer(seed=13, bias=True)
+    w_r, b, experts, shared = _tiny_layer(seed=13, bias=True, qbits=qbits)
     rng = np.random.default_rng(14)
     x = rng.normal(size=(4, 64)).astype(np.float32)
     got = O.layer_forward(x, w_r, b, experts, shared, 2)
 
     def deq(m, rows, k):
-        return _py_dequant(m[0], m[1], rows, k, 2)
+        return _py_dequant(m[0], m[1], rows, k, qbits)
 
     dense = [(deq(e.gate, 32, 64), deq(e.up, 32, 64), deq(e.down, 64, 32)) for e in experts]
     sdense = (deq(shared.gate, 32, 64), deq(shared.up, 32, 64), deq(shared.down, 64, 32))
