@@ -180,9 +180,9 @@ class QArena:
         if self.qbits == 2:
             quantize(w.view(n * rows, k), 2, self.codes[m][lo:lo + n], self.scales[m][lo:lo + n], stream=stream)
         else:
-            # the 3-bit planes are per matrix, so each expert is one call
+            # the 3- and 4-bit planes are per matrix, so each expert is one call
             for i in range(n):
-                quantize(w[i], 3, self.codes[m][lo + i], self.scales[m][lo + i], stream=stream)
+                quantize(w[i], self.qbits, self.codes[m][lo + i], self.scales[m][lo + i], stream=stream)
 
     def bytes(self) -> int:
         return sum(c.numel() for c in self.codes) + 2 * sum(s.numel() for s in self.scales)

@@ -115,7 +115,7 @@ int check_shape(const moe_shape* s) {
     return fail(MOE_ERR_INVALID_ARG, "n_experts=%d must be in [1, %d]", s->n_experts, moe::kMaxExperts);
   if (s->top_k < 1 || s->top_k > std::min(s->n_experts, moe::kMaxTopK))
     return fail(MOE_ERR_INVALID_ARG, "top_k=%d must be in [1, min(n_experts, %d)]", s->top_k, moe::kMaxTopK);
-  if (s->qbits != 2 && s->qbits != 3) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2 and 3 are supported", s->qbits);
+  if (s->qbits < 2 || s->qbits > 4) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2, 3 and 4 are supported", s->qbits);
   return MOE_OK;
 }
 
@@ -498,7 +498,7 @@ int moe_rmsnorm_bf16(const float* r, int64_t T, int32_t H, uint16_t* a, void* st
 
 int moe_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int32_t cols, int32_t qbits, float* out,
                 void* stream) {
-  if (qbits != 2 && qbits != 3) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2 and 3 are supported", qbits);
+  if (qbits < 2 || qbits > 4) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2, 3 and 4 are supported", qbits);
   if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "rows=%lld cols=%d: cols must be a positive multiple of 32", (long long)rows, cols);
   if (rows == 0) return ok();
   if (!codes || !scales || !out) return fail(MOE_ERR_INVALID_ARG, "codes, scales and out must be non-NULL");
@@ -509,7 +509,7 @@ int moe_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int3
 
 int moe_quantize(const float* w, int64_t rows, int32_t cols, int32_t qbits, uint8_t* codes, uint16_t* scales,
                  void* stream) {
-  if (qbits != 2 && qbits != 3) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2 and 3 are supported", qbits);
+  if (qbits < 2 || qbits > 4) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2, 3 and 4 are supported", qbits);
   if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "rows=%lld cols=%d: cols must be a positive multiple of 32", (long long)rows, cols);
   if (rows == 0) return ok();
   if (!codes || !scales || !w) return fail(MOE_ERR_INVALID_ARG, "w, codes and scales must be non-NULL");

@@ -114,7 +114,9 @@ __host__ __device__ __forceinline__ int64_t qt_scale_off(const QTile& t, int K, 
   return u < nuf ? base + int64_t(u) * t.gsz * 2 + t.rr * 2 + (blk & 1) : base + int64_t(nuf) * t.gsz * 2 + t.rr;
 }
 
-// Byte offset (in the high plane) of the 4 high-plane bytes of block blk.
+// (4-bit: the high plane has the low plane's layout, so qt_code_off places
+// its bytes too, from the plane's start.)
+// Byte offset (in the 3-bit high plane) of the 4 high-plane bytes of block blk.
 __host__ __device__ __forceinline__ int64_t qt_high_off(const QTile& t, int K, int blk) {
   const int nuf = K / 64, u = blk >> 1;
   const int64_t base = t.g0 * (K / 8);
@@ -191,7 +193,8 @@ __device__ __forceinline__ uint32_t spread16(uint32_t h) {
 // sp = spread16(high bits) holds bit 2 of code i at bit 2i.  Pairs 0..3 use
 // M_0..M_3 with the high bits moved to 2i+2 (sp << 2; bits up to 2i+2 <= 8
 // stay inside the mantissa); pairs 4..7 use w >> 8 and sp >> 6 with M_0..M_3
-// (shifting right keeps bit 30, the high bit of code 15).  c = q - 4.
+// (shifting right keeps bit 30, the high bit of code 15).  c = q - 4; c * s
+// rounds to fp16 for |c| = 3 (relative error <= 2^-11 per weight).
 __device__ __forceinline__ void dq3_word(uint32_t w, uint32_t sp, half2v s2, half8& lo, half8& hi) {
   const uint32_t w8 = w >> 8, hs = sp << 2, h8 = sp >> 6;
   half2v p[8];
@@ -202,6 +205,31 @@ __device__ __forceinline__ void dq3_word(uint32_t w, uint32_t sp, half2v s2, hal
     const uint32_t hsrc = i < 4 ? hs : h8;
     const uint32_t v = and_or_v(src, 0x00030003u << (2 * j), and_or(hsrc, 0x00040004u << (2 * j), magic_bits(j)));
     const f16 off = magic_val(j) + f16(4.0f);
+    half2v h = as_half2(v) - half2v{off, off};
+    p[i] = h * s2;
+  }
+  lo = half8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  hi = half8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+}
+
+// 4-bit variant: wl holds the low two bits of 16 codes and wh the high two
+// bits, both in the 2-bit layout.  Pairs 0..3 use M_0..M_3 with the high bits
+// moved to 2i+2 .. 2i+3 (wh << 2; bits up to 2i+3 <= 9 stay inside the
+// mantissa, whose bit 2i has weight 1, so the half holds M_i + q, q <= 15);
+// pairs 4..7 use wl >> 8 and wh >> 6 with M_0..M_3.  c = q - 8.  Bits that
+// the shifts carry across the half boundary fall outside the masks.
+// Unlike the 2-bit case, c * s rounds to fp16 where |c| is not a power of two
+// (as in the 3-bit case: relative error <= 2^-11 per weight).
+__device__ __forceinline__ void dq4_word(uint32_t wl, uint32_t wh, half2v s2, half8& lo, half8& hi) {
+  const uint32_t w8 = wl >> 8, hs = wh << 2, h8 = wh >> 6;
+  half2v p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = i < 4 ? i : i - 4;
+    const uint32_t src = i < 4 ? wl : w8;
+    const uint32_t hsrc = i < 4 ? hs : h8;
+    const uint32_t v = and_or_v(src, 0x00030003u << (2 * j), and_or(hsrc, 0x000C000Cu << (2 * j), magic_bits(j)));
+    const f16 off = magic_val(j) + f16(8.0f);
     half2v h = as_half2(v) - half2v{off, off};
     p[i] = h * s2;
   }

@@ -12,7 +12,7 @@
 // runs v_mfma_f32_16x16x32_f16.  Lane (n = l%16, g = l/16) streams row n:
 // in round r it loads the 64-weight unit u = 4r + g (16 bytes of 2-bit codes,
 // a 128-bit load), so the 4 lanes of a row read 64 contiguous bytes per
-// round.  Codes are unpacked in registers to exact fp16 c*s (see dq2_word);
+// round.  Codes are unpacked in registers to fp16 c*s (exact at 2 bits; see dq2_word);
 // the activations sit in LDS as fp16 in the matching permuted order.  One
 // workgroup = 4 waves = 64 rows of one expert (or of the shared expert).
 #include <algorithm>
@@ -101,12 +101,13 @@ hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared,
 }
 
 // One quantised unit of a row: UNIT = 64 weights (16 code bytes, 2 scales)
-// or 32 (8 code bytes, 1 scale).  3-bit adds UNIT/32 high-plane words.
+// or 32 (8 code bytes, 1 scale).  3-bit adds UNIT/32 high-plane words (one
+// bit per code), 4-bit UNIT/16 (two bits per code, the low plane's layout).
 template <int QBITS, int UNIT>
 struct Unit {
-  uint32_t w[UNIT / 16];  // low-plane words, 16 codes each
-  uint32_t h[UNIT / 32];  // high-plane words, 32 codes each (3-bit only)
-  uint32_t s;             // fp16 scale bits (two for UNIT = 64)
+  uint32_t w[UNIT / 16];                               // low-plane words, 16 codes each
+  uint32_t h[QBITS == 4 ? UNIT / 16 : UNIT / 32];      // high-plane words (3- and 4-bit only)
+  uint32_t s;                                          // fp16 scale bits (two for UNIT = 64)
 };
 
 // Unit u of row `row` of a matrix of `rows` rows in the tiled layout of
@@ -136,6 +137,16 @@ __device__ __forceinline__ void load_unit(Unit<QBITS, UNIT>& U, const uint8_t* c
       U.h[0] = *reinterpret_cast<const uint32_t*>(hp);
     }
   }
+  if constexpr (QBITS == 4) {
+    const uint8_t* hp = codes + int64_t(rows) * (K / 4) + qt_code_off(tl, K, blk);
+    if constexpr (UNIT == 64) {
+      const uint4v hv = *reinterpret_cast<const uint4v*>(hp);
+      U.h[0] = hv[0]; U.h[1] = hv[1]; U.h[2] = hv[2]; U.h[3] = hv[3];
+    } else {
+      const uint2v hv = *reinterpret_cast<const uint2v*>(hp);
+      U.h[0] = hv[0]; U.h[1] = hv[1];
+    }
+  }
 }
 
 template <int QBITS, int UNIT>
@@ -143,7 +154,7 @@ __device__ __forceinline__ void zero_unit(Unit<QBITS, UNIT>& U) {
 #pragma unroll
   for (int i = 0; i < UNIT / 16; ++i) U.w[i] = 0;
 #pragma unroll
-  for (int i = 0; i < UNIT / 32; ++i) U.h[i] = 0;
+  for (int i = 0; i < int(sizeof(U.h) / sizeof(U.h[0])); ++i) U.h[i] = 0;
   U.s = 0;  // zero scale: every dequantised weight is 0
 }
 
@@ -154,6 +165,8 @@ __device__ __forceinline__ void dq_unit_word(const Unit<QBITS, UNIT>& U, int d, 
   const half2v s2 = as_half2(sbits | (sbits << 16));
   if constexpr (QBITS == 2) {
     dq2_word(U.w[d], s2, lo, hi);
+  } else if constexpr (QBITS == 4) {
+    dq4_word(U.w[d], U.h[d], s2, lo, hi);
   } else {
     const uint32_t hb = (U.h[d >> 1] >> (16 * (d & 1))) & 0xffffu;
     dq3_word(U.w[d], spread16(hb), s2, lo, hi);
@@ -1380,9 +1393,12 @@ hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t 
   if (a.qbits == 2) {
     if (a.x_bf16) GS(2, uint16_t);
     else GS(2, float);
-  } else {
+  } else if (a.qbits == 3) {
     if (a.x_bf16) GS(3, uint16_t);
     else GS(3, float);
+  } else {
+    if (a.x_bf16) GS(4, uint16_t);
+    else GS(4, float);
   }
 #undef GS
   return hipGetLastError();
@@ -1397,7 +1413,9 @@ bool gemv_lds_ok(int64_t T, int H, int I, int Is) {
 
 hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases) {
   if (a.T == 0) return hipSuccess;
-  return a.qbits == 2 ? launch_gemv_q<2>(a, stream, phases) : launch_gemv_q<3>(a, stream, phases);
+  return a.qbits == 2 ? launch_gemv_q<2>(a, stream, phases)
+         : a.qbits == 3 ? launch_gemv_q<3>(a, stream, phases)
+                        : launch_gemv_q<4>(a, stream, phases);
 }
 
 template <int QBITS>
@@ -1433,7 +1451,9 @@ static hipError_t launch_decode1_q(const FfnArgs& a, const Decode1Sel& sel, floa
 
 hipError_t launch_decode1_ffn(const FfnArgs& a, const Decode1Sel& sel, float* out, float* res, hipStream_t stream) {
   if (a.E > kDecode1MaxExperts || a.T != 1) return hipErrorInvalidValue;
-  return a.qbits == 2 ? launch_decode1_q<2>(a, sel, out, res, stream) : launch_decode1_q<3>(a, sel, out, res, stream);
+  return a.qbits == 2   ? launch_decode1_q<2>(a, sel, out, res, stream)
+         : a.qbits == 3 ? launch_decode1_q<3>(a, sel, out, res, stream)
+                        : launch_decode1_q<4>(a, sel, out, res, stream);
 }
 
 }  // namespace moe

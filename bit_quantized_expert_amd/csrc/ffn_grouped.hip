@@ -1,6 +1,6 @@
 // Expert FFN for prefill-sized batches: a grouped GEMM over the device-built
 // tile list, fp16 MFMA (v_mfma_f32_32x32x16_f16) with fp32 accumulation, the
-// 2/3-bit weights dequantised in registers straight into MFMA operands.
+// 2/3/4-bit weights dequantised in registers straight into MFMA operands.
 //
 // The experts are computed from their quantised storage ("How Strata runs a
 // 125-billion-parameter model ...", intro and Step 1 byte table); with many
@@ -104,10 +104,10 @@ constexpr int kBK2 = 128, kLDA2 = kBK2 + 8;  // A row pitch in halves
 
 template <int QBITS>
 struct BRaw2 {
-  uint4v c;        // 16 code bytes: words 4h .. 4h+3
-  uint32_t s;      // two fp16 scales: blocks 2h, 2h + 1
-  uint32_t hb[2];  // 3-bit: high-plane bits of the 64 codes
-  uint32_t v;      // bit b: block 2h + b exists (else its scale reads as 0 in dq_b2)
+  uint4v c;                    // 16 code bytes: words 4h .. 4h+3
+  uint32_t s;                  // two fp16 scales: blocks 2h, 2h + 1
+  uint32_t hb[QBITS == 4 ? 4 : 2];  // high plane of the 64 codes: 3-bit one bit each, 4-bit two
+  uint32_t v;                  // bit b: block 2h + b exists (else its scale reads as 0 in dq_b2)
 };
 
 // KM >= 1: K is a multiple of 64 (even block count per row), so a lane's two
@@ -136,6 +136,13 @@ __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, c
       r.hb[0] = hv[0];
       r.hb[1] = hv[1];
     }
+    if constexpr (QBITS == 4) {
+      const uint4v hv = *reinterpret_cast<const uint4v*>(codes + int64_t(rows) * (K / 4) + qt_code_off(tl, K, bb));
+      r.hb[0] = hv[0];
+      r.hb[1] = hv[1];
+      r.hb[2] = hv[2];
+      r.hb[3] = hv[3];
+    }
     r.v = in ? 3u : 0u;
     return;
   }
@@ -158,6 +165,15 @@ __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, c
     r.hb[0] = *reinterpret_cast<const uint32_t*>(hp + qt_high_off(tl, K, bb0));
     r.hb[1] = *reinterpret_cast<const uint32_t*>(hp + qt_high_off(tl, K, bb1));
   }
+  if constexpr (QBITS == 4) {
+    const uint8_t* hp = codes + int64_t(rows) * (K / 4);
+    const uint2v h0 = *reinterpret_cast<const uint2v*>(hp + qt_code_off(tl, K, bb0));
+    const uint2v h1 = *reinterpret_cast<const uint2v*>(hp + qt_code_off(tl, K, bb1));
+    r.hb[0] = h0[0];
+    r.hb[1] = h0[1];
+    r.hb[2] = h1[0];
+    r.hb[3] = h1[1];
+  }
   r.v = (in0 ? 1u : 0u) | (in1 ? 2u : 0u);
 }
 
@@ -173,6 +189,8 @@ __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, ha
   const uint32_t w = q < 2 && sel ? r.c[q + 2] : r.c[q];
   if constexpr (QBITS == 2) {
     dq2_word(w, s2, lo, hi);
+  } else if constexpr (QBITS == 4) {
+    dq4_word(w, q < 2 && sel ? r.hb[q + 2] : r.hb[q], s2, lo, hi);
   } else {
     const uint32_t hbits = (r.hb[second ? 1 : 0] >> (16 * (q & 1))) & 0xffffu;
     dq3_word(w, spread16(hbits), s2, lo, hi);
@@ -418,6 +436,10 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, int bm, hipSt
   if (a.qbits == 2) {
     if (a.x_bf16) GQ(2, uint16_t);
     GQ(2, float);
+  }
+  if (a.qbits == 4) {
+    if (a.x_bf16) GQ(4, uint16_t);
+    GQ(4, float);
   }
   if (a.x_bf16) GQ(3, uint16_t);
   GQ(3, float);

@@ -1,9 +1,10 @@
-// Block quantiser and dequantiser for the 2-bit / 3-bit expert format.
+// Block quantiser and dequantiser for the 2-, 3- and 4-bit expert formats.
 //
 // Format: blocks of 32 weights along the reduction axis share one fp16 scale;
 // code c in [-2^(b-1), 2^(b-1)-1] stored offset-binary.  Within a block,
 // weight i sits at bits 2i of the block's 8 low-plane bytes and (3-bit) at
-// bit i of its 4 high-plane bytes; blocks, scales and high-plane pieces are
+// bit i of its 4 high-plane bytes, (4-bit) at bits 2i of its 8 high-plane
+// bytes; blocks, scales and high-plane pieces are
 // placed by the tiled layout of common.h (16-row groups, 64-weight units).
 // (The pages say experts are stored and read at 2 bits -- "How Strata runs a
 // 125-billion-parameter model ...", intro and Step 1 byte table; the block
@@ -66,6 +67,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     uint32_t* hdst = reinterpret_cast<uint32_t*>(codes + rows * cols / 4 + qt_high_off(tl, cols, j));
     *hdst = hi;
   }
+  if constexpr (QBITS == 4) {  // bits 2..3 in a second plane of the low plane's layout
+    uint32_t hi0 = 0, hi1 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      hi0 |= ((q[i] >> 2) & 3u) << (2 * i);
+      hi1 |= ((q[16 + i] >> 2) & 3u) << (2 * i);
+    }
+    *reinterpret_cast<uint2v*>(codes + rows * cols / 4 + qt_code_off(tl, cols, j)) = uint2v{hi0, hi1};
+  }
 }
 
 // One thread per 32-weight block: out = (q - off) * scale, exact in fp32.
@@ -83,7 +93,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const QTile tl = qtile<false>(r, rows);
   const uint2v lo = *reinterpret_cast<const uint2v*>(codes + qt_code_off(tl, cols, j));
   uint32_t hi = 0;
+  uint2v hi4 = uint2v{0u, 0u};
   if constexpr (QBITS == 3) hi = *reinterpret_cast<const uint32_t*>(codes + rows * cols / 4 + qt_high_off(tl, cols, j));
+  if constexpr (QBITS == 4) hi4 = *reinterpret_cast<const uint2v*>(codes + rows * cols / 4 + qt_code_off(tl, cols, j));
   const float s = float(__builtin_bit_cast(f16, scales[qt_scale_off(tl, cols, j)]));
   constexpr int off = 1 << (QBITS - 1);
   float4v* dst = reinterpret_cast<float4v*>(out + base);
@@ -95,6 +107,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       const int k = 4 * i + u;
       uint32_t q = ((k < 16 ? lo[0] : lo[1]) >> (2 * (k & 15))) & 3u;
       if constexpr (QBITS == 3) q |= ((hi >> k) & 1u) << 2;
+      if constexpr (QBITS == 4) q |= (((k < 16 ? hi4[0] : hi4[1]) >> (2 * (k & 15))) & 3u) << 2;
       t[u] = float(int(q) - off) * s;
     }
     dst[i] = t;
@@ -108,8 +121,10 @@ hipError_t launch_quantize(const float* w, int64_t rows, int cols, int qbits, ui
   const dim3 grid(unsigned((nblk + 255) / 256));
   if (qbits == 2)
     quantize_kernel<2><<<grid, 256, 0, stream>>>(w, rows, cols, codes, scales);
-  else
+  else if (qbits == 3)
     quantize_kernel<3><<<grid, 256, 0, stream>>>(w, rows, cols, codes, scales);
+  else
+    quantize_kernel<4><<<grid, 256, 0, stream>>>(w, rows, cols, codes, scales);
   return hipGetLastError();
 }
 
@@ -120,8 +135,10 @@ hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, int64_t 
   const dim3 grid(unsigned((nblk + 255) / 256));
   if (qbits == 2)
     dequant_kernel<2><<<grid, 256, 0, stream>>>(codes, scales, rows, cols, out);
-  else
+  else if (qbits == 3)
     dequant_kernel<3><<<grid, 256, 0, stream>>>(codes, scales, rows, cols, out);
+  else
+    dequant_kernel<4><<<grid, 256, 0, stream>>>(codes, scales, rows, cols, out);
   return hipGetLastError();
 }
 

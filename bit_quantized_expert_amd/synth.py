@@ -58,6 +58,8 @@ WORKLOADS = {
     "decode16": Workload("decode16", MoEShape(qbits=2, **FULL), 16, 48, 2, torch.bfloat16, True),
     "prefill": Workload("prefill", MoEShape(qbits=2, **FULL), 32768, 1, 3, torch.bfloat16, True),
     "prefill3": Workload("prefill3", MoEShape(qbits=3, **FULL), 4096, 48, 4, torch.bfloat16, False),
+    # the 4-bit block variant (codes -8..7), one layer of 4,096 tokens, uniform routing
+    "prefill4": Workload("prefill4", MoEShape(qbits=4, **FULL), 4096, 1, 6, torch.bfloat16, False),
     # a speculative-decoding verify window: the token plus three drafts, through the stack
     "verify4": Workload("verify4", MoEShape(qbits=2, **FULL), 4, 48, 5, torch.bfloat16, True),
 }

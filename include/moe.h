@@ -1,6 +1,6 @@
 /*
  * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer with
- * 2-bit / 3-bit block-quantised experts.
+ * 2-, 3- or 4-bit block-quantised experts.
  *
  * The layer (sources: "How Strata runs a 125-billion-parameter model on a
  * single 12 GB to 24 GB graphics card", intro and Step 2; "Strata Open-Source
@@ -39,9 +39,12 @@
  *   - code c in [-2^(b-1), 2^(b-1)-1], weight = c * s, stored offset-binary
  *     q = c + 2^(b-1);
  *   - per block: 8 low-plane bytes (2-bit codes, or the low two bits of
- *     3-bit ones), weight i of the block at bits 2*(i%4) of byte i/4; with
- *     3 bits also 4 high-plane bytes, bit 2 of q for weight i at bit i%8 of
- *     byte i/8; and one fp16 scale (bit pattern);
+ *     3- and 4-bit ones), weight i of the block at bits 2*(i%4) of byte i/4;
+ *     with 3 bits also 4 high-plane bytes, bit 2 of q for weight i at bit i%8
+ *     of byte i/8; with 4 bits also 8 high-plane bytes in the low plane's
+ *     layout holding bits 2..3 of q (the pages' quantisation ladder tops out
+ *     at a 4-bit file: "Strata serves a 125B MoE at 94 tokens/s ...", section
+ *     "Quality is a sizing decision"); and one fp16 scale (bit pattern);
  *   - tiled placement: rows go in groups of 16 (the last group may be
  *     shorter); within a group K is cut into units of 64 weights (two
  *     blocks), and a unit of the whole group is contiguous, row after row:
@@ -54,12 +57,14 @@
  *                                             : U*n*16 + j*8),
  *       its scale at fp16 index  G0*K/32 + (u < U ? u*n*2 + j*2 + blk%2
  *                                                  : U*n*2 + j),
- *       high-plane bytes at  G0*K/8 + (u < U ? u*n*8 + j*8 + (blk%2)*4
- *                                              : U*n*8 + j*4)
+ *       3-bit high-plane bytes at  G0*K/8 + (u < U ? u*n*8 + j*8 + (blk%2)*4
+ *                                                    : U*n*8 + j*4)
  *     within the high plane, which follows the low plane (rows*K/4 bytes);
- *   - buffer sizes are those of dense row-major planes: rows*K/4 (+ rows*K/8)
- *     code bytes and rows*K/32 scales; an arena's per-expert strides count
- *     those bytes.
+ *     the 4-bit high plane follows the low plane too and places its bytes
+ *     with the low plane's formula;
+ *   - buffer sizes are those of dense row-major planes: rows*K/4 (+ rows*K/8
+ *     at 3 bits, + rows*K/4 at 4 bits) code bytes and rows*K/32 scales; an
+ *     arena's per-expert strides count those bytes.
  * Expert matrices: gate [I][H], up [I][H] (K = H) and down [H][I] (K = I).
  * The expert kernels read one unit of 16 rows as one contiguous piece.
  */
@@ -96,7 +101,7 @@ typedef struct {
   int32_t n_experts;    /* E: routed experts, 1..4096 */
   int32_t top_k;        /* k: experts per token, 1..min(E, 32) */
   int32_t shared_inter; /* shared expert intermediate size (multiple of 32), 0 = none */
-  int32_t qbits;        /* 2 or 3 */
+  int32_t qbits;        /* 2, 3 or 4 */
 } moe_shape;
 
 /* Quantised weights of a set of experts.  Matrix m (0 = gate, 1 = up,

@@ -125,12 +125,14 @@ def check_route_protocol(gpu_logits, gpu_idx, gpu_w, oracle_logits, k):
 
 def tile_quantised(codes: np.ndarray, scales: np.ndarray, rows: int, K: int, qbits: int):
     """Row-major codes / scales (the oracle's quantiser: low plane [rows][K/4],
-    3-bit high plane [rows][K/8] after it, scales [rows][K/32]) rearranged
+    3-bit high plane [rows][K/8] or 4-bit high plane [rows][K/4] after it,
+    scales [rows][K/32]) rearranged
     into the library's tiled storage: rows in groups of 16 (the last group
     may be shorter), each 64-weight unit (two blocks) of a whole group
     contiguous, row after row -- 16 low-plane bytes, 2 scales and 8
     high-plane bytes per row and unit; with K % 64 == 32 the last unit of a
-    group is one block (8 bytes, 1 scale, 4 bytes per row)."""
+    group is one block (8 bytes, 1 scale, 4 bytes per row).  The 4-bit high
+    plane is placed like the low plane."""
     nb, nuf = K // 32, K // 64
     lo = np.asarray(codes[: rows * K // 4]).reshape(rows, K // 4)
     sc = np.asarray(scales).reshape(rows, nb)
@@ -155,5 +157,8 @@ def tile_quantised(codes: np.ndarray, scales: np.ndarray, rows: int, K: int, qbi
             out_sc[so] = sc[r, b]
             if qbits == 3:
                 out_hi[ho:ho + 4] = hi[r, 4 * b:4 * b + 4]
+    if qbits == 4:  # the second plane has the low plane's layout: tile it the same way
+        hi4, _ = tile_quantised(np.asarray(codes[rows * K // 4: rows * K // 2]), scales, rows, K, 2)
+        return np.concatenate([out_lo, hi4]), out_sc
     out_codes = out_lo if qbits == 2 else np.concatenate([out_lo, out_hi])
     return out_codes, out_sc

@@ -41,7 +41,7 @@ def test_workspace_bytes_and_bad_shapes():
     # the workspace holds at least the sorted expert outputs (P x H fp32)
     assert n16 >= 16 * 10 * 2048 * 4
     for bad in [dict(hidden=100), dict(inter=0), dict(n_experts=0), dict(n_experts=5000), dict(top_k=0),
-                dict(top_k=33), dict(qbits=4), dict(shared_inter=48)]:
+                dict(top_k=33), dict(qbits=5), dict(qbits=1), dict(shared_inter=48)]:
         assert lib.moe_workspace_bytes(ctypes.byref(_shape(**bad)), 4, ctypes.byref(opts)) == 0, bad
     assert lib.moe_workspace_bytes(ctypes.byref(_shape()), -1, None) == 0
 
@@ -68,7 +68,7 @@ def test_validation_before_any_device_call():
     assert lib.moe_layer_forward(None, 1, 4, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None, None,
                                  None, fake, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
     # unsupported qbits
-    s4 = _shape(qbits=4)
+    s4 = _shape(qbits=5)
     assert lib.moe_layer_forward(fake, 1, 4, ctypes.byref(lay), ctypes.byref(s4), fake, None, None, None, None,
                                  None, fake, 1 << 40, None) == L.MOE_ERR_UNSUPPORTED
     # misaligned expert codes
@@ -115,7 +115,8 @@ def test_validation_before_any_device_call():
     assert "LDS" in L.last_error_detail()
 
 
-@pytest.mark.parametrize("rows,K,qbits", [(3, 32, 2), (17, 96, 3), (40, 64, 2), (33, 160, 3), (64, 704, 2)])
+@pytest.mark.parametrize("rows,K,qbits", [(3, 32, 2), (17, 96, 3), (40, 64, 2), (33, 160, 3), (64, 704, 2),
+                                           (5, 96, 4), (48, 704, 4)])
 def test_tiled_layout_is_a_permutation(rows, K, qbits):
     """The tiled storage of the quantised matrices (as the tests restate it)
     moves every byte of the row-major layout to a distinct place, so it keeps

@@ -28,7 +28,7 @@ def _weights(rows, k, seed):
     return w
 
 
-@pytest.mark.parametrize("qbits", [2, 3])
+@pytest.mark.parametrize("qbits", [2, 3, 4])
 @pytest.mark.parametrize("rows,k", [(3, 32), (17, 64), (40, 96), (64, 704), (33, 2048)])
 def test_quantize_and_dequant_bit_exact(qbits, rows, k):
     M = _lib()

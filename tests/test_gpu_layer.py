@@ -75,6 +75,14 @@ RAGGED = [
     ("s3", 128, 160, 12, 4, 0, 2, 1, torch.bfloat16),
     ("s4", 256, 192, 33, 8, 96, 3, 1, torch.bfloat16),
     ("s5", 192, 128, 40, 32, 64, 2, 1, torch.bfloat16),
+    # the 4-bit format on each decode path: per-slot kernels (37 tokens; hidden not a multiple
+    # of 1024), the single-token fused path (32-weight down units), the persistent kernels with
+    # the in-kernel selection (bf16 and fp32 tokens)
+    ("q1", 96, 96, 5, 3, 64, 4, 37, torch.bfloat16),
+    ("q2", 256, 192, 33, 8, 96, 4, 1, torch.bfloat16),
+    ("q3", 1024, 128, 8, 4, 128, 4, 16, torch.bfloat16),
+    ("q4", 2048, 704, 16, 8, 704, 4, 5, torch.float32),
+    ("q5", 128, 160, 12, 4, 0, 4, 9, torch.bfloat16),
     # the largest expert count and top-k the library takes (4096, 32): selection over 64 keys per
     # lane, one token through the small-batch path
     ("m1", 64, 32, 4096, 32, 32, 2, 1, torch.bfloat16),
@@ -105,6 +113,17 @@ def test_decode1_full_shape():
     for seed_layer in range(3):
         x = synth.tokens(dl.wl, "cuda", layer=seed_layer)
         _check_layer(M, dl, x, "gemv")
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_full_shape_4bit(T):
+    """One full-shape layer (hidden 2048, 512 experts, top-10, inter 704) in
+    the 4-bit format: the single-token path and the verify-window path."""
+    M = _M()
+    wl = synth.custom("full4", 2048, 704, 512, 10, 704, 4, T, seed=31, act_dtype=torch.bfloat16, zipf_bias=True)
+    dl = _layer(wl)
+    x = synth.tokens(wl, "cuda")
+    _check_layer(M, dl, x, "gemv")
 
 
 def test_decode16_layer_and_batch_invariance():

@@ -66,6 +66,11 @@ RAGGED = [
     ("k1", 128, 256, 6, 2, 128, 2, 300, torch.bfloat16),
     ("k2", 256, 128, 9, 3, 0, 3, 333, torch.float32),
     ("k3", 320, 128, 5, 2, 256, 3, 250, torch.bfloat16),
+    # the 4-bit format: 96-row tiles with fp32 tokens, 128-row tiles with the down half step,
+    # K not a multiple of 64
+    ("q6", 256, 192, 24, 3, 96, 4, 680, torch.float32),
+    ("q7", 2048, 704, 4, 2, 704, 4, 520, torch.bfloat16),
+    ("q8", 96, 96, 5, 3, 64, 4, 37, torch.bfloat16),
     # the largest expert count and top-k (4096, 32)
     ("m3", 64, 32, 4096, 32, 32, 2, 40, torch.bfloat16),
 ]
@@ -140,3 +145,8 @@ def test_prefill_32k_sampled():
 def test_prefill3_4k_sampled():
     """4,096-token prefill of one full-shape 3-bit layer, uniform routing."""
     _sampled_check(_M(), synth.WORKLOADS["prefill3"], 24, seed=6)
+
+
+def test_prefill4_4k_sampled():
+    """4,096-token prefill of one full-shape 4-bit layer, uniform routing."""
+    _sampled_check(_M(), synth.WORKLOADS["prefill4"], 24, seed=7)
