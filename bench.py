@@ -314,6 +314,37 @@ def prefill_bench(wl, layer, dev, log, reps=5):
             "experts_used": used, "largest_expert_tokens": top}
 
 
+def fourbit_bench(dev, log, n_layers=8, replays=40):
+    """The 4-bit block variant (codes -8..7): the 4,096-token layer on the
+    grouped GEMM, and single-token decode walking n_layers resident 4-bit
+    layers (10 GB, far beyond the 256 MB Infinity Cache) in one graph."""
+    wl = synth.WORKLOADS["prefill4"]
+    s = wl.shape
+    layers = build_layers(wl, n_layers, dev, log)
+    pre = prefill_bench(wl, layers[0], dev, log)
+    xs = [synth.tokens(wl, dev, layer=100 + i, n_tokens=1) for i in range(n_layers)]
+    dec = DecodeSteps(s, layers, xs, dev)
+    dec.eager()
+    dec.capture()
+    for _ in range(3):
+        dec.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        dec.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (replays * n_layers) * 1e3
+    nbytes = s.n_experts * s.hidden * 2 + s.top_k * expert_bytes(s) + shared_bytes(s)
+    log(f"4-bit decode1: {us:.2f} us/layer, {nbytes / us / 1e3:.0f} GB/s")
+    del dec, layers
+    torch.cuda.empty_cache()
+    return {"prefill4k_layer": pre,
+            "decode1": {"avg_us": us, "tokens_per_s": 1e6 / us, "bytes": nbytes, "GBs": nbytes / us / 1e3,
+                        "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "layers": n_layers}}
+
+
 def prefill3_stack_bench(dev, log, n_layers, steps=2):
     """4,096 tokens through the 48-layer 3-bit stack (uniform routing), with
     the residual / RMSNorm / bf16 glue between layers."""
@@ -408,6 +439,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill3", action="store_true")
+    ap.add_argument("--no-4bit", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy 10 times (scales the HBM byte counters)")
     ap.add_argument("--quiet", action="store_true")
@@ -503,6 +535,10 @@ def main():
     prefill3 = None
     if not args.no_prefill3:
         prefill3 = prefill3_stack_bench(dev, log, args.layers)
+        torch.cuda.empty_cache()
+    fourbit = None
+    if not args.no_4bit:
+        fourbit = fourbit_bench(dev, log)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -536,7 +572,7 @@ def main():
                      "probe": probe},
         "cpu_baseline": cpu,
         "secondary": {"prefill32k_layer": prefill, "prefill3_4k_stack": prefill3,
-                      "decode16_stack": stack16, "verify4_stack": stack4},
+                      "decode16_stack": stack16, "verify4_stack": stack4, "four_bit": fourbit},
     }
     print(json.dumps(res), flush=True)
 
