@@ -150,3 +150,31 @@ def test_prefill3_4k_sampled():
 def test_prefill4_4k_sampled():
     """4,096-token prefill of one full-shape 4-bit layer, uniform routing."""
     _sampled_check(_M(), synth.WORKLOADS["prefill4"], 24, seed=7)
+
+
+@pytest.mark.parametrize("case", [("w3", 256, 192, 4, 2, 0, 2, 600, torch.bfloat16),
+                                  ("q6", 256, 192, 24, 3, 96, 4, 680, torch.float32)], ids=["no_shared", "shared"])
+def test_grouped_stack_glue(case):
+    """The grouped-GEMM layer with the stack glue (residual add, RMSNorm and
+    bf16 next input, no `out`), with and without a shared expert: the residual
+    update equals the layer output bit for bit, and the next input is the
+    oracle's RMSNorm + bf16 rounding of the GPU residual except at rounding
+    boundaries."""
+    from oracle import moe_oracle as O
+    M = _M()
+    name, H, I, E, k, Is, qb, T, dt = case
+    wl = synth.custom(name, H, I, E, k, Is, qb, T, seed=23, act_dtype=dt, zipf_bias=True)
+    dl = _layer(wl)
+    s = dl.s
+    x = synth.tokens(wl, "cuda")
+    out, _, _ = _forward(M, dl, x, "grouped")
+    r0 = torch.randn(T, s.hidden, device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+    r = r0.clone()
+    a = torch.empty(T, s.hidden, dtype=torch.bfloat16, device="cuda")
+    ws = M.alloc_workspace(s, T, algo="grouped")
+    M.layer_forward(x, dl.q, s, residual=r, next_in=a, algo="grouped", ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(r, r0 + out)
+    want_a = O.rmsnorm_bf16(r.cpu().numpy().astype(np.float64))
+    diff = a.float().cpu().numpy() != want_a
+    assert np.mean(diff) < 1e-3
