@@ -1,8 +1,8 @@
-"""MI355X (gfx950) sparse Mixture-of-Experts layer with 2-bit / 3-bit
-block-quantised experts: HIP kernels behind a C ABI (include/moe.h), bound
+"""MI355X (gfx950) sparse Mixture-of-Experts layer with 2-, 3- and
+4-bit block-quantised experts: HIP kernels behind a C ABI (include/moe.h), bound
 here with ctypes."""
 
 from ._lib import (  # noqa: F401
     FFN_REUSE_PLAN, FFN_SKIP_DOWN, FFN_SKIP_GATEUP, MoeError, QArena, QLayer, Shape, alloc_workspace, combine, dequant, expert_ffn, layer_forward, lib, permute,
-    quantize, read_error, rmsnorm_bf16, route, workspace_bytes,
+    quantize, read_error, repack, rmsnorm_bf16, route, workspace_bytes,
 )

@@ -67,6 +67,7 @@ _SIGS = {
     "moe_rmsnorm_bf16": (ctypes.c_int, [_VP, _I64, _I32, _VP, _VP]),
     "moe_dequant": (ctypes.c_int, [_VP, _VP, _I64, _I32, _I32, _VP, _VP]),
     "moe_quantize": (ctypes.c_int, [_VP, _I64, _I32, _I32, _VP, _VP, _VP]),
+    "moe_repack": (ctypes.c_int, [_VP, _VP, _I64, _I32, _I32, _VP, _VP, _VP]),
     "moe_read_error": (ctypes.c_int, [_VP, _SZ, _VP]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error_detail": (ctypes.c_char_p, []),
@@ -170,19 +171,38 @@ class QArena:
 
     def quantize_from(self, m: int, w: torch.Tensor, experts: slice | None = None, stream=None) -> None:
         """Quantise fp32 weights w [n_sel, rows, K] of matrix m into the arena
-        (experts `experts`, default all) with the library's moe_quantize."""
+        (experts `experts`, default all): moe_quantize into the canonical
+        layout, then moe_repack into the kernel layout the arena holds."""
         rows, k = self.mat_shapes[m]
         lo = 0 if experts is None else experts.start
         n = w.shape[0]
         if w.shape[1:] != (rows, k) or w.dtype != torch.float32:
             raise ValueError(f"expected fp32 [n, {rows}, {k}], got {tuple(w.shape)} {w.dtype}")
         w = w.contiguous()
+        codes = torch.empty(n, self.codes[m].shape[1], dtype=torch.uint8, device=w.device)
+        scales = torch.empty(n, self.scales[m].shape[1], dtype=torch.int16, device=w.device)
         if self.qbits == 2:
-            quantize(w.view(n * rows, k), 2, self.codes[m][lo:lo + n], self.scales[m][lo:lo + n], stream=stream)
+            quantize(w.view(n * rows, k), 2, codes, scales, stream=stream)
         else:
             # the 3- and 4-bit planes are per matrix, so each expert is one call
             for i in range(n):
-                quantize(w[i], self.qbits, self.codes[m][lo + i], self.scales[m][lo + i], stream=stream)
+                quantize(w[i], self.qbits, codes[i], scales[i], stream=stream)
+        self.load_canonical(m, lo, codes, scales, stream=stream)
+
+    def load_canonical(self, m: int, first: int, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+        """Repack canonical-layout codes uint8 [n, bytes] and scales int16
+        [n, count] of matrix m of experts first .. first + n - 1 into the
+        arena."""
+        rows, k = self.mat_shapes[m]
+        n = codes.shape[0]
+        if self.qbits == 2 and rows % 16 == 0:
+            # one plane, and no row group straddles two experts: the stacked matrices repack as one
+            repack(codes.reshape(-1), scales.reshape(-1), n * rows, k, 2, self.codes[m][first:first + n].reshape(-1),
+                   self.scales[m][first:first + n].reshape(-1), stream=stream)
+            return
+        for i in range(n):
+            repack(codes[i], scales[i], rows, k, self.qbits, self.codes[m][first + i], self.scales[m][first + i],
+                   stream=stream)
 
     def bytes(self) -> int:
         return sum(c.numel() for c in self.codes) + 2 * sum(s.numel() for s in self.scales)
@@ -279,6 +299,14 @@ def quantize(w, qbits: int, codes, scales, stream=None) -> None:
         raise ValueError("codes/scales buffers are too small")
     _check(lib().moe_quantize(_ptr(w), rows, cols, qbits, _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_quantize")
+
+
+def repack(codes, scales, rows: int, cols: int, qbits: int, packed_codes, packed_scales, stream=None) -> None:
+    if min(codes.numel(), packed_codes.numel()) < rows * cols * qbits // 8 or \
+            min(scales.numel(), packed_scales.numel()) < rows * cols // 32:
+        raise ValueError("codes/scales buffers are too small")
+    _check(lib().moe_repack(_ptr(codes), _ptr(scales), rows, cols, qbits, _ptr(packed_codes), _ptr(packed_scales),
+                            _stream(stream)), "moe_repack")
 
 
 def read_error(ws, stream=None) -> None:

@@ -307,7 +307,8 @@ hipError_t fused_decode(const void* x, moe_dtype xd, int64_t T, const moe_layer*
 // all selected experts and the shared expert with the combine done inside
 // the workgroup; then the residual RMSNorm when next_in is asked for.
 bool decode1_ok(int64_t T, const moe_shape* s, moe_algo algo) {
-  return algo == MOE_ALGO_GEMV && T == 1 && s->n_experts <= moe::kDecode1MaxExperts;
+  return algo == MOE_ALGO_GEMV && T == 1 && s->n_experts <= moe::kDecode1MaxExperts &&
+         moe::decode1_lds_ok(s->hidden, s->inter, s->shared_inter, s->top_k, s->shared_inter > 0);
 }
 
 hipError_t decode1(const void* x, moe_dtype xd, const moe_layer* L, const moe_shape* s, float* out, float* residual,
@@ -516,6 +517,27 @@ int moe_quantize(const float* w, int64_t rows, int32_t cols, int32_t qbits, uint
   if (!aligned(codes, 8) || !aligned(scales, 2) || !aligned(w, 16))
     return fail(MOE_ERR_INVALID_ARG, "codes must be 8-, scales 2- and w 16-byte aligned");
   return device_status(moe::launch_quantize(w, rows, cols, qbits, codes, scales, as_stream(stream)), "moe_quantize");
+}
+
+int moe_repack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int32_t cols, int32_t qbits,
+               uint8_t* packed_codes, uint16_t* packed_scales, void* stream) {
+  if (qbits < 2 || qbits > 4) return fail(MOE_ERR_UNSUPPORTED, "qbits=%d: only 2, 3 and 4 are supported", qbits);
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "rows=%lld cols=%d: cols must be a positive multiple of 32", (long long)rows, cols);
+  if (rows == 0) return ok();
+  if (!codes || !scales || !packed_codes || !packed_scales)
+    return fail(MOE_ERR_INVALID_ARG, "codes, scales, packed_codes and packed_scales must be non-NULL");
+  if (!aligned(codes, 8) || !aligned(packed_codes, 8) || !aligned(scales, 2) || !aligned(packed_scales, 2))
+    return fail(MOE_ERR_INVALID_ARG, "codes and packed_codes must be 8-, scales and packed_scales 2-byte aligned");
+  const uintptr_t nc = uintptr_t(rows) * uintptr_t(cols) / 8 * uintptr_t(qbits), ns = uintptr_t(rows) * (cols / 32) * 2;
+  const uintptr_t in[2][2] = {{uintptr_t(codes), uintptr_t(codes) + nc}, {uintptr_t(scales), uintptr_t(scales) + ns}};
+  const uintptr_t out[2][2] = {{uintptr_t(packed_codes), uintptr_t(packed_codes) + nc},
+                               {uintptr_t(packed_scales), uintptr_t(packed_scales) + ns}};
+  for (const auto& a : in)
+    for (const auto& b : out)
+      if (a[0] < b[1] && b[0] < a[1]) return fail(MOE_ERR_INVALID_ARG, "moe_repack is out of place: outputs overlap inputs");
+  return device_status(moe::launch_repack(codes, scales, rows, cols, qbits, packed_codes, packed_scales,
+                                          as_stream(stream)),
+                       "moe_repack");
 }
 
 int moe_read_error(void* workspace, size_t workspace_bytes, void* stream) {

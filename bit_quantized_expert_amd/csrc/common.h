@@ -73,7 +73,9 @@ __device__ __forceinline__ float16v mfma32_bf16(bf16x8 a, bf16x8 b, float16v c) 
 // blocks), and one unit of the whole group is contiguous, row after row:
 //   low code plane (2 bits per weight): 16 bytes per row and unit,
 //   scales (fp16, one per block):        4 bytes per row and unit,
-//   3-bit high plane (1 bit per weight):  8 bytes per row and unit.
+//   3-bit high plane (1 bit per weight):  8 bytes per row and unit, each
+//                                        block's word rearranged by
+//                                        qt_high3_word.
 // When K % 64 == 32 the last unit of a group holds one block (8, 2 and 4
 // bytes per row).  A group occupies the bytes its rows take in row-major
 // order, so buffer sizes, the offset of the high plane (rows * K / 4 bytes)
@@ -180,7 +182,7 @@ __device__ __forceinline__ void dq2_word(uint32_t w, half2v s2, half8& lo, half8
 }
 
 // Spread the 16 bits of h to even bit positions: bit k -> bit 2k.
-__device__ __forceinline__ uint32_t spread16(uint32_t h) {
+__host__ __device__ __forceinline__ uint32_t spread16(uint32_t h) {
   h &= 0xffffu;
   h = (h | (h << 8)) & 0x00ff00ffu;
   h = (h | (h << 4)) & 0x0f0f0f0fu;
@@ -189,20 +191,38 @@ __device__ __forceinline__ uint32_t spread16(uint32_t h) {
   return h;
 }
 
-// 3-bit variant: w holds the low two bits of 16 codes (2-bit layout) and
-// sp = spread16(high bits) holds bit 2 of code i at bit 2i.  Pairs 0..3 use
-// M_0..M_3 with the high bits moved to 2i+2 (sp << 2; bits up to 2i+2 <= 8
-// stay inside the mantissa); pairs 4..7 use w >> 8 and sp >> 6 with M_0..M_3
-// (shifting right keeps bit 30, the high bit of code 15).  c = q - 4; c * s
-// rounds to fp16 for |c| = 3 (relative error <= 2^-11 per weight).
-__device__ __forceinline__ void dq3_word(uint32_t w, uint32_t sp, half2v s2, half8& lo, half8& hi) {
-  const uint32_t w8 = w >> 8, hs = sp << 2, h8 = sp >> 6;
+// The kernels' 3-bit high-plane word of a block: the block's 32 high bits
+// (bit i = bit 2 of q for code i) rearranged once, at repack, so that bit i
+// of codes 0..15 (the block's first 16-code word A) sits at bit 2i + 1 and
+// bit i of codes 16..31 (word B) at bit 2i.  Shifted by a constant, the high
+// bits of either word then line up with the fp16 mantissa slots of its pairs
+// (dq3_word), with the other word's bits on odd positions outside the masks.
+__host__ __device__ __forceinline__ uint32_t qt_high3_word(uint32_t h) {
+  return (spread16(h & 0xffffu) << 1) | spread16(h >> 16);
+}
+
+// The high bits of 16-code word `second` (0 = A, 1 = B) of a block for
+// dq3_word: bit 2 of code j at bit 2j + 2 (pairs 0..3, lo) and of code i at
+// bit 2i - 6 (pairs 4..7, hi).
+__device__ __forceinline__ void high3_slots(uint32_t hw, int second, uint32_t& lo, uint32_t& hi) {
+  lo = second ? hw << 2 : hw << 1;
+  hi = second ? hw >> 6 : hw >> 7;
+}
+
+// 3-bit variant: w holds the low two bits of 16 codes (2-bit layout); hlo
+// and hhi hold bit 2 of code i at bit 2i + 2 (pairs 0..3) and 2i - 6 (pairs
+// 4..7), with bits on odd positions ignored (high3_slots).  Pairs 0..3 use
+// M_0..M_3 (bits up to 2i + 2 <= 8 stay inside the mantissa); pairs 4..7 use
+// w >> 8 with M_0..M_3.  c = q - 4; c * s rounds to fp16 for |c| = 3
+// (relative error <= 2^-11 per weight).
+__device__ __forceinline__ void dq3_word(uint32_t w, uint32_t hlo, uint32_t hhi, half2v s2, half8& lo, half8& hi) {
+  const uint32_t w8 = w >> 8;
   half2v p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = i < 4 ? i : i - 4;
     const uint32_t src = i < 4 ? w : w8;
-    const uint32_t hsrc = i < 4 ? hs : h8;
+    const uint32_t hsrc = i < 4 ? hlo : hhi;
     const uint32_t v = and_or_v(src, 0x00030003u << (2 * j), and_or(hsrc, 0x00040004u << (2 * j), magic_bits(j)));
     const f16 off = magic_val(j) + f16(4.0f);
     half2v h = as_half2(v) - half2v{off, off};

@@ -83,8 +83,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     }
     n_tiles += st;
   }
-  if (threadIdx.x == 0) {
-    header[kHdrError] = 0;
+  if (threadIdx.x == 0) {  // the error word belongs to the permutation: left as it is
     header[kHdrActive] = n_active;
     header[kHdrValid] = n_valid;
     header[kHdrTiles] = n_tiles;
@@ -168,8 +167,9 @@ __device__ __forceinline__ void dq_unit_word(const Unit<QBITS, UNIT>& U, int d, 
   } else if constexpr (QBITS == 4) {
     dq4_word(U.w[d], U.h[d], s2, lo, hi);
   } else {
-    const uint32_t hb = (U.h[d >> 1] >> (16 * (d & 1))) & 0xffffu;
-    dq3_word(U.w[d], spread16(hb), s2, lo, hi);
+    uint32_t hlo, hhi;
+    high3_slots(U.h[d >> 1], d & 1, hlo, hhi);
+    dq3_word(U.w[d], hlo, hhi, s2, lo, hi);
   }
 }
 
@@ -1405,8 +1405,7 @@ hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t 
 }
 
 bool gemv_lds_ok(int64_t T, int H, int I, int Is) {
-  if (T <= 1) return true;
-  const size_t m = size_t(std::min<int64_t>(T, kGemvMaxM));
+  const size_t m = size_t(std::max<int64_t>(1, std::min<int64_t>(T, kGemvMaxM)));
   const size_t kmax = size_t(std::max(I, Is));
   return m * (H + 8) * sizeof(f16) + 16384 <= kLdsBytes && m * (kmax + 8) * sizeof(f16) + 16384 <= kLdsBytes;
 }
@@ -1449,8 +1448,15 @@ static hipError_t launch_decode1_q(const FfnArgs& a, const Decode1Sel& sel, floa
   return hipGetLastError();
 }
 
+bool decode1_lds_ok(int H, int I, int Is, int k, bool has_shared) {
+  const size_t slots = size_t(k) + (has_shared ? 1 : 0);
+  const size_t ldh = size_t(std::max(I, has_shared ? Is : 0)) + 8;
+  return size_t(H) * sizeof(f16) + 16384 <= kLdsBytes && slots * ldh * sizeof(f16) + 16384 <= kLdsBytes;
+}
+
 hipError_t launch_decode1_ffn(const FfnArgs& a, const Decode1Sel& sel, float* out, float* res, hipStream_t stream) {
   if (a.E > kDecode1MaxExperts || a.T != 1) return hipErrorInvalidValue;
+  if (!decode1_lds_ok(a.H, a.I, a.Is, a.k, a.has_shared)) return hipErrorInvalidValue;
   return a.qbits == 2   ? launch_decode1_q<2>(a, sel, out, res, stream)
          : a.qbits == 3 ? launch_decode1_q<3>(a, sel, out, res, stream)
                         : launch_decode1_q<4>(a, sel, out, res, stream);

@@ -192,8 +192,9 @@ __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, ha
   } else if constexpr (QBITS == 4) {
     dq4_word(w, q < 2 && sel ? r.hb[q + 2] : r.hb[q], s2, lo, hi);
   } else {
-    const uint32_t hbits = (r.hb[second ? 1 : 0] >> (16 * (q & 1))) & 0xffffu;
-    dq3_word(w, spread16(hbits), s2, lo, hi);
+    uint32_t hlo, hhi;
+    high3_slots(r.hb[second ? 1 : 0], q & 1, hlo, hhi);
+    dq3_word(w, hlo, hhi, s2, lo, hi);
   }
 }
 

@@ -50,6 +50,9 @@ struct FfnArgs {
 
 hipError_t launch_quantize(const float* w, int64_t rows, int cols, int qbits, uint8_t* codes,
                            uint16_t* scales, hipStream_t stream);
+// Canonical row-major planes -> the tiled kernel layout of common.h.
+hipError_t launch_repack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int cols, int qbits,
+                         uint8_t* tcodes, uint16_t* tscales, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int cols,
                           int qbits, float* out, hipStream_t stream);
 hipError_t launch_router_gemv(const void* x, bool x_bf16, int64_t T, int H, const void* w, bool w_bf16,
@@ -98,6 +101,9 @@ hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, int bm, hipSt
 // down + combine into out and/or res.  The selected experts occupy slots in
 // ascending expert order; idx/w are the API's rank-ordered outputs.
 constexpr int kDecode1MaxExperts = 512;
+// LDS of the fused single-token kernels: the token (H fp16) in gate/up, the
+// h rows of all k (+ shared) slots in down + combine; whether both fit.
+bool decode1_lds_ok(int H, int I, int Is, int k, bool has_shared);
 struct Decode1Sel {
   const float* logits;   // [E] router logits of the token
   int32_t* idx;          // [k] experts, rank order (written)

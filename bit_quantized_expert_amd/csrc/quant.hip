@@ -1,11 +1,14 @@
-// Block quantiser and dequantiser for the 2-, 3- and 4-bit expert formats.
+// Block quantiser, dequantiser and repack for the 2-, 3- and 4-bit expert
+// formats.
 //
 // Format: blocks of 32 weights along the reduction axis share one fp16 scale;
-// code c in [-2^(b-1), 2^(b-1)-1] stored offset-binary.  Within a block,
-// weight i sits at bits 2i of the block's 8 low-plane bytes and (3-bit) at
-// bit i of its 4 high-plane bytes, (4-bit) at bits 2i of its 8 high-plane
-// bytes; blocks, scales and high-plane pieces are
-// placed by the tiled layout of common.h (16-row groups, 64-weight units).
+// code c in [-2^(b-1), 2^(b-1)-1] stored offset-binary.  The quantiser and the
+// dequantiser use the canonical row-major layout of the C ABI: a low plane
+// [rows][cols/4] bytes (weight k of a row at bits 2(k%4) of byte k/4), then
+// for 3 bits a high plane [rows][cols/8] (bit 2 of q at bit k%8 of byte k/8)
+// or for 4 bits a second plane [rows][cols/4] in the low plane's layout (bits
+// 2..3 of q), and scales [rows][cols/32].  The repack kernel turns that into
+// the kernels' own layout (tiled, common.h), once, when weights are uploaded.
 // (The pages say experts are stored and read at 2 bits -- "How Strata runs a
 // 125-billion-parameter model ...", intro and Step 1 byte table; the block
 // layout is this library's own.)
@@ -48,9 +51,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     if (d != 0.0f) c = fminf(fmaxf(__builtin_rintf(__fdiv_rn(v[i], d)), cmin), cmax);
     q[i] = uint32_t(int(c) + off);
   }
-  const QTile tl = qtile<false>(r, rows);
   // a zero scale is stored as +0 whatever the sign of the largest element
-  scales[qt_scale_off(tl, cols, j)] = d == 0.0f ? uint16_t(0) : __builtin_bit_cast(uint16_t, d16);
+  scales[b] = d == 0.0f ? uint16_t(0) : __builtin_bit_cast(uint16_t, d16);
   // low plane: 8 bytes per block
   uint32_t lo0 = 0, lo1 = 0;
 #pragma unroll
@@ -58,13 +60,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     lo0 |= (q[i] & 3u) << (2 * i);
     lo1 |= (q[16 + i] & 3u) << (2 * i);
   }
-  uint2v* dst = reinterpret_cast<uint2v*>(codes + qt_code_off(tl, cols, j));
+  uint2v* dst = reinterpret_cast<uint2v*>(codes + b * 8);  // == r * cols / 4 + j * 8
   *dst = uint2v{lo0, lo1};
   if constexpr (QBITS == 3) {
     uint32_t hi = 0;
 #pragma unroll
     for (int i = 0; i < kBlock; ++i) hi |= ((q[i] >> 2) & 1u) << i;
-    uint32_t* hdst = reinterpret_cast<uint32_t*>(codes + rows * cols / 4 + qt_high_off(tl, cols, j));
+    uint32_t* hdst = reinterpret_cast<uint32_t*>(codes + rows * cols / 4 + b * 4);
     *hdst = hi;
   }
   if constexpr (QBITS == 4) {  // bits 2..3 in a second plane of the low plane's layout
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
       hi0 |= ((q[i] >> 2) & 3u) << (2 * i);
       hi1 |= ((q[16 + i] >> 2) & 3u) << (2 * i);
     }
-    *reinterpret_cast<uint2v*>(codes + rows * cols / 4 + qt_code_off(tl, cols, j)) = uint2v{hi0, hi1};
+    *reinterpret_cast<uint2v*>(codes + rows * cols / 4 + b * 8) = uint2v{hi0, hi1};
   }
 }
 
@@ -88,15 +90,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (b >= nblk) return;
   const int64_t base = b * kBlock;  // == r * cols + j * 32 (row-major output)
-  const int64_t r = b / bpr;
-  const int j = int(b - r * bpr);
-  const QTile tl = qtile<false>(r, rows);
-  const uint2v lo = *reinterpret_cast<const uint2v*>(codes + qt_code_off(tl, cols, j));
+  const uint2v lo = *reinterpret_cast<const uint2v*>(codes + b * 8);
   uint32_t hi = 0;
   uint2v hi4 = uint2v{0u, 0u};
-  if constexpr (QBITS == 3) hi = *reinterpret_cast<const uint32_t*>(codes + rows * cols / 4 + qt_high_off(tl, cols, j));
-  if constexpr (QBITS == 4) hi4 = *reinterpret_cast<const uint2v*>(codes + rows * cols / 4 + qt_code_off(tl, cols, j));
-  const float s = float(__builtin_bit_cast(f16, scales[qt_scale_off(tl, cols, j)]));
+  if constexpr (QBITS == 3) hi = *reinterpret_cast<const uint32_t*>(codes + rows * cols / 4 + b * 4);
+  if constexpr (QBITS == 4) hi4 = *reinterpret_cast<const uint2v*>(codes + rows * cols / 4 + b * 8);
+  const float s = float(__builtin_bit_cast(f16, scales[b]));
   constexpr int off = 1 << (QBITS - 1);
   float4v* dst = reinterpret_cast<float4v*>(out + base);
 #pragma unroll
@@ -112,6 +111,48 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     }
     dst[i] = t;
   }
+}
+
+// One thread per 32-weight block: canonical row-major block -> the tiled
+// placement of common.h.  The 3-bit high-plane word of a block (bit i = code
+// i) is stored pre-spread for the unpack: bit i of codes 0..15 moves to bit
+// 2i + 1 and bit i of codes 16..31 to bit 2i (qt_high3_word), so no unpack
+// has to spread bits at run time.  Every other piece moves unchanged.
+template <int QBITS>
+__global__ __launch_bounds__(256) void repack_kernel(const uint8_t* __restrict__ codes,
+                                                    const uint16_t* __restrict__ scales, int64_t rows, int cols,
+                                                    uint8_t* __restrict__ tcodes, uint16_t* __restrict__ tscales) {
+  const int bpr = cols / kBlock;
+  const int64_t nblk = rows * bpr;
+  const int64_t b = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (b >= nblk) return;
+  const int64_t r = b / bpr;
+  const int j = int(b - r * bpr);
+  const QTile tl = qtile<false>(r, rows);
+  tscales[qt_scale_off(tl, cols, j)] = scales[b];
+  *reinterpret_cast<uint2v*>(tcodes + qt_code_off(tl, cols, j)) = *reinterpret_cast<const uint2v*>(codes + b * 8);
+  const int64_t plane = rows * cols / 4;
+  if constexpr (QBITS == 3) {
+    const uint32_t h = *reinterpret_cast<const uint32_t*>(codes + plane + b * 4);
+    *reinterpret_cast<uint32_t*>(tcodes + plane + qt_high_off(tl, cols, j)) = qt_high3_word(h);
+  }
+  if constexpr (QBITS == 4)
+    *reinterpret_cast<uint2v*>(tcodes + plane + qt_code_off(tl, cols, j)) =
+        *reinterpret_cast<const uint2v*>(codes + plane + b * 8);
+}
+
+hipError_t launch_repack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int cols, int qbits,
+                         uint8_t* tcodes, uint16_t* tscales, hipStream_t stream) {
+  const int64_t nblk = rows * (cols / kBlock);
+  if (nblk == 0) return hipSuccess;
+  const dim3 grid(unsigned((nblk + 255) / 256));
+  if (qbits == 2)
+    repack_kernel<2><<<grid, 256, 0, stream>>>(codes, scales, rows, cols, tcodes, tscales);
+  else if (qbits == 3)
+    repack_kernel<3><<<grid, 256, 0, stream>>>(codes, scales, rows, cols, tcodes, tscales);
+  else
+    repack_kernel<4><<<grid, 256, 0, stream>>>(codes, scales, rows, cols, tcodes, tscales);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(const float* w, int64_t rows, int cols, int qbits, uint8_t* codes,

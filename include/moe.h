@@ -38,35 +38,25 @@
  *   - blocks of 32 consecutive weights along K share one fp16 scale s;
  *   - code c in [-2^(b-1), 2^(b-1)-1], weight = c * s, stored offset-binary
  *     q = c + 2^(b-1);
- *   - per block: 8 low-plane bytes (2-bit codes, or the low two bits of
- *     3- and 4-bit ones), weight i of the block at bits 2*(i%4) of byte i/4;
- *     with 3 bits also 4 high-plane bytes, bit 2 of q for weight i at bit i%8
- *     of byte i/8; with 4 bits also 8 high-plane bytes in the low plane's
- *     layout holding bits 2..3 of q (the pages' quantisation ladder tops out
- *     at a 4-bit file: "Strata serves a 125B MoE at 94 tokens/s ...", section
- *     "Quality is a sizing decision"); and one fp16 scale (bit pattern);
- *   - tiled placement: rows go in groups of 16 (the last group may be
- *     shorter); within a group K is cut into units of 64 weights (two
- *     blocks), and a unit of the whole group is contiguous, row after row:
- *     16 low-plane bytes, 2 scales and 8 high-plane bytes per row and unit.
- *     With K % 64 == 32 a group's last unit is one block (8 bytes, 1 scale,
- *     4 bytes per row).  Groups follow each other in row order.  So with G0
- *     the first row of row r's group, n its size, j = r - G0, u = blk / 2
- *     and U = K / 64 full units, block blk of row r has
- *       low-plane bytes at  G0*K/4  + (u < U ? u*n*16 + j*16 + (blk%2)*8
- *                                             : U*n*16 + j*8),
- *       its scale at fp16 index  G0*K/32 + (u < U ? u*n*2 + j*2 + blk%2
- *                                                  : U*n*2 + j),
- *       3-bit high-plane bytes at  G0*K/8 + (u < U ? u*n*8 + j*8 + (blk%2)*4
- *                                                    : U*n*8 + j*4)
- *     within the high plane, which follows the low plane (rows*K/4 bytes);
- *     the 4-bit high plane follows the low plane too and places its bytes
- *     with the low plane's formula;
- *   - buffer sizes are those of dense row-major planes: rows*K/4 (+ rows*K/8
- *     at 3 bits, + rows*K/4 at 4 bits) code bytes and rows*K/32 scales; an
- *     arena's per-expert strides count those bytes.
+ *   - canonical layout (what moe_quantize writes and moe_dequant and
+ *     moe_repack read), row-major planes:
+ *       low plane   [rows][K/4] bytes: bits 0..1 of q for weight k of a row
+ *                   at bits 2*(k%4) of byte k/4 (the 2-bit codes themselves);
+ *       3 bits:     then a high plane [rows][K/8]: bit 2 of q at bit k%8 of
+ *                   byte k/8;
+ *       4 bits:     then a second plane [rows][K/4] in the low plane's
+ *                   layout holding bits 2..3 of q (the pages' quantisation
+ *                   ladder tops out at a 4-bit file: "Strata serves a 125B
+ *                   MoE at 94 tokens/s ...", section "Quality is a sizing
+ *                   decision");
+ *       scales      [rows][K/32] fp16 bit patterns;
+ *     so a matrix takes rows*K*b/8 code bytes and rows*K/32 scales;
+ *   - kernel layout (what moe_qweights must hold): the same bytes rearranged
+ *     by moe_repack, once, when weights are uploaded.  Buffer sizes, plane
+ *     offsets and per-expert strides are the canonical ones; the placement
+ *     inside a matrix belongs to the kernels (it groups rows so that one
+ *     weight load reads one contiguous piece) and is not part of this ABI.
  * Expert matrices: gate [I][H], up [I][H] (K = H) and down [H][I] (K = I).
- * The expert kernels read one unit of 16 rows as one contiguous piece.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -104,9 +94,10 @@ typedef struct {
   int32_t qbits;        /* 2, 3 or 4 */
 } moe_shape;
 
-/* Quantised weights of a set of experts.  Matrix m (0 = gate, 1 = up,
- * 2 = down) of expert e starts at codes[m] + e * code_stride bytes, and its
- * scales at scales[m] + e * scale_stride fp16 elements.  codes[m] and
+/* Quantised weights of a set of experts, in the kernel layout (moe_repack).
+ * Matrix m (0 = gate, 1 = up, 2 = down) of expert e starts at codes[m] +
+ * e * code_stride bytes, and its scales at scales[m] + e * scale_stride fp16
+ * elements.  codes[m] and
  * code_stride must be multiples of 16 bytes; scales[m] must be 4-byte aligned
  * and scale_stride even. */
 typedef struct {
@@ -215,17 +206,30 @@ int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_lay
 int moe_rmsnorm_bf16(const float* r, int64_t T, int32_t H, uint16_t* a, void* stream);
 
 /* out[r][k] = (q - 2^(b-1)) * scale[r][k/32] in fp32 (exact) for one matrix
- * [rows][cols] in the block format above. */
+ * [rows][cols] in the canonical layout.  codes 8-byte, scales 2-byte and out
+ * 16-byte aligned. */
 int moe_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int32_t cols,
                 int32_t qbits, float* out, void* stream);
 
-/* Quantise fp32 w [rows][cols] to the block format (used to build synthetic
- * expert arenas).  Per block: m = signed element of largest magnitude (first
- * on ties), d = fp16_RNE(m / c_min), c = clamp(rint_half_even(w / d), c_min,
- * c_max), c = 0 for the whole block when d == 0 (then d is stored as +0);
- * all in fp32. */
+/* Quantise fp32 w [rows][cols] to the canonical layout (used to build
+ * synthetic expert arenas).  Per block: m = signed element of largest
+ * magnitude (first on ties), d = fp16_RNE(m / c_min), c = clamp(
+ * rint_half_even(w / d), c_min, c_max), c = 0 for the whole block when d == 0
+ * (then d is stored as +0); all in fp32.  codes 8-byte, scales 2-byte and w
+ * 16-byte aligned. */
 int moe_quantize(const float* w, int64_t rows, int32_t cols, int32_t qbits, uint8_t* codes,
                  uint16_t* scales, void* stream);
+
+/* Rearrange one matrix [rows][cols] from the canonical layout (codes,
+ * scales) into the kernel layout (packed_codes, packed_scales: the same byte
+ * counts, rows*cols*qbits/8 and rows*cols/32 * 2), the form moe_qweights
+ * holds.  Out of place: the output buffers must not overlap the inputs
+ * (MOE_ERR_INVALID_ARG).  Allocates nothing; asynchronous on `stream`.
+ * codes and packed_codes 8-byte aligned, scales and packed_scales 2-byte
+ * aligned.  A matrix of an arena is repacked on its own (its rows start a
+ * new row group), at the arena's per-expert offset. */
+int moe_repack(const uint8_t* codes, const uint16_t* scales, int64_t rows, int32_t cols, int32_t qbits,
+               uint8_t* packed_codes, uint16_t* packed_scales, void* stream);
 
 /* Synchronises `stream`, then returns MOE_ERR_INDEX if the most recent
  * moe_permute (or moe_layer_forward) on this workspace met an expert id

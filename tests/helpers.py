@@ -123,16 +123,29 @@ def check_route_protocol(gpu_logits, gpu_idx, gpu_w, oracle_logits, k):
     return flagged
 
 
+def _high3_word_bytes(four: np.ndarray) -> np.ndarray:
+    """The kernels' 3-bit high-plane word of a block: bit i of the block's
+    canonical word (code i) goes to bit 2i + 1 for codes 0..15 and to bit
+    2(i - 16) for codes 16..31."""
+    h = int.from_bytes(bytes(np.asarray(four, np.uint8)), "little")
+    out = 0
+    for i in range(32):
+        if (h >> i) & 1:
+            out |= 1 << (2 * i + 1 if i < 16 else 2 * (i - 16))
+    return np.frombuffer(out.to_bytes(4, "little"), np.uint8)
+
+
 def tile_quantised(codes: np.ndarray, scales: np.ndarray, rows: int, K: int, qbits: int):
-    """Row-major codes / scales (the oracle's quantiser: low plane [rows][K/4],
-    3-bit high plane [rows][K/8] or 4-bit high plane [rows][K/4] after it,
-    scales [rows][K/32]) rearranged
-    into the library's tiled storage: rows in groups of 16 (the last group
-    may be shorter), each 64-weight unit (two blocks) of a whole group
-    contiguous, row after row -- 16 low-plane bytes, 2 scales and 8
-    high-plane bytes per row and unit; with K % 64 == 32 the last unit of a
-    group is one block (8 bytes, 1 scale, 4 bytes per row).  The 4-bit high
-    plane is placed like the low plane."""
+    """The library's kernel layout (what moe_repack writes), restated from
+    its definition: canonical row-major codes / scales (the oracle's
+    quantiser: low plane [rows][K/4], 3-bit high plane [rows][K/8] or 4-bit
+    high plane [rows][K/4] after it, scales [rows][K/32]) rearranged into
+    rows in groups of 16 (the last group may be shorter), each 64-weight unit
+    (two blocks) of a whole group contiguous, row after row -- 16 low-plane
+    bytes, 2 scales and 8 high-plane bytes per row and unit; with K % 64 ==
+    32 the last unit of a group is one block (8 bytes, 1 scale, 4 bytes per
+    row).  The 4-bit high plane is placed like the low plane; each 3-bit
+    high-plane word of a block has its bits rearranged (_high3_word_bytes)."""
     nb, nuf = K // 32, K // 64
     lo = np.asarray(codes[: rows * K // 4]).reshape(rows, K // 4)
     sc = np.asarray(scales).reshape(rows, nb)
@@ -156,9 +169,118 @@ def tile_quantised(codes: np.ndarray, scales: np.ndarray, rows: int, K: int, qbi
             out_lo[co:co + 8] = lo[r, 8 * b:8 * b + 8]
             out_sc[so] = sc[r, b]
             if qbits == 3:
-                out_hi[ho:ho + 4] = hi[r, 4 * b:4 * b + 4]
+                out_hi[ho:ho + 4] = _high3_word_bytes(hi[r, 4 * b:4 * b + 4])
     if qbits == 4:  # the second plane has the low plane's layout: tile it the same way
         hi4, _ = tile_quantised(np.asarray(codes[rows * K // 4: rows * K // 2]), scales, rows, K, 2)
         return np.concatenate([out_lo, hi4]), out_sc
     out_codes = out_lo if qbits == 2 else np.concatenate([out_lo, out_hi])
     return out_codes, out_sc
+
+
+# ---------------------------------------------------------------------------
+# Stacked workloads: device stacks and on-demand oracle layers.
+# ---------------------------------------------------------------------------
+
+def build_device_stack(wl: synth.Workload, n_layers: int, device="cuda"):
+    """n_layers resident device layers of a workload (quantised arenas only;
+    the fp32 draws are dropped after quantising)."""
+    from bit_quantized_expert_amd import QArena, QLayer
+    s = wl.shape
+    layers = []
+    for l in range(n_layers):
+        w_r, bias = synth.router(wl, l, device)
+        arena = QArena(s.n_experts, s.hidden, s.inter, s.qbits, device)
+        for lo in range(0, s.n_experts, 128):
+            sl = slice(lo, min(s.n_experts, lo + 128))
+            for m, w in enumerate(synth.expert_weights(wl, l, device, experts=sl)):
+                arena.quantize_from(m, w, experts=sl)
+        sarena = None
+        sw = synth.shared_weights(wl, l, device)
+        if sw is not None:
+            sarena = QArena(1, s.hidden, s.shared_inter, s.qbits, device)
+            for m, w in enumerate(sw):
+                sarena.quantize_from(m, w[None])
+        layers.append(QLayer(w_r, bias, arena, sarena))
+    torch.cuda.synchronize()
+    return layers
+
+
+class _DenseExpert:
+    """An oracle expert whose dequantised matrices are computed once (the
+    stack tests evaluate the same experts several times per layer)."""
+
+    def __init__(self, q: O.QExpert):
+        self._dense = q.dense()
+
+    def dense(self):
+        return self._dense
+
+
+class OracleLayer:
+    """The oracle's view of layer `layer` of a workload: router in float64 and
+    experts quantised by the oracle from the same seeded fp32 draws, built on
+    demand (several experts at once on a thread pool: the numpy work releases
+    the interpreter lock)."""
+
+    def __init__(self, wl: synth.Workload, layer: int, device="cuda", threads: int | None = None):
+        import os
+        threads = threads or max(1, min(16, os.cpu_count() or 1))
+        self.wl, self.layer, self.s, self.device, self.threads = wl, layer, wl.shape, device, threads
+        w_r, bias = synth.router(wl, layer, device)
+        self.w_router = w_r.float().cpu().numpy().astype(np.float64)
+        self.bias = None if bias is None else bias.cpu().numpy().astype(np.float64)
+        self._experts: dict[int, O.QExpert] = {}
+        self._shared = None
+        sw = synth.shared_weights(wl, layer, device)
+        if sw is not None:
+            self._shared = O.QExpert.from_float(*(w.cpu().numpy() for w in sw), self.s.qbits)
+
+    def need(self, ids) -> None:
+        import concurrent.futures as cf
+        todo = sorted({int(e) for e in np.asarray(ids).ravel()} - set(self._experts))
+        draws = []
+        for e in todo:
+            g, u, d = synth.expert_weights(self.wl, self.layer, self.device, experts=slice(e, e + 1))
+            draws.append((e, g[0].cpu().numpy(), u[0].cpu().numpy(), d[0].cpu().numpy()))
+        qb = self.s.qbits
+        with cf.ThreadPoolExecutor(self.threads) as ex:
+            for e, q in zip(todo, ex.map(lambda t: _DenseExpert(O.QExpert.from_float(t[1], t[2], t[3], qb)), draws)):
+                self._experts[e] = q
+
+    class _View:
+        def __init__(self, ol):
+            self.ol = ol
+
+        def __len__(self):
+            return self.ol.s.n_experts
+
+        def __getitem__(self, e):
+            return self.ol._experts[int(e)]
+
+    def logits(self, a) -> np.ndarray:
+        return O.router_logits(a, self.w_router, self.bias)
+
+    def forward(self, a, idx, return_all=False):
+        """The oracle layer on activations a at the given selection idx (the
+        experts of idx must have been prepared with need())."""
+        return O.layer_forward(a, self.w_router, self.bias, OracleLayer._View(self), self._shared, self.s.top_k,
+                               return_all=return_all, idx=idx)
+
+
+def drift_tolerant_selection(own_logits, own_idx, gpu_idx, drift, k):
+    """End-to-end near-tie rule for stacks.  The oracle runs on its own
+    activations, which differ from the GPU's by bf16 rounding flips; the
+    logit perturbation that difference causes is `drift` per token (max
+    |oracle logits on its own activation - oracle logits on the GPU's|).  A
+    token whose oracle selection differs from the GPU's is accepted when
+    every differing rank is a swap whose oracle gap is within TIE_TAU + 2 *
+    drift, and is then evaluated at the GPU's selection.  Returns (idx to
+    evaluate, flagged tokens)."""
+    use = np.array(own_idx, copy=True)
+    flagged = np.where(np.any(own_idx != gpu_idx, axis=1))[0]
+    for t in flagged:
+        gap = np.abs(own_logits[t, gpu_idx[t]] - own_logits[t, own_idx[t]])
+        band = TIE_TAU + 2.0 * float(drift[t])
+        assert np.all(gap <= band), f"token {t}: selection differs beyond the near-tie band ({gap.max():.3e} > {band:.3e})"
+        use[t] = gpu_idx[t]
+    return use, flagged

@@ -21,7 +21,7 @@ def _shape(**kw):
 def test_exports_every_header_symbol():
     lib = L.lib()
     names = L.header_symbols()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
 
@@ -102,6 +102,17 @@ def test_validation_before_any_device_call():
     assert lib.moe_permute(fake, 4096, ctypes.byref(s), fake, fake, fake, fake, fake, 16, None) \
         == L.MOE_ERR_WORKSPACE
     assert lib.moe_read_error(None, 0, None) == L.MOE_ERR_INVALID_ARG
+    # repack argument checks: qbits, cols, NULL, alignment, overlapping buffers (out of place only)
+    assert lib.moe_repack(fake, fake, 4, 64, 5, fake, fake, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_repack(fake, fake, 4, 48, 2, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_repack(None, fake, 4, 64, 2, fake, fake, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_repack(ctypes.c_void_p(0x100004), fake, 4, 64, 2, ctypes.c_void_p(0x200000), fake, None) \
+        == L.MOE_ERR_INVALID_ARG
+    src, dst = 0x100000, 0x100000 + 4 * 64 // 4 - 8   # codes of 4 x 64 2-bit weights: 64 bytes; overlap by 8
+    assert lib.moe_repack(ctypes.c_void_p(src), ctypes.c_void_p(0x300000), 4, 64, 2, ctypes.c_void_p(dst),
+                          ctypes.c_void_p(0x400000), None) == L.MOE_ERR_INVALID_ARG
+    assert "overlap" in L.last_error_detail()
+    assert lib.moe_repack(None, None, 0, 64, 2, None, None, None) == L.MOE_OK
     # the GEMV kernels stage up to 16 token rows of `hidden` in LDS: asked for explicitly where that
     # does not fit (hidden 8192 at 16 tokens), the call is refused before any device work
     big = _shape(hidden=8192)
@@ -118,18 +129,42 @@ def test_validation_before_any_device_call():
 @pytest.mark.parametrize("rows,K,qbits", [(3, 32, 2), (17, 96, 3), (40, 64, 2), (33, 160, 3), (64, 704, 2),
                                            (5, 96, 4), (48, 704, 4)])
 def test_tiled_layout_is_a_permutation(rows, K, qbits):
-    """The tiled storage of the quantised matrices (as the tests restate it)
-    moves every byte of the row-major layout to a distinct place, so it keeps
-    the buffer sizes: tiling distinct byte values gives every value once."""
+    """The kernel layout (as the tests restate it) moves every piece of the
+    canonical layout to a distinct place, so it keeps the buffer sizes:
+    tiling distinct labels gives every label once.  Low planes (and the 4-bit
+    second plane) and scales move byte by byte / scale by scale; a 3-bit
+    high-plane word moves as a whole, with a bijection of its 32 bits."""
     import numpy as np
-    from tests.helpers import tile_quantised
-    n_codes, n_scales = rows * K * qbits // 8, rows * K // 32
+    from tests.helpers import _high3_word_bytes, tile_quantised
+    n_lo, n_scales = rows * K // 4, rows * K // 32
+    lo_planes = 2 if qbits == 4 else 1
+    n_codes = rows * K * qbits // 8
+    # byte / scale labels of the 2-bit-layout planes
     codes = np.arange(n_codes, dtype=np.int64)
     scales = np.arange(n_scales, dtype=np.int64)
-    # distinct labels instead of bytes: run the mapping on int64 arrays of positions
     tc, ts = _tile_positions(codes, scales, rows, K, qbits, tile_quantised)
-    assert sorted(tc.tolist()) == list(range(n_codes))
+    assert sorted(tc[:lo_planes * n_lo].tolist()) == list(range(lo_planes * n_lo))
     assert sorted(ts.tolist()) == list(range(n_scales))
+    if qbits == 3:
+        # word labels of the high plane: a label's bit b fills a whole word (all-ones words are fixed points
+        # of the bit rearrangement), so each output word spells the index of its source word
+        n_words = rows * K // 32
+        got = np.zeros(n_words, np.int64)
+        for b in range(max(1, int(n_words - 1).bit_length())):
+            hi = np.zeros(n_words * 4, np.uint8)
+            for wd in range(n_words):
+                if (wd >> b) & 1:
+                    hi[4 * wd:4 * wd + 4] = 0xFF
+            c = np.concatenate([np.zeros(n_lo, np.uint8), hi])
+            out, _ = tile_quantised(c, np.zeros(n_scales, np.uint16), rows, K, 3)
+            words = out[n_lo:].reshape(n_words, 4)
+            assert np.all((words == 0) | (words == 0xFF))
+            got |= (words[:, 0] == 0xFF).astype(np.int64) << b
+        assert sorted(got.tolist()) == list(range(n_words))
+        # within a word: a bijection of the 32 bit positions
+        images = [int.from_bytes(bytes(_high3_word_bytes(np.frombuffer((1 << i).to_bytes(4, "little"), np.uint8))),
+                                 "little") for i in range(32)]
+        assert all(bin(v).count("1") == 1 for v in images) and len(set(images)) == 32
     # a one-group matrix with K a multiple of 64 keeps each row's 16-byte units in row order
     if rows <= 16 and K % 64 == 0:
         first_unit = tc[:16 * rows].reshape(rows, 16)
@@ -138,7 +173,9 @@ def test_tiled_layout_is_a_permutation(rows, K, qbits):
 
 def _tile_positions(codes, scales, rows, K, qbits, tile):
     """tile() on position labels: the helper copies values, so labels that fit
-    its dtypes (uint8 bytes / uint16 scales) are tiled in chunks of 256 / 65536."""
+    its dtypes (uint8 bytes / uint16 scales) are tiled in chunks of 256 / 65536.
+    (The 3-bit high plane's bits are rearranged within words, so its byte
+    labels are not meaningful; the caller checks it separately.)"""
     import numpy as np
     out_c = np.zeros_like(codes)
     out_s = np.zeros_like(scales)

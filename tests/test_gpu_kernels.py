@@ -37,13 +37,67 @@ def test_quantize_and_dequant_bit_exact(qbits, rows, k):
     scales = torch.empty(rows * k // 32, dtype=torch.int16, device="cuda")
     M.quantize(w.cuda(), qbits, codes, scales)
     want_codes, want_scales = O.quantize(w.numpy(), qbits)
-    tiled_codes, tiled_scales = tile_quantised(want_codes, want_scales, rows, k, qbits)
-    assert np.array_equal(codes.cpu().numpy(), tiled_codes)
-    assert np.array_equal(scales.cpu().numpy().view(np.uint16), tiled_scales)
+    # the canonical layout, byte for byte
+    assert np.array_equal(codes.cpu().numpy(), want_codes)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), want_scales.reshape(-1))
     out = torch.empty(rows, k, dtype=torch.float32, device="cuda")
-    M.dequant(codes, scales, rows, k, qbits, out)  # the library's (tiled) storage in, the plain matrix out
+    M.dequant(codes, scales, rows, k, qbits, out)
     want = O.dequant(want_codes, want_scales, rows, k, qbits)
     assert np.array_equal(out.cpu().numpy().astype(np.float64), want)
+
+
+@pytest.mark.parametrize("qbits", [2, 3, 4])
+@pytest.mark.parametrize("rows,k", [(3, 32), (17, 64), (40, 96), (64, 704), (33, 2048)])
+def test_repack_matches_kernel_layout(qbits, rows, k):
+    """moe_repack of the oracle's canonical bytes gives the kernel layout as
+    the tests restate it from its definition."""
+    M = _lib()
+    w = _weights(rows, k, seed=rows * 7 + k)
+    want_codes, want_scales = O.quantize(w.numpy(), qbits)
+    codes = torch.from_numpy(want_codes).cuda()
+    scales = torch.from_numpy(want_scales.reshape(-1).view(np.int16)).cuda()
+    pc = torch.full_like(codes, 0xAB)
+    ps = torch.full_like(scales, 0x5A5A)
+    M.repack(codes, scales, rows, k, qbits, pc, ps)
+    tiled_codes, tiled_scales = tile_quantised(want_codes, want_scales, rows, k, qbits)
+    assert np.array_equal(pc.cpu().numpy(), tiled_codes)
+    assert np.array_equal(ps.cpu().numpy().view(np.uint16), tiled_scales)
+
+
+def test_layer_from_caller_canonical_codes():
+    """A caller holding canonical row-major codes (here: the oracle's own
+    quantiser output) uploads them, repacks them with moe_repack and runs the
+    layer: the output matches the oracle layer on those codes."""
+    from tests.helpers import assert_close_output
+    M = _lib()
+    H, I, E, k, Is, qb, T = 256, 192, 12, 3, 96, 3, 9
+    rng = np.random.default_rng(17)
+    experts = [O.QExpert.from_float(*(rng.normal(0, 0.02, sh).astype(np.float32)
+                                      for sh in ((I, H), (I, H), (H, I))), qb) for _ in range(E)]
+    shared = O.QExpert.from_float(*(rng.normal(0, 0.02, sh).astype(np.float32)
+                                    for sh in ((Is, H), (Is, H), (H, Is))), qb)
+    arena = M.QArena(E, H, I, qb, "cuda")
+    sarena = M.QArena(1, H, Is, qb, "cuda")
+    for m in range(3):
+        for e, ex in enumerate(experts):
+            c, sc = (ex.gate, ex.up, ex.down)[m]
+            arena.load_canonical(m, e, torch.from_numpy(c)[None].cuda(),
+                                 torch.from_numpy(sc.reshape(-1).view(np.int16))[None].cuda())
+        c, sc = (shared.gate, shared.up, shared.down)[m]
+        sarena.load_canonical(m, 0, torch.from_numpy(c)[None].cuda(),
+                              torch.from_numpy(sc.reshape(-1).view(np.int16))[None].cuda())
+    w_r = (torch.from_numpy(rng.normal(0, 0.02, (E, H)).astype(np.float32))).to(torch.bfloat16).cuda()
+    q = M.QLayer(w_r, None, arena, sarena)
+    s = synth.MoEShape(H, I, E, k, Is, qb)
+    x = torch.from_numpy(rng.normal(size=(T, H)).astype(np.float32)).to(torch.bfloat16).cuda()
+    for algo in ("gemv", "grouped"):
+        out = torch.empty(T, H, device="cuda")
+        idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        M.layer_forward(x, q, s, out=out, topk_idx=idx, algo=algo, ws=M.alloc_workspace(s, T, algo=algo))
+        torch.cuda.synchronize()
+        ref = O.layer_forward(x.float().cpu().numpy().astype(np.float64), w_r.float().cpu().numpy().astype(np.float64),
+                              None, experts, shared, k, idx=idx.cpu().numpy())
+        assert_close_output(out.cpu().numpy(), ref, f"canonical codes, {algo}")
 
 
 def _route(M, wl, T, layer=0):
@@ -203,3 +257,39 @@ def test_permute_out_of_range_ids_are_reported(T):
         M.read_error(ws)
     assert ei.value.status == -5
     M.read_error(ws)  # cleared
+
+
+def test_permute_error_survives_expert_ffn():
+    """An out-of-range id recorded by moe_permute is still reported after
+    moe_expert_ffn ran on the same workspace (the FFN's plan leaves the
+    record alone)."""
+    M = _lib()
+    E, k, T = 16, 2, 5
+    wl = synth.custom("err", 64, 32, E, k, 32, 2, T, seed=3, act_dtype=torch.bfloat16)
+    s = wl.shape
+    arena = M.QArena(E, 64, 32, 2, "cuda")
+    for m, (r, c) in enumerate(arena.mat_shapes):
+        arena.quantize_from(m, torch.zeros(E, r, c, device="cuda"))
+    sarena = M.QArena(1, 64, 32, 2, "cuda")
+    for m, (r, c) in enumerate(sarena.mat_shapes):
+        sarena.quantize_from(m, torch.zeros(1, r, c, device="cuda"))
+    q = M.QLayer(torch.zeros(E, 64, dtype=torch.bfloat16, device="cuda"), None, arena, sarena)
+    rng = np.random.default_rng(4)
+    idx_np = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    idx_np[3, 1] = E + 7
+    for algo in ("gemv", "grouped"):
+        ws = M.alloc_workspace(s, T, algo=algo)
+        idx = torch.from_numpy(idx_np.astype(np.int32)).cuda()
+        counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+        pp = torch.empty_like(sp)
+        M.permute(idx, T, s, counts, offsets, sp, pp, ws)
+        x = synth.tokens(wl, "cuda")
+        y = torch.empty(T * k, 64, device="cuda")
+        so = torch.empty(T, 64, device="cuda")
+        M.expert_ffn(x, q, s, offsets, sp, y, so, algo=algo, ws=ws)
+        with pytest.raises(M.MoeError) as ei:
+            M.read_error(ws)
+        assert ei.value.status == -5, algo
+        M.read_error(ws)  # cleared

@@ -75,6 +75,10 @@ RAGGED = [
     ("s3", 128, 160, 12, 4, 0, 2, 1, torch.bfloat16),
     ("s4", 256, 192, 33, 8, 96, 3, 1, torch.bfloat16),
     ("s5", 192, 128, 40, 32, 64, 2, 1, torch.bfloat16),
+    # one token whose 33 (or 9) h rows are more than the single-token down + combine kernel can
+    # stage in LDS: the layer takes the multi-token decode kernels instead
+    ("s6", 64, 2560, 40, 32, 64, 2, 1, torch.bfloat16),
+    ("s7", 64, 64, 16, 8, 20480, 3, 1, torch.bfloat16),
     # the 4-bit format on each decode path: per-slot kernels (37 tokens; hidden not a multiple
     # of 1024), the single-token fused path (32-weight down units), the persistent kernels with
     # the in-kernel selection (bf16 and fp32 tokens)

@@ -178,3 +178,78 @@ def test_grouped_stack_glue(case):
     want_a = O.rmsnorm_bf16(r.cpu().numpy().astype(np.float64))
     diff = a.float().cpu().numpy() != want_a
     assert np.mean(diff) < 1e-3
+
+
+def _stepwise(M, dl, x, algo):
+    """route -> permute -> expert_ffn (fp32 y_sorted, shared_out) -> combine,
+    each through its own entry point."""
+    s = dl.s
+    T = x.shape[0]
+    ws = M.alloc_workspace(s, T, algo=algo)
+    idx = torch.empty(T, s.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, s.top_k, device="cuda")
+    M.route(x, dl.q, s, idx, w, ws=ws)
+    counts = torch.empty(s.n_experts, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(s.n_experts + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * s.top_k, dtype=torch.int32, device="cuda")
+    pp = torch.empty_like(sp)
+    M.permute(idx, T, s, counts, offsets, sp, pp, ws)
+    y = torch.empty(T * s.top_k, s.hidden, device="cuda")
+    so = torch.empty(T, s.hidden, device="cuda") if s.shared_inter else None
+    M.expert_ffn(x, dl.q, s, offsets, sp, y, so, algo=algo, ws=ws)
+    out = torch.empty(T, s.hidden, device="cuda")
+    M.combine(y, pp, w, so, T, s, out=out)
+    torch.cuda.synchronize()
+    return idx, w, offsets, sp, pp, y, so, out
+
+
+@pytest.mark.parametrize("case", [c for c in RAGGED if c[0] in ("g3", "g5", "w2", "w4", "b1", "k3", "q6", "m3")],
+                         ids=lambda c: c[0])
+def test_grouped_expert_ffn_standalone(case):
+    """moe_expert_ffn with the grouped GEMM writes fp32 y_sorted and
+    shared_out (not the fp16 hand-off of the layer): every row against the
+    oracle's expert outputs in sorted order and its shared expert, and the
+    combine of them against the oracle layer."""
+    M = _M()
+    name, H, I, E, k, Is, qb, T, dt = case
+    wl = synth.custom(name, H, I, E, k, Is, qb, T, seed=27, act_dtype=dt, zipf_bias=True)
+    dl = _layer(wl)
+    x = synth.tokens(wl, "cuda")
+    idx, w, offsets, sp, pp, y, so, out = _stepwise(M, dl, x, "grouped")
+    ref = dl.oracle_forward(x_to_numpy(x), idx=idx.cpu().numpy(), return_all=True)
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(sp.cpu().numpy(), ref["sorted_pair"])
+    assert_close_output(y.cpu().numpy(), ref["y"], f"{name} y_sorted")
+    if so is not None:
+        assert_close_output(so.cpu().numpy(), ref["shared"], f"{name} shared_out")
+    assert_close_output(out.cpu().numpy(), ref["out"], f"{name} combine")
+
+
+def test_grouped_expert_ffn_standalone_4k_sampled():
+    """The same at the 3-bit 4,096-token layer: a sample of sorted positions
+    (first and last of a few experts, random others) and of shared-expert
+    rows, each computed by the oracle on its own."""
+    from oracle import moe_oracle as O
+    M = _M()
+    wl = synth.WORKLOADS["prefill3"]
+    dl = _layer(wl)
+    s = dl.s
+    x = synth.tokens(wl, "cuda")
+    idx, w, offsets, sp, pp, y, so, out = _stepwise(M, dl, x, "grouped")
+    off = offsets.cpu().numpy()
+    spn = sp.cpu().numpy()
+    rng = np.random.default_rng(9)
+    experts = rng.choice(s.n_experts, 6, replace=False)
+    pos = [p for e in experts for p in (off[e], off[e + 1] - 1) if off[e + 1] > off[e]]
+    pos = np.unique(np.concatenate([pos, rng.choice(len(spn), 10, replace=False)]))
+    xn = x_to_numpy(x)
+    got = y[torch.from_numpy(pos).cuda()].cpu().numpy()
+    want = np.zeros_like(got, dtype=np.float64)
+    for i, p in enumerate(pos):
+        e = int(np.searchsorted(off, p, side="right") - 1)
+        t = spn[p] // s.top_k
+        want[i] = O.swiglu(xn[t:t + 1], *dl.oracle_expert(e).dense())[0]
+    assert_close_output(got, want, "4k y_sorted sampled")
+    rows = np.array([0, 1, 2047, 4095])
+    want_s = O.swiglu(xn[rows], *dl.oracle_shared().dense())
+    assert_close_output(so[torch.from_numpy(rows).cuda()].cpu().numpy(), want_s, "4k shared_out sampled")

@@ -361,6 +361,31 @@ def test_stack_two_layers_brute_force():
     assert np.allclose(r, rr, rtol=1e-14, atol=0)
 
 
+def test_stack_teacher_forcing():
+    """Teacher forcing replaces a layer's activation and nothing else.
+    Closed form: zero activations at every layer give zero layer outputs
+    (silu(0) * 0 = 0 for every expert), so the residual stays x0 exactly.
+    Brute force: a 2-layer stack whose layer 1 is fed a foreign activation a*
+    equals x0 + MoE_0(a_0) + MoE_1(a*) with a_0 the normalised x0 from
+    pure-Python loops."""
+    layers = [_tiny_layer(seed=30 + l, bias=True) for l in range(3)]
+    x0 = np.random.default_rng(33).normal(size=(3, 64))
+    r, acts, outs = O.stack_forward(x0, layers, 2, teacher=lambda l: np.zeros((3, 64)))
+    assert np.array_equal(r, x0)
+    assert all(np.array_equal(o, np.zeros((3, 64))) for o in outs)
+    a_star = O.bf16_round(np.random.default_rng(34).normal(size=(3, 64)))
+    ms = np.array([sum(v * v for v in row) / 64 for row in x0])
+    a0 = O.bf16_round(x0 / np.sqrt(ms + 1e-6)[:, None])
+    r, acts, outs = O.stack_forward(x0, layers[:2], 2, teacher=lambda l: a0 if l == 0 else a_star)
+    assert np.array_equal(acts[1], a_star)
+    want = x0 + O.layer_forward(a0, *layers[0], 2) + O.layer_forward(a_star, *layers[1], 2)
+    assert np.allclose(r, want, rtol=1e-14, atol=0)
+    # and with the oracle's own activations fed back, teacher forcing changes nothing
+    r_plain, acts_plain, _ = O.stack_forward(x0, layers, 2)
+    r_tf, _, _ = O.stack_forward(x0, layers, 2, teacher=lambda l: acts_plain[l])
+    assert np.array_equal(r_plain, r_tf)
+
+
 # ---------------------------------------------------------------- sizes
 
 def test_byte_census_matches_pages():
