@@ -64,6 +64,8 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP]),
     "moe_layer_forward": (ctypes.c_int, [_VP, ctypes.c_int, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                                          _VP]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [_VP, ctypes.c_int, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                 _VP]),
     "moe_rmsnorm_bf16": (ctypes.c_int, [_VP, _I64, _I32, _VP, _VP]),
     "moe_dequant": (ctypes.c_int, [_VP, _VP, _I64, _I32, _I32, _VP, _VP]),
     "moe_quantize": (ctypes.c_int, [_VP, _I64, _I32, _I32, _VP, _VP, _VP]),
@@ -282,6 +284,17 @@ def layer_forward(x, layer: QLayer, shape, out=None, residual=None, next_in=None
                                    ctypes.byref(Shape.of(shape)), _ptr(out), _ptr(residual), _ptr(next_in),
                                    _ptr(topk_idx), _ptr(topk_w), ctypes.byref(_opts(algo)), wp, wn,
                                    _stream(stream)), "moe_layer_forward")
+
+
+def layer_forward_noalloc(x, layer: QLayer, shape, out=None, residual=None, next_in=None, topk_idx=None,
+                          topk_w=None, algo="auto", stream=None) -> None:
+    """moe_layer_forward without a workspace argument (the library's own
+    per-GPU scratch array; shapes up to MOE_NOALLOC_SCRATCH_BYTES of
+    workspace)."""
+    _check(lib().moe_layer_forward_noalloc(_ptr(x), _dtype_code(x), x.shape[0], ctypes.byref(layer.c_struct()),
+                                           ctypes.byref(Shape.of(shape)), _ptr(out), _ptr(residual), _ptr(next_in),
+                                           _ptr(topk_idx), _ptr(topk_w), ctypes.byref(_opts(algo)), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def rmsnorm_bf16(r, a, stream=None) -> None:

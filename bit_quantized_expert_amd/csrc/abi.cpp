@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "launch.h"
@@ -436,25 +437,33 @@ int moe_combine(const float* y_sorted, const int32_t* pair_pos, const float* top
   }
 }
 
-int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer, const moe_shape* shape,
-                      float* out, float* residual, uint16_t* next_in_bf16, int32_t* topk_idx, float* topk_w,
-                      const moe_options* opts, void* workspace, size_t workspace_bytes, void* stream) {
-  try {
-    if (int r = check_shape(shape)) return r;
-    if (int r = check_T(T, shape)) return r;
-    if (int r = check_opts(opts)) return r;
-    if (int r = check_layer(layer, shape, true, true)) return r;
-    if (int r = check_dtype(x_dtype, "x")) return r;
-    if (T == 0) return ok();
-    if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
-    if (!out && !residual) return fail(MOE_ERR_INVALID_ARG, "one of out and residual must be non-NULL");
-    if (next_in_bf16 && !residual) return fail(MOE_ERR_INVALID_ARG, "next_in_bf16 needs residual");
-    for (const void* p : {(const void*)x, (const void*)out, (const void*)residual})
-      if (p && !aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "x, out and residual must be 16-byte aligned");
-    const WsLayout W = ws_layout(*shape, T);
-    if (int r = check_ws(workspace, workspace_bytes, W.total)) return r;
-    hipStream_t st = as_stream(stream);
-    void* ws = workspace;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the whole layer (both entry points), before any HIP call.
+int check_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer, const moe_shape* shape,
+                        const float* out, const float* residual, const uint16_t* next_in_bf16,
+                        const moe_options* opts) {
+  if (int r = check_shape(shape)) return r;
+  if (int r = check_T(T, shape)) return r;
+  if (int r = check_opts(opts)) return r;
+  if (int r = check_layer(layer, shape, true, true)) return r;
+  if (int r = check_dtype(x_dtype, "x")) return r;
+  if (T == 0) return MOE_OK;
+  if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+  if (!out && !residual) return fail(MOE_ERR_INVALID_ARG, "one of out and residual must be non-NULL");
+  if (next_in_bf16 && !residual) return fail(MOE_ERR_INVALID_ARG, "next_in_bf16 needs residual");
+  for (const void* p : {(const void*)x, (const void*)out, (const void*)residual})
+    if (p && !aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "x, out and residual must be 16-byte aligned");
+  return MOE_OK;
+}
+
+// The layer on a checked workspace of W.total bytes at ws.
+int layer_forward_ws(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer, const moe_shape* shape,
+                     float* out, float* residual, uint16_t* next_in_bf16, int32_t* topk_idx, float* topk_w,
+                     const moe_options* opts, void* ws, const WsLayout& W, hipStream_t st) {
+  {
     int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, W.topk_idx);
     float* w = topk_w ? topk_w : at<float>(ws, W.topk_w);
     const moe_algo algo = pick_algo(opts, T, shape);
@@ -485,8 +494,75 @@ int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_lay
            : moe::launch_combine(y, pair_pos, w, s_out, T, shape->hidden, shape->top_k, out, residual,
                                  next_in_bf16, st);
     return device_status(e, "moe_layer_forward/combine");
+  }
+}
+
+// ---- the no-allocation variant: its workspace is a file-scope device array.
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// only the address hipGetSymbolAddress returns for the current device is
+// used (kernel arguments and every other host-side use).
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up once
+// per device.
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "moe_layer_forward_noalloc/hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, "moe_layer_forward_noalloc/hipGetSymbolAddress");
+    if (!p || !aligned(p, kAlign)) return fail(MOE_ERR_DEVICE, "scratch array address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer, const moe_shape* shape,
+                      float* out, float* residual, uint16_t* next_in_bf16, int32_t* topk_idx, float* topk_w,
+                      const moe_options* opts, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (int r = check_layer_forward(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, opts)) return r;
+    if (T == 0) return ok();
+    const WsLayout W = ws_layout(*shape, T);
+    if (int r = check_ws(workspace, workspace_bytes, W.total)) return r;
+    return layer_forward_ws(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, topk_idx, topk_w, opts,
+                            workspace, W, as_stream(stream));
   } catch (...) {
     return fail(MOE_ERR_DEVICE, "moe_layer_forward: unexpected exception");
+  }
+}
+
+int moe_layer_forward_noalloc(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer,
+                              const moe_shape* shape, float* out, float* residual, uint16_t* next_in_bf16,
+                              int32_t* topk_idx, float* topk_w, const moe_options* opts, void* stream) {
+  try {
+    if (int r = check_layer_forward(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, opts)) return r;
+    if (T == 0) return ok();
+    const WsLayout W = ws_layout(*shape, T);
+    if (W.total > kScratchBytes)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_layer_forward_noalloc: this shape needs %zu bytes of workspace at T=%lld; "
+                  "the scratch array holds %zu (use moe_layer_forward with a workspace)", W.total, (long long)T,
+                  kScratchBytes);
+    void* ws = nullptr;
+    if (int r = scratch_of_current_device(&ws)) return r;
+    return layer_forward_ws(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, topk_idx, topk_w, opts, ws, W,
+                            as_stream(stream));
+  } catch (...) {
+    return fail(MOE_ERR_DEVICE, "moe_layer_forward_noalloc: unexpected exception");
   }
 }
 

@@ -201,6 +201,27 @@ int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_lay
                       const moe_options* opts, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the whole
+ * layer exactly as moe_layer_forward computes it (same kernels, same bits),
+ * with its workspace taken from a scratch array the library holds on each
+ * GPU instead of from the caller.  The array has MOE_NOALLOC_SCRATCH_BYTES
+ * (16 MiB: every shape whose moe_workspace_bytes fits, e.g. the full-shape
+ * layer of 512 experts, top-10, hidden 2048, inter 704 up to 155 tokens); it
+ * comes with the library's device code on each GPU the library runs on and
+ * is held until the process ends.  A larger shape
+ * returns MOE_ERR_UNSUPPORTED before any device work.  The call allocates
+ * nothing.  Every call on one GPU uses that GPU's one array, which keeps the
+ * previous call's contents (the layer needs nothing in it zeroed): calls that
+ * overlap on one GPU (other streams, other threads) race, so serialise them
+ * on one stream.  The first call on a device looks the array up on that
+ * device (hipGetSymbolAddress). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int moe_layer_forward_noalloc(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer,
+                              const moe_shape* shape, float* out, float* residual,
+                              uint16_t* next_in_bf16, int32_t* topk_idx, float* topk_w,
+                              const moe_options* opts, void* stream);
+
 /* a[t] = bf16_RNE(r[t] / sqrt(mean(r[t]^2) + 1e-6)) for r [T][H] fp32 (the
  * input of the first layer of a stack). */
 int moe_rmsnorm_bf16(const float* r, int64_t T, int32_t H, uint16_t* a, void* stream);

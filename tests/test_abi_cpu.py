@@ -21,7 +21,7 @@ def _shape(**kw):
 def test_exports_every_header_symbol():
     lib = L.lib()
     names = L.header_symbols()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
 
@@ -113,6 +113,14 @@ def test_validation_before_any_device_call():
                           ctypes.c_void_p(0x400000), None) == L.MOE_ERR_INVALID_ARG
     assert "overlap" in L.last_error_detail()
     assert lib.moe_repack(None, None, 0, 64, 2, None, None, None) == L.MOE_OK
+    # the no-allocation layer: checks as moe_layer_forward, then the scratch limit, all before any device call
+    assert lib.moe_layer_forward_noalloc(None, 1, 4, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None,
+                                         None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_forward_noalloc(fake, 1, 0, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None,
+                                         None, None, None) == L.MOE_OK
+    assert lib.moe_layer_forward_noalloc(fake, 1, 4096, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None,
+                                         None, None, None) == L.MOE_ERR_UNSUPPORTED
+    assert "scratch" in L.last_error_detail()
     # the GEMV kernels stage up to 16 token rows of `hidden` in LDS: asked for explicitly where that
     # does not fit (hidden 8192 at 16 tokens), the call is refused before any device work
     big = _shape(hidden=8192)
