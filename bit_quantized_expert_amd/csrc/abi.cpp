@@ -46,7 +46,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 constexpr int kMinTileBM = 32;
 
 struct WsLayout {
-  size_t header, slots, tile_expert, tile_m0, chunk_hist, h_routed, h_shared;
+  size_t header, slots, tile_expert, tile_m0, chunk_hist, h_routed, h_shared, x16;
   size_t end_perm, end_ffn;
   size_t logits, end_route;
   size_t topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos, slot_expert, y_sorted, shared_out, total;
@@ -74,6 +74,7 @@ WsLayout ws_layout(const moe_shape& s, int64_t T) {
   L.end_perm = off;
   L.h_routed = take(size_t(P) * s.inter * 2);
   L.h_shared = take(size_t(T) * s.shared_inter * 2);
+  L.x16 = take(size_t(T) * s.hidden * 2);
   L.end_ffn = off;
   L.logits = take(size_t(T) * E * 4);
   L.end_route = off;
@@ -238,6 +239,7 @@ moe::FfnArgs ffn_args(const void* x, moe_dtype xd, int64_t T, const moe_layer* L
   a.tile_m0 = at<int32_t>(ws, W.tile_m0);
   a.h_routed = at<_Float16>(ws, W.h_routed);
   a.h_shared = at<_Float16>(ws, W.h_shared);
+  a.x16 = at<_Float16>(ws, W.x16);
   a.y_sorted = y_sorted;
   a.shared_out = shared_out;
   return a;

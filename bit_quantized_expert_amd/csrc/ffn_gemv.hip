@@ -646,32 +646,21 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(FfnArgs a) {
 // to the MFMAs.  Accumulation classes and orders are those of the kernels
 // above, so results are bit-identical to the single-token path.
 // ---------------------------------------------------------------------------
-#ifndef MOE_TP_D
-#define MOE_TP_D 4
-#endif
-#ifndef MOE_TP_NW
-#define MOE_TP_NW 4
-#endif
-#ifndef MOE_TP_MINW
-#define MOE_TP_MINW 1
-#endif
-#ifndef MOE_TP_EARLY
-#define MOE_TP_EARLY 2
-#endif
-#ifndef MOE_GEMV_PERS
-#define MOE_GEMV_PERS 1
-#endif
+constexpr int kTpD = 4;      // rounds of weight loads in flight in the per-slot gate/up kernel
+constexpr int kTpNW = 4;     // row blocks (waves of gate rows) per workgroup of the per-slot kernels
+constexpr int kTpMinW = 1;   // workgroups per CU asked of the per-slot gate/up kernel
+constexpr int kTpEarly = 2;  // items per thread of an early activation staging
 constexpr int kPersGrid = 512;       // persistent gate/up workgroups (two per CU)
 constexpr int kPersGridDown = 1024;  // persistent down workgroups (four per CU)
 // NW row blocks of 16 per workgroup; waves 0..NW-1 take the gate rows of
 // block wv, waves NW..2NW-1 the up rows (half the dequantisation per wave);
 // the up sums reach the gate waves through LDS for the SwiGLU.
 template <int QBITS, int UNIT, typename XT, int NW>
-__global__ __launch_bounds__(128 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(FfnArgs a) {
+__global__ __launch_bounds__(128 * NW, kTpMinW) void gemv_gateup_tp_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) f16 xs[];
   __shared__ float4v up_x[NW][64];  // the up waves' sums, per lane
   constexpr int kThreads = 128 * NW;  // the launch's block size (blockDim would be a load)
-  constexpr int D = MOE_TP_D;
+  constexpr int D = kTpD;
   static_assert(D % 4 == 0, "the pipeline depth is a multiple of the 4 accumulation classes");
   const int4 si = a.slots[blockIdx.y];
   const int m_total = si.z;
@@ -705,7 +694,7 @@ __global__ __launch_bounds__(128 * NW, MOE_TP_MINW) void gemv_gateup_tp_kernel(F
     __syncthreads();
   }
   constexpr int NB = sizeof(XT) == 4 ? 2 : 4;  // staging items per thread per batch
-  constexpr int NBE = MOE_TP_EARLY;             // items per thread of an early staging (registers held
+  constexpr int NBE = kTpEarly;             // items per thread of an early staging (registers held
                                                 // across the weight loads)
   const int chunks = H / 16;
 
@@ -1303,7 +1292,7 @@ __global__ __launch_bounds__(256) void gemv_down_pers_kernel(FfnArgs a, int ldsw
 // ---------------------------------------------------------------------------
 template <int QBITS>
 static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases) {
-  constexpr int NW = MOE_TP_NW;
+  constexpr int NW = kTpNW;
   const int64_t P = a.T * a.k;
   const int slots = int(std::min<int64_t>(a.E, P)) + (a.has_shared ? 1 : 0);
   const int mrows = int(std::min<int64_t>(kGemvMaxM, std::max<int64_t>(a.T, 1)));
@@ -1321,7 +1310,7 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
 #undef GU
     } else {
       const size_t lds = size_t(mrows) * (a.H + 8) * sizeof(f16);
-      const bool pers = MOE_GEMV_PERS && a.T <= kGemvMaxM && u64 && a.H % 1024 == 0 &&
+      const bool pers = a.T <= kGemvMaxM && u64 && a.H % 1024 == 0 &&
                         (!a.has_shared || a.Is == a.I);
       if (pers) {
         const int n_rb = (a.I + 63) / 64;
@@ -1354,7 +1343,7 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
       const int ldsw = kmax + 8;
       const size_t lds = size_t(mrows) * ldsw * sizeof(f16);
       const int rounds = (a.I / 64 + 3) / 4;
-      const bool pers = MOE_GEMV_PERS && a.T <= kGemvMaxM && a.I % 64 == 0 && rounds <= 4 &&
+      const bool pers = a.T <= kGemvMaxM && a.I % 64 == 0 && rounds <= 4 &&
                         (!a.has_shared || a.Is == a.I);
       if (pers) {
         const int n_rb = (a.H + 63) / 64;
@@ -1382,7 +1371,7 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
 hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t stream) {
   const int64_t P = a.T * a.k;
   const size_t lds_p = size_t(a.T) * (a.H + 8) * sizeof(f16);
-  const bool ok = MOE_GEMV_PERS && a.T >= 2 && a.T <= kGemvMaxM && a.H % 1024 == 0 &&
+  const bool ok = a.T >= 2 && a.T <= kGemvMaxM && a.H % 1024 == 0 &&
                   (!a.has_shared || a.Is == a.I) && a.E <= kSelPersMaxExperts && P <= 1024 &&
                   lds_p + 16384 <= kLdsBytes;
   if (!ok) return hipErrorNotSupported;

@@ -26,62 +26,20 @@
 
 namespace moe {
 
-// Waves per workgroup: 8 (BM x 512 tiles, one workgroup per CU) with 128-row
-// tiles; 4 (BM x 256, two workgroups per CU, so that one's prologue and
-// epilogue overlap the other's MFMAs) with the 96-row tiles of short segments
-// (measured on the 3-bit 4,096-token layer: gate/up -2%, down -8%; with
-// 128-row tiles 4 waves were no faster).
-#ifndef MOE_GROUPED2_WAVES
-#define MOE_GROUPED2_WAVES(BM) ((BM) == 96 ? 4 : 8)
-#endif
-#ifndef MOE_GROUPED2_PD
-#define MOE_GROUPED2_PD 1
-#endif
 
-// Raw A operand of one thread for one K step: two 16-element groups.
-template <typename AT>
-struct ARaw {
-  uint4v v[2][sizeof(AT) == 4 ? 4 : 2];  // fp32: 64 B per group; 16-bit: 32 B
-};
-
-template <typename AT>
-__device__ __forceinline__ void load_araw(const AT* src, ARaw<AT>& r, int i) {
-  const uint4v* p = reinterpret_cast<const uint4v*>(src);
-#pragma unroll
-  for (int q = 0; q < (sizeof(AT) == 4 ? 4 : 2); ++q) r.v[i][q] = p[q];
-}
-
-// Convert one raw group to the two permuted fp16 slices (the order of
-// load_x16: lo = weights {0,8,1,9,2,10,3,11}, hi = {4,12,5,13,6,14,7,15}).
-template <typename AT>
-__device__ __forceinline__ void cvt_araw(const ARaw<AT>& r, int i, half8& lo, half8& hi) {
-  if constexpr (std::is_same<AT, f16>::value) {  // h: already fp16 in the permuted order
-    lo = __builtin_bit_cast(half8, r.v[i][0]);
-    hi = __builtin_bit_cast(half8, r.v[i][1]);
-  } else {
-    float v[16];
-    if constexpr (sizeof(AT) == 4) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[4 * q + u] = __uint_as_float(r.v[i][q][u]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          v[8 * q + 2 * u] = __uint_as_float(r.v[i][q][u] << 16);
-          v[8 * q + 2 * u + 1] = __uint_as_float(r.v[i][q][u] & 0xffff0000u);
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      lo[2 * q] = f16(v[q]);
-      lo[2 * q + 1] = f16(v[q + 8]);
-      hi[2 * q] = f16(v[4 + q]);
-      hi[2 * q + 1] = f16(v[12 + q]);
-    }
-  }
+// The activations of the gate/up GEMM, converted once per call into x16: an
+// fp16 copy of x [T][H] whose 16-element groups hold the permuted order the
+// dequantiser produces (load_x16: {0,8,1,9,...} then {4,12,5,13,...}), so
+// that staging an A tile is a plain copy for every n-tile that reads it.
+template <typename XT>
+__global__ __launch_bounds__(256) void x16_kernel(const XT* __restrict__ x, int64_t groups, f16* __restrict__ x16) {
+  const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= groups) return;
+  half8 lo, hi;
+  load_x16<XT>(x + g * 16, lo, hi);
+  half8* d = reinterpret_cast<half8*>(x16 + g * 16);
+  d[0] = lo;
+  d[1] = hi;
 }
 
 // ---------------------------------------------------------------------------
@@ -110,46 +68,69 @@ struct BRaw2 {
   uint32_t v;                  // bit b: block 2h + b exists (else its scale reads as 0 in dq_b2)
 };
 
+// Where a lane's weights of step 0 start, for K a multiple of 64 (KM >= 1):
+// with 16-row groups of whole 64-weight units, block 4 step + 2h of row r
+// sits at a fixed offset plus step * 512 code bytes (step * 64 scales, step *
+// 256 3-bit high-plane bytes), so a step's loads are base + step * stride.
+// Rows past the matrix use row 0 (zeroed at dequantisation).
+struct BSrc {
+  const uint8_t* c;    // low plane
+  const uint16_t* s;   // scales
+  const uint8_t* hp;   // 3-bit high plane / 4-bit second plane
+};
+
+// (Unit h of the row, written out: with K == 64 unit 1 does not exist, and
+// lane h = 1 only ever reads it at the half step, one unit back.)
+template <int QBITS>
+__device__ __forceinline__ BSrc bsrc_k64(const uint8_t* codes, const uint16_t* scales, int rows, int K, int row,
+                                         int h, bool ok) {
+  const QTile tl = qtile<true>(ok ? row : 0, rows);  // weight rows are multiples of 32: every group is full
+  BSrc b;
+  b.c = codes + tl.g0 * (K / 4) + h * 256 + tl.rr * 16;
+  b.s = scales + tl.g0 * (K / 32) + h * 32 + tl.rr * 2;
+  const uint8_t* plane = codes + int64_t(rows) * (K / 4);
+  b.hp = QBITS == 3 ? plane + tl.g0 * (K / 8) + h * 128 + tl.rr * 8 : plane + tl.g0 * (K / 4) + h * 256 + tl.rr * 16;
+  return b;
+}
+
 // KM >= 1: K is a multiple of 64 (even block count per row), so a lane's two
 // blocks are in or out together and its 16 code bytes, 4 scale bytes (and
 // 8 high-plane bytes) are aligned for single loads.
 // A half step (K % 128 == 64, the last step: blocks 4 step and 4 step + 1
 // only) is loaded by both lanes of a column from the first block: lane h then
 // dequantises block 4 step + h alone (dq_b2 with sel), and the step runs half
-// the MFMAs.
+// the MFMAs.  `step` is clamped to the last one (a prefetch past the end
+// loads a real address and is zeroed).
 template <int QBITS, int KM>
+__device__ __forceinline__ void load_b2k(BRaw2<QBITS>& r, const BSrc& b, int K, int step, int nsteps, int h, bool ok) {
+  const bool in = ok && step < nsteps;
+  const int st = min(step, nsteps - 1);
+  const bool half_step = KM == 2 && 4 * st + 2 >= K / 32;  // only blocks 4 step, 4 step + 1 (K % 128 == 64)
+  const int back = half_step ? h : 0;                         // lane h = 1 reads its column's first block
+  r.c = *reinterpret_cast<const uint4v*>(b.c + st * 512 - back * 256);
+  r.s = *reinterpret_cast<const uint32_t*>(b.s + st * 64 - back * 32);
+  if constexpr (QBITS == 3) {
+    const uint2v hv = *reinterpret_cast<const uint2v*>(b.hp + st * 256 - back * 128);
+    r.hb[0] = hv[0];
+    r.hb[1] = hv[1];
+  }
+  if constexpr (QBITS == 4) {
+    const uint4v hv = *reinterpret_cast<const uint4v*>(b.hp + st * 512 - back * 256);
+    r.hb[0] = hv[0];
+    r.hb[1] = hv[1];
+    r.hb[2] = hv[2];
+    r.hb[3] = hv[3];
+  }
+  r.v = in ? 3u : 0u;
+}
+
+// Any K (a multiple of 32): one load per block (8 code bytes, one scale: a K
+// with an odd block count ends in a one-block unit), each unconditional from
+// a clamped address; blocks of this lane b0 = 4 * step + 2h and b0 + 1, each
+// zero past K or past the matrix.
+template <int QBITS>
 __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, const uint16_t* scales, int rows,
                                         int K, int row, int step, int h, bool ok) {
-  if constexpr (KM >= 1) {
-    const int nb = K / 32;
-    const bool half_step = KM == 2 && 4 * step + 2 >= nb;  // only blocks 4 step, 4 step + 1 (K % 128 == 64)
-    const int b0 = 4 * step + (half_step ? 0 : 2 * h);
-    const bool in = ok && b0 < nb;
-    const int rr = in ? row : 0, bb = in ? b0 : 0;
-    const QTile tl = qtile<true>(rr, rows);  // tiled layout (common.h); weight rows are multiples of 32
-    // raw values only: a select on a loaded value here would wait for the
-    // load; blocks past K are zeroed through their scale at dequantisation
-    r.c = *reinterpret_cast<const uint4v*>(codes + qt_code_off(tl, K, bb));
-    r.s = *reinterpret_cast<const uint32_t*>(scales + qt_scale_off(tl, K, bb));
-    if constexpr (QBITS == 3) {
-      const uint2v hv = *reinterpret_cast<const uint2v*>(codes + int64_t(rows) * (K / 4) + qt_high_off(tl, K, bb));
-      r.hb[0] = hv[0];
-      r.hb[1] = hv[1];
-    }
-    if constexpr (QBITS == 4) {
-      const uint4v hv = *reinterpret_cast<const uint4v*>(codes + int64_t(rows) * (K / 4) + qt_code_off(tl, K, bb));
-      r.hb[0] = hv[0];
-      r.hb[1] = hv[1];
-      r.hb[2] = hv[2];
-      r.hb[3] = hv[3];
-    }
-    r.v = in ? 3u : 0u;
-    return;
-  }
-  // blocks of this lane: b0 = 4 * step + 2h and b0 + 1, each zero past K or
-  // past the matrix.  One load per block (8 code bytes, one scale: a K with
-  // an odd block count ends in a one-block unit), each unconditional from a
-  // clamped address.
   const int nb = K / 32;
   const int b0 = 4 * step + 2 * h;
   const bool in0 = ok && b0 < nb, in1 = ok && b0 + 1 < nb;
@@ -201,9 +182,8 @@ __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, ha
 // KM: 0 = any K (a multiple of 32), 1 = K a multiple of 64, 2 = K a multiple
 // of 64 that may end in a half step (K % 128 == 64; the checks and selects of
 // half steps cost VALU in every step, so only this instantiation has them).
-template <int QBITS, typename AT, bool GATEUP, int NWV, int PD, int KM, int BM>
-__global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void grouped_gemm2_kernel(FfnArgs a,
-                                                                                                 int n_ntiles) {
+template <int QBITS, bool GATEUP, int NWV, int KM, int BM>
+__global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kernel(FfnArgs a, int n_ntiles) {
   static_assert(BM % 32 == 0 && BM <= 128, "whole 32-row MFMA tiles");
   constexpr int NT = 64 * NWV;                         // threads
   constexpr int MI = BM / 32;                          // MFMA row tiles per wave
@@ -234,9 +214,10 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
 
-  // ---- A sources: thread handles items tid + NT i (i < AI) of the BM x 8
-  // groups; an item past the tile loads a real row and is never stored
-  const AT* asrc[AI];
+  // ---- A sources (fp16 in the permuted order: the x16 copy of x, or h):
+  // thread handles items tid + NT i (i < AI) of the BM x 8 groups; an item
+  // past the tile loads a real row and is never stored
+  const f16* asrc[AI];
   int arow[AI], agrp[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
@@ -246,10 +227,9 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
     const int r = min(arow[i], rows_valid - 1);  // rows past the segment read a real row; never stored
     if constexpr (GATEUP) {
       const int64_t tok = shared ? int64_t(m0 + r) : int64_t(a.sorted_pair[lo + m0 + r] / a.k);
-      asrc[i] = static_cast<const AT*>(a.x) + tok * H;
+      asrc[i] = a.x16 + tok * H + agrp[i] * 16;
     } else {
-      const f16* hb = shared ? a.h_shared + int64_t(m0 + r) * K : a.h_routed + int64_t(lo + m0 + r) * K;
-      asrc[i] = reinterpret_cast<const AT*>(hb);
+      asrc[i] = (shared ? a.h_shared + int64_t(m0 + r) * K : a.h_routed + int64_t(lo + m0 + r) * K) + agrp[i] * 16;
     }
   }
   // ---- B sources: two 32-column sets per wave
@@ -271,27 +251,38 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
     bsc[j] = M.scales + ex * M.scale_stride;
     bok[j] = brow[j] < Nrows;
   }
+  // a wave whose columns all lie past the matrix (the last n-tile of a
+  // matrix whose rows are not a multiple of the tile) stages its share of A
+  // and keeps the barriers, but loads and multiplies nothing
+  const bool live = (GATEUP ? nt * (32 * NWV) + 32 * wv : nt * (64 * NWV) + 64 * wv) < Nrows;
+  BSrc bsrc[2];
+  if constexpr (KM >= 1) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bsrc[j] = bsrc_k64<QBITS>(bc[j], bsc[j], Nrows, K, brow[j], h, bok[j]);
+  }
   const int nsteps = (K + kBK2 - 1) / kBK2;
+  auto load_b = [&](BRaw2<QBITS>& r, int j, int step) {
+    if constexpr (KM >= 1) load_b2k<QBITS, KM>(r, bsrc[j], K, step, nsteps, h, bok[j]);
+    else load_b2<QBITS>(r, bc[j], bsc[j], Nrows, K, brow[j], step, h, bok[j]);
+  };
 
-  using Raw = ARaw<AT>;
-  constexpr int AR = (AI + 1) / 2;  // ARaw holds two groups
-  auto load_a = [&](int step, Raw (&r)[AR]) {
+  auto load_a = [&](int step, uint4v (&r)[AI][2]) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      int col = step * kBK2 + agrp[i] * 16;
-      if (col >= K) col = 0;  // K tail: the matching weights are zero
-      load_araw<AT>(asrc[i] + col, r[i >> 1], i & 1);
+      // K tail: the group's weights are zero, so any finite values do: the row's first group
+      const int col = step * kBK2 + agrp[i] * 16 < K ? step * kBK2 : -agrp[i] * 16;
+      const uint4v* p = reinterpret_cast<const uint4v*>(asrc[i] + col);
+      r[i][0] = p[0];
+      r[i][1] = p[1];
     }
   };
-  auto store_a = [&](const Raw (&r)[AR], f16* buf) {
+  auto store_a = [&](const uint4v (&r)[AI][2], f16* buf) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       if (AITEMS % NT != 0 && tid + NT * i >= AITEMS) continue;
-      half8 l8, h8;
-      cvt_araw<AT>(r[i >> 1], i & 1, l8, h8);
-      half8* d = reinterpret_cast<half8*>(buf + arow[i] * kLDA2 + agrp[i] * 16);
-      d[0] = l8;
-      d[1] = h8;
+      uint4v* d = reinterpret_cast<uint4v*>(buf + arow[i] * kLDA2 + agrp[i] * 16);
+      d[0] = r[i][0];
+      d[1] = r[i][1];
     }
   };
 
@@ -303,31 +294,27 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // B ring: the weights of steps step .. step + PD - 1 are in flight (a
-  // ring of PD register sets; slot p holds steps p, p + PD, ...).  A slot is
-  // dequantised in place and reloaded only after its step's MFMAs, and every
-  // load is unconditional (steps past K are clamped in load_b2 / load_a): a
-  // reload before the use needs a register copy, and those copies, like
-  // loads under a branch, make the compiler wait for every load in flight.
-  Raw ar[AR];
-  BRaw2<QBITS> bring[PD][2];
+  // B ring of one step: the weights of the next step are loaded right after
+  // this step's are dequantised.  Every load is unconditional (steps past K
+  // are clamped): a reload before the use needs a register copy, and those
+  // copies, like loads under a branch, make the compiler wait for every load
+  // in flight.
+  uint4v ar[AI][2];
+  BRaw2<QBITS> bring[2];
   load_a(0, ar);
+  if (live) {
 #pragma unroll
-  for (int p = 0; p < PD; ++p)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) load_b2<QBITS, KM>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], p, h, bok[j]);
+    for (int j = 0; j < 2; ++j) load_b(bring[j], j, 0);
+  }
   store_a(ar, As[0]);
   __syncthreads();
-  for (int s0 = 0; s0 < nsteps; s0 += PD) {
-#pragma unroll
-    for (int p = 0; p < PD; ++p) {
-      const int step = s0 + p;
-      if (step >= nsteps) break;
-      const int cur = step & 1;
-      load_a(min(step + 1, nsteps - 1), ar);  // the next step's activations (the last step reloads its own)
-      // keep the activation loads here, a whole step ahead of their LDS store
-      // (the scheduler would otherwise sink them to their use)
-      __builtin_amdgcn_sched_barrier(0);
+  for (int step = 0; step < nsteps; ++step) {
+    const int cur = step & 1;
+    load_a(min(step + 1, nsteps - 1), ar);  // the next step's activations (the last step reloads its own)
+    // keep the activation loads here, a whole step ahead of their LDS store
+    // (the scheduler would otherwise sink them to their use)
+    __builtin_amdgcn_sched_barrier(0);
+    if (live) {
       const f16* Ab = As[cur];
       // half step (K % 128 == 64, the last step): lane h holds block 4 step + h, A columns
       // 32h .. 32h + 31, and words 2, 3 (k-steps 4 .. 7) are not run
@@ -339,7 +326,7 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
         if (q >= 2 && half_step) break;
         half8 blo[2], bhi[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bring[p][j], q, sel, blo[j], bhi[j]);
+        for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bring[j], q, sel, blo[j], bhi[j]);
 #pragma unroll
         for (int half_ = 0; half_ < 2; ++half_) {
           half8 af[MI];
@@ -353,15 +340,15 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
         }
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        load_b2<QBITS, KM>(bring[p][j], bc[j], bsc[j], Nrows, K, brow[j], step + PD, h, bok[j]);
-      store_a(ar, As[cur ^ 1]);  // (after the last step: a buffer nobody reads any more)
-      __syncthreads();
+      for (int j = 0; j < 2; ++j) load_b(bring[j], j, step + 1);
     }
+    store_a(ar, As[cur ^ 1]);  // (after the last step: a buffer nobody reads any more)
+    __syncthreads();
   }
 
   // ---- epilogue.  32 x 32 D layout: lane l holds column l % 32 and rows
   // 8*(q/4) + 4*(l/32) + q%4, q = 0..15.
+  if (!live) return;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -392,17 +379,32 @@ __global__ __launch_bounds__(64 * NWV, sizeof(AT) == 4 || NWV > 4 ? 1 : 2) void 
   }
 }
 
-template <int QBITS, typename XT, int BM>
+// Waves per workgroup: 8 (BM x 512 tiles, one workgroup per CU) with 128-row
+// tiles; 4 (BM x 256, two workgroups per CU, so that one's prologue and
+// epilogue overlap the other's MFMAs) with the 96-row tiles of short segments
+// (measured on the 3-bit 4,096-token layer: gate/up -2%, down -8%; with
+// 128-row tiles 4 waves were no faster, and a second step of weight loads in
+// flight was no faster either).
+constexpr int grouped_waves(int bm) { return bm == 96 ? 4 : 8; }
+
+template <int QBITS, int BM>
 static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases) {
-  constexpr int W = MOE_GROUPED2_WAVES(BM), PD = MOE_GROUPED2_PD;
+  constexpr int W = grouped_waves(BM);
   if (phases & kPhaseGateUp) {
+    const int64_t groups = a.T * (a.H / 16);
+    if (a.x_bf16)
+      x16_kernel<uint16_t><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const uint16_t*>(a.x),
+                                                                              groups, a.x16);
+    else
+      x16_kernel<float><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const float*>(a.x), groups,
+                                                                           a.x16);
     const int rows = std::max(a.I, a.has_shared ? a.Is : 0);
     const int nn = (rows + 32 * W - 1) / (32 * W);
     const int64_t total = max_tiles * nn;
     const unsigned grid = unsigned((total + 7) / 8 * 8);
-    if (a.H % 128 == 0) grouped_gemm2_kernel<QBITS, XT, true, W, PD, 1, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
-    else if (a.H % 64 == 0) grouped_gemm2_kernel<QBITS, XT, true, W, PD, 2, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
-    else grouped_gemm2_kernel<QBITS, XT, true, W, PD, 0, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    if (a.H % 128 == 0) grouped_gemm2_kernel<QBITS, true, W, 1, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    else if (a.H % 64 == 0) grouped_gemm2_kernel<QBITS, true, W, 2, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+    else grouped_gemm2_kernel<QBITS, true, W, 0, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
   }
   if (phases & kPhaseDown) {
     const int nn = (a.H + 64 * W - 1) / (64 * W);
@@ -411,11 +413,11 @@ static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStrea
     const bool k64 = a.I % 64 == 0 && (!a.has_shared || a.Is % 64 == 0);
     const bool k128 = a.I % 128 == 0 && (!a.has_shared || a.Is % 128 == 0);
     if (k128)
-      grouped_gemm2_kernel<QBITS, f16, false, W, PD, 1, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+      grouped_gemm2_kernel<QBITS, false, W, 1, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
     else if (k64)
-      grouped_gemm2_kernel<QBITS, f16, false, W, PD, 2, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+      grouped_gemm2_kernel<QBITS, false, W, 2, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
     else
-      grouped_gemm2_kernel<QBITS, f16, false, W, PD, 0, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
+      grouped_gemm2_kernel<QBITS, false, W, 0, BM><<<grid, 64 * W, 0, stream>>>(a, nn);
   }
   return hipGetLastError();
 }
@@ -431,19 +433,13 @@ int grouped_tile_rows(int64_t T, int k, int E) {
 hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, int bm, hipStream_t stream, int phases) {
   if (a.T == 0) return hipSuccess;
   if (bm != 96 && bm != 128) return hipErrorInvalidValue;
-#define GQ(Q_, X_) \
-  return bm == 96 ? launch_grouped_q<Q_, X_, 96>(a, max_tiles, stream, phases) \
-                  : launch_grouped_q<Q_, X_, 128>(a, max_tiles, stream, phases)
-  if (a.qbits == 2) {
-    if (a.x_bf16) GQ(2, uint16_t);
-    GQ(2, float);
-  }
-  if (a.qbits == 4) {
-    if (a.x_bf16) GQ(4, uint16_t);
-    GQ(4, float);
-  }
-  if (a.x_bf16) GQ(3, uint16_t);
-  GQ(3, float);
+  if ((phases & kPhaseGateUp) && !a.x16) return hipErrorInvalidValue;
+#define GQ(Q_) \
+  return bm == 96 ? launch_grouped_q<Q_, 96>(a, max_tiles, stream, phases) \
+                  : launch_grouped_q<Q_, 128>(a, max_tiles, stream, phases)
+  if (a.qbits == 2) GQ(2);
+  if (a.qbits == 4) GQ(4);
+  GQ(3);
 #undef GQ
 }
 

@@ -42,6 +42,8 @@ struct FfnArgs {
   _Float16* h_routed;          // [P][I] SwiGLU activations, sorted order, columns
                                //   permuted within groups of 16 (MFMA operand order)
   _Float16* h_shared;          // [T][Is]
+  _Float16* x16;               // grouped GEMM: [T][H] fp16 copy of x in the permuted
+                               //   16-group order (written by its gate/up launch)
   float* y_sorted;             // [P][H]
   _Float16* y_sorted_h;        // grouped GEMM: when non-null, the routed down output
                                //   goes here in fp16 instead of y_sorted

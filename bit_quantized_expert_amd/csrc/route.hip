@@ -198,13 +198,10 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------
 constexpr int kRtT = 128, kRtE = 128;  // tile: tokens x experts
 constexpr int kRtOutPitch = kRtE + 4;   // LDS row pitch of the logits tile in floats
-#ifndef MOE_ROUTER_GEMM_MIN_T
-#define MOE_ROUTER_GEMM_MIN_T 2048
-#endif
-constexpr int64_t kRouterGemmMinT = MOE_ROUTER_GEMM_MIN_T;
-#ifndef MOE_ROUTER_SMALL_EPW
-#define MOE_ROUTER_SMALL_EPW 2  // experts per workgroup of the router at <= 16 tokens (one workgroup per CU at 512 experts)
-#endif  // below: router_mfma_kernel's 16 x 16 tiles
+constexpr int64_t kRouterGemmMinT = 2048;  // tokens from which the 128 x 128 tiles run
+// experts per workgroup of the router at <= 16 tokens (one workgroup per CU
+// at 512 experts); router_mfma_kernel's 16 x 16 tiles are below
+constexpr int kRouterSmallEpw = 2;
 // LDS row pitch of the staged operands in bf16: an odd number of 16-byte
 // units, so the 16 rows of a fragment read hit distinct banks
 template <int RK>
@@ -380,7 +377,7 @@ hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_
     return hipGetLastError();
   }
   if (T <= 16) {
-    constexpr int EPW = MOE_ROUTER_SMALL_EPW;
+    constexpr int EPW = kRouterSmallEpw;
     router_mfma_kernel<EPW><<<dim3(unsigned((E + EPW - 1) / EPW)), 512, 0, stream>>>(x, T, H, w, bias, E, logits);
   } else {
     const dim3 grid(unsigned((E + 15) / 16), unsigned((T + 15) / 16));
