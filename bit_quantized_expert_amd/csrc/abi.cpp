@@ -257,6 +257,10 @@ hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, co
                                     at<int4>(ws, W.slots), at<int32_t>(ws, W.tile_expert),
                                     at<int32_t>(ws, W.tile_m0), sorted_pair, s->top_k, st);
     if (e != hipSuccess) return e;
+    if (algo == MOE_ALGO_GROUPED) {  // the grouped gate/up GEMM reads x through its fp16 copy
+      e = moe::launch_x16(a, st);
+      if (e != hipSuccess) return e;
+    }
   }
   const int phases = (flags & MOE_FFN_SKIP_GATEUP ? 0 : moe::kPhaseGateUp) | (flags & MOE_FFN_SKIP_DOWN ? 0 : moe::kPhaseDown);
   if (algo == MOE_ALGO_GROUPED) {

@@ -391,13 +391,6 @@ template <int QBITS, int BM>
 static hipError_t launch_grouped_q(const FfnArgs& a, int64_t max_tiles, hipStream_t stream, int phases) {
   constexpr int W = grouped_waves(BM);
   if (phases & kPhaseGateUp) {
-    const int64_t groups = a.T * (a.H / 16);
-    if (a.x_bf16)
-      x16_kernel<uint16_t><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const uint16_t*>(a.x),
-                                                                              groups, a.x16);
-    else
-      x16_kernel<float><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const float*>(a.x), groups,
-                                                                           a.x16);
     const int rows = std::max(a.I, a.has_shared ? a.Is : 0);
     const int nn = (rows + 32 * W - 1) / (32 * W);
     const int64_t total = max_tiles * nn;
@@ -430,10 +423,20 @@ int grouped_tile_rows(int64_t T, int k, int E) {
   return P <= 90 * active ? 96 : 128;
 }
 
+hipError_t launch_x16(const FfnArgs& a, hipStream_t stream) {
+  const int64_t groups = a.T * (a.H / 16);
+  if (groups == 0) return hipSuccess;
+  if (a.x_bf16)
+    x16_kernel<uint16_t><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const uint16_t*>(a.x), groups,
+                                                                            a.x16);
+  else
+    x16_kernel<float><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const float*>(a.x), groups, a.x16);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, int bm, hipStream_t stream, int phases) {
   if (a.T == 0) return hipSuccess;
   if (bm != 96 && bm != 128) return hipErrorInvalidValue;
-  if ((phases & kPhaseGateUp) && !a.x16) return hipErrorInvalidValue;
 #define GQ(Q_) \
   return bm == 96 ? launch_grouped_q<Q_, 96>(a, max_tiles, stream, phases) \
                   : launch_grouped_q<Q_, 128>(a, max_tiles, stream, phases)

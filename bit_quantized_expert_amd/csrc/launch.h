@@ -97,6 +97,8 @@ hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t 
 // tile_bm = grouped_tile_rows(T, k, E) (96 or 128) and launched with the same
 // bm; max_tiles bounds the list for the launch grid.
 int grouped_tile_rows(int64_t T, int k, int E);
+// a.x -> a.x16 (the grouped gate/up GEMM's activations), part of the plan step.
+hipError_t launch_x16(const FfnArgs& a, hipStream_t stream);
 hipError_t launch_ffn_grouped(const FfnArgs& a, int64_t max_tiles, int bm, hipStream_t stream, int phases);
 // The fused single-token decode FFN (needs E <= kDecode1MaxExperts): gate/up
 // with the selection made from the router logits in every workgroup, then

@@ -118,9 +118,9 @@ typedef struct {
 
 /* Phase control of moe_expert_ffn (flags of moe_options; moe_layer_forward
  * takes none).  For running one projection kernel alone, e.g. to time it:
- * REUSE_PLAN skips building the slot table from offsets (reusing the one the
- * previous moe_expert_ffn call on this workspace built, for the same offsets
- * and T); SKIP_GATEUP skips the gate/up projection (reusing the activations
+ * REUSE_PLAN skips building the slot table from offsets and the grouped
+ * GEMM's fp16 copy of x (reusing what the previous moe_expert_ffn call on
+ * this workspace built, for the same x, offsets and T); SKIP_GATEUP skips the gate/up projection (reusing the activations
  * left in the workspace by the previous call); SKIP_DOWN skips the down
  * projection (y_sorted and shared_out are then not written). */
 enum {
