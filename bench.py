@@ -196,7 +196,6 @@ def time_phase(states, xs, layers, skip, reps):
 
 TRAFFIC_FILES = {
     "grouped_gateup_prefill3": ("grouped_gateup_prefill3_traffic.txt", ("ffn_grouped.hip", "common.h", "launch.h")),
-    "gemv_gateup_decode1": ("gemv_gateup_decode1_traffic.txt", ("ffn_gemv.hip", "common.h", "launch.h")),
 }
 
 
@@ -469,7 +468,6 @@ def decode1_bench(args, dev, log):
                               "gateup_GBs": gu_b / float(np.median(gu)) / 1e6,
                               "down_gemv_us": float(np.median(dn)) * 1e3,
                               "down_GBs": dn_b / float(np.median(dn)) / 1e6,
-                              "gateup_traffic_bytes": measured_traffic("gemv_gateup_decode1"),
                               "note": "launched alone with the slot table given (not the mode inside the layer)"},
             "probe": probe}
 
