@@ -16,7 +16,8 @@ Secondary workloads, each built from its own seeds and reported with its own
 roofline and an oracle CPU baseline on a bounded sample:
   decode1   single-token decode walking 48 resident 2-bit layers (HBM)
   decode16  16 tokens through a 48-layer 2-bit stack (HBM)
-  verify4   the verify window (a token + 3 drafts) through a 48-layer stack
+  verify4   the verify window (a token + 3 drafts) through a 48-layer stack;
+            also with the opt-in route tail skip (speed and output shift)
   prefill   32,768 tokens through one 2-bit layer (MFMA, Zipf-skewed routing)
   four_bit  the 4-bit block variant (4,096-token layer; single-token decode)
 plus a kernel probe (the decode GEMV kernels alone over every expert of a
@@ -239,9 +240,9 @@ class Stack:
     """T tokens through the resident layers with the residual + RMSNorm +
     bf16 glue, as plain launches or as one captured graph."""
 
-    def __init__(self, wl, layers, dev, record_acts=False):
+    def __init__(self, wl, layers, dev, flags=0):
         s = wl.shape
-        self.wl, self.s, self.layers, self.T = wl, s, layers, wl.tokens
+        self.wl, self.s, self.layers, self.T, self.flags = wl, s, layers, wl.tokens, flags
         self.x0 = synth.tokens(wl, dev).float()
         self.r = torch.empty(self.T, s.hidden, device=dev)
         self.a = torch.empty(self.T, s.hidden, dtype=torch.bfloat16, device=dev)
@@ -256,7 +257,8 @@ class Stack:
         for l, layer in enumerate(self.layers):
             if record is not None and l in record:
                 record[l] = self.a.clone()
-            M.layer_forward(self.a, layer, self.s, residual=self.r, next_in=self.a, topk_idx=self.idx[l], ws=self.ws)
+            M.layer_forward(self.a, layer, self.s, residual=self.r, next_in=self.a, topk_idx=self.idx[l], ws=self.ws,
+                            flags=self.flags)
 
     def capture(self):
         self.graph = torch.cuda.CUDAGraph()
@@ -517,6 +519,57 @@ def decode_stack_secondary(name, args, dev, log):
                          "unit": "GB/s", "frac": nbytes / med / 1e6 / HBM_PEAK_GBS, "traffic": None}}
 
 
+def tail_skip_secondary(args, dev, log, first_tail=7):
+    """The opt-in route tail skip on the verify-window stack (a token + 3
+    drafts through 48 layers): speed with and without it (graph replays), the
+    experts it drops, and the output shift it causes -- per layer on the same
+    inputs (the exact stack's activations), and at the end of the stack."""
+    wl = synth.WORKLOADS["verify4"]
+    s = wl.shape
+    L = args.layers
+    layers = build_layers(wl, L, dev, log)
+    exact = Stack(wl, layers, dev)
+    skip = Stack(wl, layers, dev, flags=M.ROUTE_TAIL_SKIP)
+    acts = {l: None for l in range(L)}
+    exact.step(record=acts)
+    skip.step()
+    torch.cuda.synchronize()
+    end_shift = float(torch.linalg.vector_norm(skip.r - exact.r) / torch.linalg.vector_norm(exact.r))
+    steps = max(20, args.steps)
+    exact.capture()
+    skip.capture()
+    ms_exact, _ = event_steps(exact.replay, steps, 3)
+    ms_skip, _ = event_steps(skip.replay, steps, 3)
+    # per layer, the same input through the layer with and without the skip
+    ws = M.alloc_workspace(s, wl.tokens, device=dev)
+    o0 = torch.empty(wl.tokens, s.hidden, device=dev)
+    o1 = torch.empty_like(o0)
+    idx = torch.empty(wl.tokens, s.top_k, dtype=torch.int32, device=dev)
+    shifts, dropped, used = [], [], []
+    for l in range(L):
+        M.layer_forward(acts[l], layers[l], s, out=o0, topk_idx=idx, ws=ws)
+        M.layer_forward(acts[l], layers[l], s, out=o1, ws=ws, flags=M.ROUTE_TAIL_SKIP)
+        shifts.append(float(torch.linalg.vector_norm(o1 - o0) / torch.linalg.vector_norm(o0)))
+        ix = idx.cpu().numpy()
+        sel = set(np.unique(ix).tolist())
+        head = set(np.unique(ix[:, :first_tail]).tolist())
+        used.append(len(sel))
+        dropped.append(len(sel - head))
+    del exact, skip, layers, ws, acts
+    release()
+    me, ms = float(np.median(ms_exact)), float(np.median(ms_skip))
+    log(f"verify4 tail skip: {ms:.3f} vs {me:.3f} ms/step ({me / ms - 1:+.1%}); dropped {np.mean(dropped):.2f} of "
+        f"{np.mean(used):.1f} experts per layer; per-layer relL2 shift median {np.median(shifts):.2e}, "
+        f"end of stack {end_shift:.2e}")
+    return {"what": "route tail skip (opt-in): verify window of 4 tokens through the 48-layer stack; experts no "
+                    "token ranks 0..6 are dropped", "ms_per_step": {"exact": stats(ms_exact), "tail_skip": stats(ms_skip)},
+            "speedup": me / ms, "experts_per_layer": float(np.mean(used)),
+            "dropped_per_layer": float(np.mean(dropped)),
+            "expert_bytes_saved_per_layer": float(np.mean(dropped)) * expert_bytes(s),
+            "out_shift_relL2_per_layer": {"median": float(np.median(shifts)), "max": float(np.max(shifts))},
+            "out_shift_relL2_end_of_stack": end_shift}
+
+
 def prefill32k_secondary(args, dev, log):
     wl = synth.WORKLOADS["prefill"]
     s = wl.shape
@@ -592,7 +645,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--only", default="", help="comma list: headline,decode1,decode16,verify4,prefill,four_bit")
+    ap.add_argument("--only", default="",
+                    help="comma list: headline,decode1,decode16,verify4,tail_skip,prefill,four_bit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy 10 times (scales the HBM byte counters)")
@@ -633,6 +687,8 @@ def main():
     for name in ("decode16", "verify4"):
         if want(name):
             res_sec[name + "_stack"] = decode_stack_secondary(name, args, dev, log)
+    if want("tail_skip"):
+        res_sec["verify4_tail_skip"] = tail_skip_secondary(args, dev, log)
     if want("prefill"):
         res_sec["prefill32k_layer"] = prefill32k_secondary(args, dev, log)
     if want("four_bit"):

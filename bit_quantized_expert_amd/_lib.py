@@ -22,6 +22,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEV
 MOE_F32, MOE_BF16 = 0, 1
 ALGO = {"auto": 0, "gemv": 1, "grouped": 2}
 FFN_REUSE_PLAN, FFN_SKIP_GATEUP, FFN_SKIP_DOWN = 1, 2, 4
+ROUTE_TAIL_SKIP = 8  # moe_layer_forward option: the verify-window route tail skip
 
 
 class MoeError(RuntimeError):
@@ -278,22 +279,23 @@ def combine(y_sorted, pair_pos, topk_w, shared_out, T: int, shape, out=None, res
 
 
 def layer_forward(x, layer: QLayer, shape, out=None, residual=None, next_in=None, topk_idx=None, topk_w=None,
-                  algo="auto", ws=None, stream=None) -> None:
+                  algo="auto", ws=None, stream=None, flags: int = 0) -> None:
     wp, wn = _ws(ws)
     _check(lib().moe_layer_forward(_ptr(x), _dtype_code(x), x.shape[0], ctypes.byref(layer.c_struct()),
                                    ctypes.byref(Shape.of(shape)), _ptr(out), _ptr(residual), _ptr(next_in),
-                                   _ptr(topk_idx), _ptr(topk_w), ctypes.byref(_opts(algo)), wp, wn,
+                                   _ptr(topk_idx), _ptr(topk_w), ctypes.byref(_opts(algo, flags)), wp, wn,
                                    _stream(stream)), "moe_layer_forward")
 
 
 def layer_forward_noalloc(x, layer: QLayer, shape, out=None, residual=None, next_in=None, topk_idx=None,
-                          topk_w=None, algo="auto", stream=None) -> None:
+                          topk_w=None, algo="auto", stream=None, flags: int = 0) -> None:
     """moe_layer_forward without a workspace argument (the library's own
     per-GPU scratch array; shapes up to MOE_NOALLOC_SCRATCH_BYTES of
     workspace)."""
     _check(lib().moe_layer_forward_noalloc(_ptr(x), _dtype_code(x), x.shape[0], ctypes.byref(layer.c_struct()),
                                            ctypes.byref(Shape.of(shape)), _ptr(out), _ptr(residual), _ptr(next_in),
-                                           _ptr(topk_idx), _ptr(topk_w), ctypes.byref(_opts(algo)), _stream(stream)),
+                                           _ptr(topk_idx), _ptr(topk_w), ctypes.byref(_opts(algo, flags)),
+                                           _stream(stream)),
            "moe_layer_forward_noalloc")
 
 

@@ -171,6 +171,16 @@ moe_algo pick_algo(const moe_options* o, int64_t T, const moe_shape* s) {
   return T <= 16 && moe::gemv_lds_ok(T, s->hidden, s->inter, s->shared_inter) ? MOE_ALGO_GEMV : MOE_ALGO_GROUPED;
 }
 
+// The route tail skip's first tail rank (the pages' 7) when it applies: the
+// option is set, the layer is one verify window (T <= 4) and the top-k has a
+// tail (k > 7); else 0.
+constexpr int kTailSkipRank = 7;
+constexpr int64_t kVerifyWindow = 4;
+int tail_skip_rank(const moe_options* o, int64_t T, const moe_shape* s) {
+  const bool on = o && (o->flags & MOE_LAYER_ROUTE_TAIL_SKIP);
+  return on && T <= kVerifyWindow && s->top_k > kTailSkipRank ? kTailSkipRank : 0;
+}
+
 int check_algo(moe_algo algo, int64_t T, const moe_shape* s) {
   if (algo == MOE_ALGO_GEMV && !moe::gemv_lds_ok(T, s->hidden, s->inter, s->shared_inter))
     return fail(MOE_ERR_UNSUPPORTED, "the GEMV kernels stage min(T, 16) token rows of hidden=%d and inter=%d in LDS, "
@@ -179,11 +189,15 @@ int check_algo(moe_algo algo, int64_t T, const moe_shape* s) {
   return MOE_OK;
 }
 
-int check_opts(const moe_options* o, bool ffn_flags_ok = false) {
+enum OptsFor { kOptsPlain, kOptsFfn, kOptsLayer };
+
+int check_opts(const moe_options* o, OptsFor what = kOptsPlain) {
   if (!o) return MOE_OK;
   if (o->ffn_algo < MOE_ALGO_AUTO || o->ffn_algo > MOE_ALGO_GROUPED)
     return fail(MOE_ERR_INVALID_ARG, "ffn_algo=%d is not a moe_algo", int(o->ffn_algo));
-  const int allowed = ffn_flags_ok ? (MOE_FFN_REUSE_PLAN | MOE_FFN_SKIP_GATEUP | MOE_FFN_SKIP_DOWN) : 0;
+  const int allowed = what == kOptsFfn     ? (MOE_FFN_REUSE_PLAN | MOE_FFN_SKIP_GATEUP | MOE_FFN_SKIP_DOWN)
+                      : what == kOptsLayer ? MOE_LAYER_ROUTE_TAIL_SKIP
+                                           : 0;
   if (o->flags & ~allowed) return fail(MOE_ERR_INVALID_ARG, "flags=0x%x not accepted by this call", unsigned(o->flags));
   return MOE_OK;
 }
@@ -281,7 +295,7 @@ bool fused_decode_ok(int64_t T, const moe_shape* s, moe_algo algo) {
 
 hipError_t fused_decode(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s, float* out,
                         float* residual, uint16_t* next_in, int32_t* idx, float* w, void* ws, const WsLayout& W,
-                        hipStream_t st) {
+                        hipStream_t st, int kc) {
   float* logits = at<float>(ws, W.logits);
   hipError_t e = route_logits(x, xd, T, L, s, logits, st);
   if (e != hipSuccess) return e;
@@ -292,13 +306,13 @@ hipError_t fused_decode(const void* x, moe_dtype xd, int64_t T, const moe_layer*
   float* s_out = s->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;
   moe::FfnArgs a = ffn_args(x, xd, T, L, s, offsets, sorted_pair, y, s_out, ws, W);
   const moe::SelOut so{logits, idx, w, at<int32_t>(ws, W.counts), offsets, sorted_pair, pair_pos,
-                       at<int32_t>(ws, W.header), at<int4>(ws, W.slots)};
+                       at<int32_t>(ws, W.header), at<int4>(ws, W.slots), kc};
   // the gate/up kernel makes the selection itself where it can, else a selection launch first
   e = moe::launch_gateup_select(a, so, st);
   if (e == hipErrorNotSupported) {
     e = moe::launch_select_small(logits, int(T), s->n_experts, s->top_k, s_out != nullptr, idx, w,
                                  at<int32_t>(ws, W.counts), offsets, sorted_pair, pair_pos,
-                                 at<int32_t>(ws, W.header), at<int4>(ws, W.slots), st);
+                                 at<int32_t>(ws, W.header), at<int4>(ws, W.slots), kc, st);
     if (e != hipSuccess) return e;
     e = moe::launch_ffn_gemv(a, st, moe::kPhaseGateUp);
   }
@@ -319,14 +333,14 @@ bool decode1_ok(int64_t T, const moe_shape* s, moe_algo algo) {
 }
 
 hipError_t decode1(const void* x, moe_dtype xd, const moe_layer* L, const moe_shape* s, float* out, float* residual,
-                   uint16_t* next_in, int32_t* idx, float* w, void* ws, const WsLayout& W, hipStream_t st) {
+                   uint16_t* next_in, int32_t* idx, float* w, void* ws, const WsLayout& W, hipStream_t st, int kc) {
   float* logits = at<float>(ws, W.logits);
   hipError_t e = route_logits(x, xd, 1, L, s, logits, st);
   if (e != hipSuccess) return e;
   float* s_out = s->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;  // only marks the shared expert
   moe::FfnArgs a = ffn_args(x, xd, 1, L, s, nullptr, nullptr, nullptr, s_out, ws, W);
   const moe::Decode1Sel sel{logits, idx, w, at<int32_t>(ws, W.pair_pos), at<int32_t>(ws, W.slot_expert),
-                            at<int32_t>(ws, W.header)};
+                            at<int32_t>(ws, W.header), kc};
   e = moe::launch_decode1_ffn(a, sel, out, residual, st);
   if (e != hipSuccess || !next_in) return e;
   return moe::launch_residual_rmsnorm(residual, 1, s->hidden, next_in, st);
@@ -403,7 +417,7 @@ int moe_expert_ffn(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer*
   try {
     if (int r = check_shape(shape)) return r;
     if (int r = check_T(T, shape)) return r;
-    if (int r = check_opts(opts, true)) return r;
+    if (int r = check_opts(opts, kOptsFfn)) return r;
     if (int r = check_layer(layer, shape, false, true)) return r;
     if (int r = check_dtype(x_dtype, "x")) return r;
     if (T == 0) return ok();
@@ -453,10 +467,13 @@ int check_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_l
                         const moe_options* opts) {
   if (int r = check_shape(shape)) return r;
   if (int r = check_T(T, shape)) return r;
-  if (int r = check_opts(opts)) return r;
+  if (int r = check_opts(opts, kOptsLayer)) return r;
   if (int r = check_layer(layer, shape, true, true)) return r;
   if (int r = check_dtype(x_dtype, "x")) return r;
   if (T == 0) return MOE_OK;
+  if (tail_skip_rank(opts, T, shape) && pick_algo(opts, T, shape) != MOE_ALGO_GEMV)
+    return fail(MOE_ERR_UNSUPPORTED, "the route tail skip runs on the GEMV (decode) path; T=%lld takes the grouped "
+                "GEMM here", (long long)T);
   if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
   if (!out && !residual) return fail(MOE_ERR_INVALID_ARG, "one of out and residual must be non-NULL");
   if (next_in_bf16 && !residual) return fail(MOE_ERR_INVALID_ARG, "next_in_bf16 needs residual");
@@ -474,11 +491,13 @@ int layer_forward_ws(const void* x, moe_dtype x_dtype, int64_t T, const moe_laye
     float* w = topk_w ? topk_w : at<float>(ws, W.topk_w);
     const moe_algo algo = pick_algo(opts, T, shape);
     if (int r = check_algo(algo, T, shape)) return r;
+    const int kc = tail_skip_rank(opts, T, shape);
     if (decode1_ok(T, shape, algo))
-      return device_status(decode1(x, x_dtype, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st),
+      return device_status(decode1(x, x_dtype, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st, kc),
                            "moe_layer_forward");
     if (fused_decode_ok(T, shape, algo))
-      return device_status(fused_decode(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st),
+      return device_status(fused_decode(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st,
+                                        kc),
                            "moe_layer_forward");
     hipError_t e = do_route(x, x_dtype, T, layer, shape, at<float>(ws, W.logits), idx, w, st);
     if (e != hipSuccess) return device_status(e, "moe_layer_forward/route");

@@ -231,8 +231,11 @@ __global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnAr
   WaveKeys<8> K;
   uint64_t sel[8];
   bool rank_here = false;  // the one wave that also ranks the selection and stores it
+  // route tail skip: the slots are the token's top-kc experts (ranks below
+  // kc); ranks, weights and the selection written out stay those of the top-k
+  const int kc = sl.kc > 0 && sl.kc < a.k ? sl.kc : a.k;
   if (sl.logits) {
-    shared = j >= a.k;
+    shared = j >= kc;
     if (blockIdx.x * 16 >= (shared ? a.Is : a.I)) return;
     ex = 0;
     hrow = shared ? 0 : j;
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnAr
       __shared__ int s_ex;
       if (wv == 0) {
         wave_keys<8>(sl.logits, a.E, K);
-        wave_select<8>(K, a.k, sel);
+        wave_select<8>(K, kc, sel);
         const int e = wave_nth_selected<8>(sel, j);  // slot j: the j-th selected expert in index order
         if (lane == 0) s_ex = e;
       }
@@ -301,11 +304,27 @@ __global__ __launch_bounds__(64 * k1tokWaves) void gemv_gateup_1tok_kernel(FfnAr
     // ranks, weights and the slot maps, while this wave's weight loads are in flight
     float my_val;
     int my_idx, my_slot;
-    wave_rank<8>(K, sel, a.k, my_val, my_idx, my_slot);
+    if (kc == a.k) {
+      wave_rank<8>(K, sel, a.k, my_val, my_idx, my_slot);
+    } else {
+      // the full top-k for the ranks and weights; a rank below kc is slot
+      // (the number of the top-kc experts with a lower index)
+      uint64_t selk[8];
+      wave_select<8>(K, a.k, selk);
+      wave_rank<8>(K, selk, a.k, my_val, my_idx, my_slot);
+      const int v = my_idx >> 6, b = my_idx & 63;
+      int below = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        below += u < v ? __builtin_popcountll(sel[u]) : u == v ? __builtin_popcountll(sel[u] & ((1ull << b) - 1ull)) : 0;
+      my_slot = below;
+    }
     const float my_w = wave_topk_weight(my_val, a.k);
     if (lane < a.k) {
       sl.idx[lane] = my_idx;
       sl.w[lane] = my_w;
+    }
+    if (lane < kc) {
       sl.slot_of_rank[lane] = my_slot;
       sl.slot_expert[my_slot] = my_idx;
     }
@@ -1407,15 +1426,19 @@ hipError_t launch_ffn_gemv(const FfnArgs& a, hipStream_t stream, int phases) {
 }
 
 template <int QBITS>
-static hipError_t launch_decode1_q(const FfnArgs& a, const Decode1Sel& sel, float* out, float* res,
+static hipError_t launch_decode1_q(const FfnArgs& a_full, const Decode1Sel& sel, float* out, float* res,
                                    hipStream_t stream) {
+  // the down + combine kernel sums the computed ranks only (all k, or the
+  // ranks below kc under the route tail skip)
+  FfnArgs a = a_full;
+  if (sel.kc > 0 && sel.kc < a.k) a.k = sel.kc;
   const int slots = a.k + (a.has_shared ? 1 : 0);
   const int max_rows = std::max(a.I, a.has_shared ? a.Is : 0);
   {
     const bool u64 = a.H % 64 == 0;
     const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
 #define GU(U_, X_) \
-  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a, sel, a.slots)
+  gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a_full, sel, a.slots)
     if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
     else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU

@@ -79,9 +79,10 @@ hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared,
 // position, token count, token mask: bit t set when token t uses the slot};
 // empty slots have count 0).  Slot tables built by launch_plan carry the
 // mask for T <= kGemvMaxM (0 otherwise: tokens then come from sorted_pair).
+// kc: route tail skip (experts no token ranks below kc are dropped; 0 = off).
 hipError_t launch_select_small(const float* logits, int T, int E, int k, int has_shared, int32_t* idx, float* w,
                                int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                               int32_t* header, int4* slots, hipStream_t stream);
+                               int32_t* header, int4* slots, int kc, hipStream_t stream);
 
 // Routed + shared expert FFN on the decode kernels: h then y_sorted / shared_out.
 enum { kPhaseGateUp = 1, kPhaseDown = 2 };
@@ -115,6 +116,8 @@ struct Decode1Sel {
   int32_t* slot_of_rank; // [k] slot of rank r (written)
   int32_t* slot_expert;  // [k] expert of slot s (written)
   int32_t* header;       // workspace header: the error word is cleared
+  int kc;                // route tail skip: only the token's ranks below kc are computed (its
+                         //   top-kc experts are the slots); 0 or >= k: all k ranks
 };
 hipError_t launch_decode1_ffn(const FfnArgs& a, const Decode1Sel& sel, float* out, float* res, hipStream_t stream);
 // res[t] -> a[t] = bf16_RNE(res[t] / sqrt(mean(res[t]^2) + 1e-6)) with the

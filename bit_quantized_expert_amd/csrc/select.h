@@ -30,6 +30,8 @@ struct SelOut {
   int32_t* pair_pos;    // [T k]
   int32_t* header;      // workspace header: error, active, valid
   int4* slots;          // slot table (min(E, T k) + 1 entries)
+  int kc;               // route tail skip: an expert is computed only if some token ranks it
+                        // below kc (0 or >= k: every selected expert is computed)
 };
 
 // LDS of the selection for up to EMAX experts and NW waves.
@@ -37,6 +39,7 @@ template <int EMAX, int NW>
 struct SelLds {
   int cnt[EMAX];          // count | active << 16, then (scanned) offset | slot << 16
   uint32_t tmask[EMAX];   // bit t: token t chose the expert (a token picks an expert at most once)
+  uint32_t hmask[EMAX];   // route tail skip: bit t: token t ranks the expert below kc
   uint16_t slot_e[EMAX];  // expert of active slot s
   int tmp[NW];
 };
@@ -56,7 +59,15 @@ __device__ int select_in_workgroup(const SelOut& o, int T, int E, int k, int has
   constexpr int NT = 64 * NW;
   constexpr int TPW = (kSelMaxT + NW - 1) / NW;  // tokens per wave
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += NT) S.tmask[e] = 0u;
+  // route tail skip ("How Strata runs a 125-billion-parameter model ...",
+  // Step 2, "Verify-window route tail skip"): an expert that no token ranks
+  // below kc is dropped (its pairs add nothing); the selection, ranks and
+  // weights written out are those of the full top-k
+  const bool skip = o.kc > 0 && o.kc < k;
+  for (int e = threadIdx.x; e < E; e += NT) {
+    S.tmask[e] = 0u;
+    if (skip) S.hmask[e] = 0u;
+  }
   __syncthreads();
 
   // ---- top-k of tokens wv, wv + NW, ... (one wave per token at a time).
@@ -87,6 +98,13 @@ __device__ int select_in_workgroup(const SelOut& o, int T, int E, int k, int has
 #pragma unroll
     for (int v = 0; v < V; ++v)
       if ((msel[v] >> lane) & 1ull) atomicOr(&S.tmask[lane + 64 * v], 1u << t);
+    if (skip) {  // the token's head ranks 0 .. kc - 1: its top-kc
+      uint64_t mhead[V];
+      wave_select<V>(K, o.kc, mhead);
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if ((mhead[v] >> lane) & 1ull) atomicOr(&S.hmask[lane + 64 * v], 1u << t);
+    }
     if (write) {  // ranks and weights: only the workgroup that writes them out
       float my_val;
       int my_slot;
@@ -104,6 +122,8 @@ __device__ int select_in_workgroup(const SelOut& o, int T, int E, int k, int has
   // offsets, the high half the slot of each active expert (counts <= 16 T
   // and active experts <= EMAX <= 4096, so neither half carries)
   for (int e = threadIdx.x; e < E; e += NT) {
+    const bool active = skip ? S.hmask[e] != 0u : S.tmask[e] != 0u;
+    if (skip && !active) S.tmask[e] = 0u;  // a dropped expert: no pairs, no slot
     const int c = __builtin_popcount(S.tmask[e]);
     if (write) o.counts[e] = c;
     S.cnt[e] = c | (c > 0 ? 1 << 16 : 0);
@@ -129,9 +149,13 @@ __device__ int select_in_workgroup(const SelOut& o, int T, int E, int k, int has
       const int t = wv + NW * i;
       if (t < T && lane < k) {
         const int e = my_idx[i], p = t * k + lane;
-        const int pos = (S.cnt[e] & 0xffff) + __builtin_popcount(S.tmask[e] & ((1u << t) - 1u));
-        o.sorted_pair[pos] = p;
-        o.pair_pos[p] = pos;
+        if (S.tmask[e] == 0u) {  // dropped by the route tail skip: the combine adds nothing for it
+          o.pair_pos[p] = -1;
+        } else {
+          const int pos = (S.cnt[e] & 0xffff) + __builtin_popcount(S.tmask[e] & ((1u << t) - 1u));
+          o.sorted_pair[pos] = p;
+          o.pair_pos[p] = pos;
+        }
       }
     }
     // slot table tail: the shared expert after the active ones; slots past

@@ -20,10 +20,10 @@ __global__ __launch_bounds__(1024) void select_small_kernel(SelOut o, int T, int
 
 hipError_t launch_select_small(const float* logits, int T, int E, int k, int has_shared, int32_t* idx, float* w,
                                int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                               int32_t* header, int4* slots, hipStream_t stream) {
+                               int32_t* header, int4* slots, int kc, hipStream_t stream) {
   if (T > kSelMaxT || T * k > 1024) return hipErrorInvalidValue;
   const int v = (E + 63) / 64;
-  const SelOut o{logits, idx, w, counts, offsets, sorted_pair, pair_pos, header, slots};
+  const SelOut o{logits, idx, w, counts, offsets, sorted_pair, pair_pos, header, slots, kc};
 #define SEL(V_) select_small_kernel<V_><<<1, 1024, 0, stream>>>(o, T, E, k, has_shared)
   if (v <= 1) SEL(1);
   else if (v <= 2) SEL(2);

@@ -129,9 +129,23 @@ enum {
   MOE_FFN_SKIP_DOWN = 4
 };
 
+/* Option of moe_layer_forward (and moe_layer_forward_noalloc): the route
+ * tail skip of a verify window ("How Strata runs a 125-billion-parameter
+ * model ...", Step 2, "Verify-window route tail skip (STRATA_ROUTE_TAIL_SKIP=7)").
+ * With T <= 4 tokens (one window) on the GEMV path, an expert that no token
+ * of the window ranks 0..6 of its top-k (every token that chose it ranks it
+ * 7 or later, the smallest router weights) is neither read nor computed, and
+ * its pairs add nothing to the sum; the other weights are not renormalised.
+ * An approximation: the output differs from the exact layer (the pages keep
+ * it for experts missing from VRAM and report a small distribution shift).
+ * topk_idx / topk_w still return the full selection.  No effect when T > 4
+ * or top_k <= 7; MOE_ERR_UNSUPPORTED with MOE_ALGO_GROUPED at T <= 4. */
+enum { MOE_LAYER_ROUTE_TAIL_SKIP = 8 };
+
 typedef struct {
   moe_algo ffn_algo;
-  int32_t flags; /* MOE_FFN_* bits for moe_expert_ffn; 0 for every other call */
+  int32_t flags; /* MOE_FFN_* bits for moe_expert_ffn; MOE_LAYER_ROUTE_TAIL_SKIP for
+                    moe_layer_forward; 0 for every other call */
 } moe_options;
 
 /* Bytes of workspace moe_layer_forward needs for T tokens (also enough for

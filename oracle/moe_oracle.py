@@ -280,15 +280,30 @@ class QExpert:
                 dequant(*self.down, h, i, b))
 
 
+class _OnlyExperts:
+    """The experts of a layer, of which only `kept` are evaluated (the others
+    are None: their outputs are left at zero)."""
+
+    def __init__(self, experts, kept):
+        self.experts, self.kept = experts, kept
+
+    def __len__(self):
+        return len(self.experts)
+
+    def __getitem__(self, e):
+        return self.experts[e] if int(e) in self.kept else None
+
+
 def expert_outputs(x: np.ndarray, topk_idx: np.ndarray, experts, sorted_pair: np.ndarray,
                    offsets: np.ndarray) -> np.ndarray:
-    """Y[s] = expert(sorted_pair[s] // k)(x[token]) for every pair, sorted order."""
+    """Y[s] = expert(sorted_pair[s] // k)(x[token]) for every pair, sorted order
+    (rows of an expert given as None stay zero)."""
     x = np.asarray(x, dtype=np.float64)
     t, k = topk_idx.shape
     y = np.zeros((t * k, x.shape[1]), dtype=np.float64)
     for e in range(len(offsets) - 1):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        if hi == lo:
+        if hi == lo or experts[e] is None:
             continue
         tokens = sorted_pair[lo:hi] // k
         y[lo:hi] = swiglu(x[tokens], *experts[e].dense())
@@ -308,13 +323,32 @@ def combine(y_sorted: np.ndarray, pair_pos: np.ndarray, topk_w: np.ndarray,
     return out
 
 
-def layer_forward(x, w_router, bias, experts, shared, k: int, return_all: bool = False, idx=None):
+def tail_skip_keep(idx: np.ndarray, first_tail_rank: int) -> np.ndarray:
+    """The route tail skip of a verify window ("How Strata runs a
+    125-billion-parameter model ...", Step 2, "Verify-window route tail skip
+    (STRATA_ROUTE_TAIL_SKIP=7)"): an expert that every token of the window
+    ranks in the tail of its top-k (rank >= first_tail_rank, the smallest
+    router weights) contributes almost nothing and is skipped; every expert
+    that at least one token ranks below first_tail_rank is kept.  Reading
+    taken here: a token that did not select an expert does not rank it, so an
+    expert is kept iff some token ranks it 0 .. first_tail_rank - 1, and a
+    skipped expert's pairs contribute nothing (the other weights are not
+    renormalised).  Returns the keep mask of the pairs [T, k] (rank order)."""
+    idx = np.asarray(idx)
+    head = np.unique(idx[:, :first_tail_rank])
+    return np.isin(idx, head)
+
+
+def layer_forward(x, w_router, bias, experts, shared, k: int, return_all: bool = False, idx=None,
+                  tail_skip: int | None = None):
     """One MoE layer: route, permute, routed SwiGLU experts, shared expert,
     weighted combine.  `experts` is a sequence of QExpert (length E); `shared`
     is a QExpert or None.  If `idx` [T, k] is given it replaces the selection
     (the weights are still the renormalised softmax of this layer's logits at
     those experts) -- used to evaluate the layer at another implementation's
-    choice among near-tied experts."""
+    choice among near-tied experts.  With `tail_skip` (the first tail rank,
+    the pages' 7) the T tokens are one verify window and the route tail skip
+    drops the experts tail_skip_keep rejects."""
     x = np.asarray(x, dtype=np.float64)
     if idx is None:
         logits, idx, w = route(x, w_router, bias, k)
@@ -322,10 +356,12 @@ def layer_forward(x, w_router, bias, experts, shared, k: int, return_all: bool =
         logits = router_logits(x, w_router, bias)
         idx = np.asarray(idx, dtype=np.int32)
         w = topk_weights(logits, idx)
+    keep = np.ones(idx.shape, dtype=bool) if tail_skip is None else tail_skip_keep(idx, tail_skip)
     counts, offsets, sorted_pair, pair_pos = permute(idx, len(experts))
-    y = expert_outputs(x, idx, experts, sorted_pair, offsets)
+    kept_experts = set(np.asarray(idx)[keep].tolist())
+    y = expert_outputs(x, idx, _OnlyExperts(experts, kept_experts), sorted_pair, offsets)
     s = swiglu(x, *shared.dense()) if shared is not None else None
-    out = combine(y, pair_pos, w, s)
+    out = combine(y, pair_pos, np.where(keep, w, 0.0), s)
     if return_all:
         return dict(out=out, logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
                     sorted_pair=sorted_pair, pair_pos=pair_pos, y=y, shared=s)

@@ -297,3 +297,71 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for got, w_ in zip((out, r, a, idx), want):
             assert torch.equal(got, w_), f"replay {rep} differs"
+
+
+TAIL = [
+    # name, H, I, E, k, Is, qbits, T, dtype: full shape (single-token kernels, in-kernel selection of the
+    # persistent gate/up kernel), and ragged shapes on the one-workgroup selection kernel
+    ("full", 2048, 704, 512, 10, 704, 2, None, torch.bfloat16),
+    ("r12", 96, 96, 40, 12, 64, 3, None, torch.bfloat16),
+    ("e1k", 64, 32, 1024, 16, 32, 2, None, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", TAIL, ids=[c[0] for c in TAIL])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_route_tail_skip(case, T):
+    """The opt-in route tail skip of a verify window against the oracle's
+    rule (an expert no token ranks 0..6 adds nothing): the selection and
+    weights are those of the exact layer, the output is the oracle's layer
+    with the same experts dropped."""
+    from oracle import moe_oracle as O
+    M = _M()
+    name, H, I, E, k, Is, qb, _, dt = case
+    wl = synth.custom(f"tail_{name}", H, I, E, k, Is, qb, T, seed=41, act_dtype=dt, zipf_bias=True)
+    dl = _layer(wl)
+    s = dl.s
+    x = synth.tokens(wl, "cuda", n_tokens=T, layer=T)
+    res = {}
+    for flags in (0, M.ROUTE_TAIL_SKIP):
+        out = torch.empty(T, s.hidden, device="cuda")
+        idx = torch.empty(T, s.top_k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, s.top_k, device="cuda")
+        M.layer_forward(x, dl.q, s, out=out, topk_idx=idx, topk_w=w, ws=M.alloc_workspace(s, T), flags=flags)
+        torch.cuda.synchronize()
+        res[flags] = (out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy())
+    (o0, i0, w0), (o1, i1, w1) = res[0], res[M.ROUTE_TAIL_SKIP]
+    assert np.array_equal(i0, i1) and np.array_equal(w0, w1)
+    wr, b = dl.oracle_router()
+    for e in np.unique(i1):
+        dl.oracle_expert(int(e))
+    want = O.layer_forward(x_to_numpy(x), wr, b, dl.oracle_experts(), dl.oracle_shared(), k, idx=i1, tail_skip=7)
+    assert_close_output(o1, want, f"{name} T={T} tail skip")
+    keep = O.tail_skip_keep(i1, 7)
+    if not keep.all():  # something was dropped: the output moved off the exact layer
+        assert not np.array_equal(o0, o1)
+    else:
+        assert np.array_equal(o0, o1)
+
+
+def test_route_tail_skip_no_effect_and_refusals():
+    """No tail (top-k <= 7) or more than a window of tokens: the option changes
+    no bit.  Forced onto the grouped GEMM at a window's size it is refused."""
+    M = _M()
+    for (H, I, E, k, Is, T) in [(96, 96, 40, 7, 64, 3), (2048, 704, 512, 10, 704, 5), (2048, 704, 512, 10, 704, 16)]:
+        wl = synth.custom(f"tnone{k}_{T}", H, I, E, k, Is, 2, T, seed=43, act_dtype=torch.bfloat16, zipf_bias=True)
+        dl = _layer(wl)
+        s = dl.s
+        x = synth.tokens(wl, "cuda")
+        outs = []
+        for flags in (0, M.ROUTE_TAIL_SKIP):
+            out = torch.empty(T, s.hidden, device="cuda")
+            M.layer_forward(x, dl.q, s, out=out, ws=M.alloc_workspace(s, T), flags=flags)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        assert np.array_equal(outs[0], outs[1]), (k, T)
+    x4 = x[:4].contiguous()
+    with pytest.raises(M.MoeError) as ei:
+        M.layer_forward(x4, dl.q, s, out=torch.empty(4, s.hidden, device="cuda"), algo="grouped",
+                        ws=M.alloc_workspace(s, 4, algo="grouped"), flags=M.ROUTE_TAIL_SKIP)
+    assert ei.value.status == -2

@@ -326,6 +326,49 @@ def test_layer_brute_force_tiny(qbits):
         assert np.linalg.norm(got[t] - out) <= 1e-12 * np.linalg.norm(out)
 
 
+def test_route_tail_skip_brute_force():
+    """The route tail skip against pure-Python loops on a 3-token window:
+    an expert is dropped iff no token ranks it below the first tail rank, its
+    pairs add nothing, the other weights are untouched."""
+    w_r, b, experts, shared = _tiny_layer(seed=40, bias=True, n_experts=8)
+    rng = np.random.default_rng(41)
+    x = rng.normal(size=(3, 64)).astype(np.float32).astype(np.float64)
+    k, first_tail = 4, 2
+    got = O.layer_forward(x, w_r, b, experts, shared, k, tail_skip=first_tail)
+    logits = O.router_logits(x, w_r, b)
+    sel = [sorted(range(8), key=lambda e: (-logits[t, e], e))[:k] for t in range(3)]
+    head = {sel[t][j] for t in range(3) for j in range(first_tail)}
+    want = np.zeros((3, 64))
+    for t in range(3):
+        z = [math.exp(logits[t, e] - logits[t, sel[t][0]]) for e in sel[t]]
+        out = np.array(_py_swiglu(list(x[t]), *shared.dense()))
+        for j, e in enumerate(sel[t]):
+            if e in head:
+                out = out + z[j] / sum(z) * np.array(_py_swiglu(list(x[t]), *experts[e].dense()))
+        want[t] = out
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-15)
+    # something was dropped in this window (else the case would not test the rule)
+    assert any(e not in head for t in range(3) for e in sel[t])
+
+
+def test_route_tail_skip_closed_forms():
+    w_r, b, experts, shared = _tiny_layer(seed=42, bias=True, n_experts=8)
+    x = np.random.default_rng(43).normal(size=(4, 64))
+    plain = O.layer_forward(x, w_r, b, experts, shared, 3)
+    # a first tail rank at or past k drops nothing
+    assert np.array_equal(O.layer_forward(x, w_r, b, experts, shared, 3, tail_skip=3), plain)
+    # one token: exactly ranks >= the first tail rank are dropped
+    one = O.layer_forward(x[:1], w_r, b, experts, shared, 3, tail_skip=1)
+    r = O.layer_forward(x[:1], w_r, b, experts, shared, 3, return_all=True)
+    e0 = r["idx"][0, 0]
+    want = r["shared"][0] + r["w"][0, 0] * r["y"][r["pair_pos"][0]]
+    assert np.allclose(one[0], want, rtol=1e-13, atol=0) and e0 == r["idx"][0, 0]
+    # the keep mask: never drops an expert some token ranks in the head
+    idx = np.array([[5, 1, 7], [1, 2, 5], [3, 4, 6]])
+    keep = O.tail_skip_keep(idx, 2)
+    assert keep.tolist() == [[True, True, False], [True, True, True], [True, True, False]]
+
+
 # ---------------------------------------------------------------- stacks
 
 def test_bf16_round_ties_and_fp32_agreement():
