@@ -9,6 +9,9 @@ import pytest
 
 from bit_quantized_expert_amd import _lib as L
 
+if os.environ.get("MOE_ABI_TEST_LIB"):  # the sanitized build (tests/test_abi_sanitized.py)
+    L.LIB_PATH = os.environ["MOE_ABI_TEST_LIB"]
+
 pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libmoe.so not built")
 
 
