@@ -221,7 +221,7 @@ int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_lay
  * with its workspace taken from a scratch array the library holds on each
  * GPU instead of from the caller.  The array has MOE_NOALLOC_SCRATCH_BYTES
  * (16 MiB: every shape whose moe_workspace_bytes fits, e.g. the full-shape
- * layer of 512 experts, top-10, hidden 2048, inter 704 up to 155 tokens); it
+ * layer of 512 experts, top-10, hidden 2048, inter 704 up to 149 tokens); it
  * comes with the library's device code on each GPU the library runs on and
  * is held until the process ends.  A larger shape
  * returns MOE_ERR_UNSUPPORTED before any device work.  The call allocates

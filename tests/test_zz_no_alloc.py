@@ -47,13 +47,24 @@ def _both(M, dl, x, algo, glue):
 
 
 @pytest.mark.parametrize("name,algo,T1,T2", [("decode16", "auto", 16, 3), ("decode16", "auto", 9, 1),
-                                              ("decode16", "grouped", 150, 40)])
+                                              ("decode16", "grouped", 149, 40)])
 def test_noalloc_matches_layer_forward(name, algo, T1, T2):
     M = _M()
     dl = DeviceLayer(synth.WORKLOADS[name], 0)
     x = synth.tokens(dl.wl, "cuda", n_tokens=T1, layer=5)
     _both(M, dl, x, algo, glue=False)
     _both(M, dl, x[:T2].contiguous(), algo, glue=True)
+
+
+def test_noalloc_largest_shape_fits():
+    """The header's statement of the limit: the full-shape layer fits the
+    scratch array up to 149 tokens and not at 150 (argument checks only)."""
+    import ctypes
+    from bit_quantized_expert_amd import _lib as L
+    s = L.Shape(2048, 704, 512, 10, 704, 2)
+    limit = 16 << 20
+    assert L.lib().moe_workspace_bytes(ctypes.byref(s), 149, None) <= limit
+    assert L.lib().moe_workspace_bytes(ctypes.byref(s), 150, None) > limit
 
 
 def test_noalloc_ragged_and_limit():
