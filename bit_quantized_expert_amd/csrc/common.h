@@ -163,22 +163,94 @@ __device__ __forceinline__ uint32_t magic_bits(int i) {
 }
 __device__ __forceinline__ f16 magic_val(int i) { return f16(float(1 << (10 - 2 * i))); }
 
+// One word's dequantisation, split into a preparation (the shifted source
+// words and the scale, once per word) and the 8 pairs (dq_pair: two or three
+// VALU ops plus a packed subtract and multiply each), so that a caller can
+// spread the pairs of one word between other work.  Pair i < NA takes its
+// code bits from `a` (and `ha`), pair i >= NA from `b` (and `hb`), with
+// M_{i} resp. M_{i - NA}.
+struct DqSrc {
+  uint32_t a, b;    // low two bits of the codes: the word and its shifted copy
+  uint32_t ha, hb;  // 3-bit: bit 2 of the codes; 4-bit: bits 2..3; placed for pairs < NA and >= NA
+  half2v s2;        // block scale in both halves
+};
+
+// 2-bit: pairs 0..4 from w, 5..7 from w >> 10.
+__device__ __forceinline__ DqSrc dq2_src(uint32_t w, half2v s2) { return DqSrc{w, w >> 10, 0u, 0u, s2}; }
+
+// 3-bit: w holds the low two bits of 16 codes (2-bit layout); hlo and hhi
+// hold bit 2 of code i at bit 2i + 2 (pairs 0..3) and 2i - 6 (pairs 4..7),
+// with bits on odd positions ignored (high3_slots).  Pairs 0..3 use M_0..M_3
+// (bits up to 2i + 2 <= 8 stay inside the mantissa); pairs 4..7 use w >> 8
+// with M_0..M_3.  c = q - 4; c * s rounds to fp16 for |c| = 3 (relative
+// error <= 2^-11 per weight).
+__device__ __forceinline__ DqSrc dq3_src(uint32_t w, uint32_t hlo, uint32_t hhi, half2v s2) {
+  return DqSrc{w, w >> 8, hlo, hhi, s2};
+}
+
+// 4-bit: wl holds the low two bits of 16 codes and wh the high two bits, both
+// in the 2-bit layout.  Pairs 0..3 use M_0..M_3 with the high bits moved to
+// 2i+2 .. 2i+3 (wh << 2; bits up to 2i+3 <= 9 stay inside the mantissa, whose
+// bit 2i has weight 1, so the half holds M_i + q, q <= 15); pairs 4..7 use
+// wl >> 8 and wh >> 6 with M_0..M_3.  c = q - 8.  Bits that the shifts carry
+// across the half boundary fall outside the masks.  Unlike the 2-bit case,
+// c * s rounds to fp16 where |c| is not a power of two (as in the 3-bit
+// case: relative error <= 2^-11 per weight).
+__device__ __forceinline__ DqSrc dq4_src(uint32_t wl, uint32_t wh, half2v s2) {
+  return DqSrc{wl, wl >> 8, wh << 2, wh >> 6, s2};
+}
+
+// Pair i (0..7) of a prepared word, (code i, code i + 8) as fp16 c * s, in
+// dq_stages() dependent steps, so that a caller can interleave the steps of
+// several pairs: step 0 starts the pair's work word t, the last leaves the
+// fp16 pair in it.  Steps: [3-bit, 4-bit: high bits OR-ed into M_j], low bits
+// OR-ed in, subtract M_j + 2^(QBITS-1), multiply by the scale.
+template <int QBITS>
+constexpr int dq_stages() { return QBITS == 2 ? 3 : 4; }
+
+template <int QBITS>
+__device__ __forceinline__ void dq_step(const DqSrc& d, int i, int k, uint32_t& t) {
+  constexpr int NA = QBITS == 2 ? 5 : 4;
+  constexpr int S = dq_stages<QBITS>();
+  const int j = i < NA ? i : i - NA;
+  const uint32_t src = i < NA ? d.a : d.b;
+  if (k == S - 2) {
+    const f16 off = magic_val(j) + f16(float(1 << (QBITS - 1)));
+    t = as_u32(as_half2(t) - half2v{off, off});
+  } else if (k == S - 1) {
+    t = as_u32(as_half2(t) * d.s2);
+  } else if constexpr (QBITS == 2) {
+    t = and_or(src, 0x00030003u << (2 * j), magic_bits(j));
+  } else if (k == 0) {
+    constexpr uint32_t hmask = QBITS == 3 ? 0x00040004u : 0x000C000Cu;
+    t = and_or(i < NA ? d.ha : d.hb, hmask << (2 * j), magic_bits(j));
+  } else {
+    t = and_or_v(src, 0x00030003u << (2 * j), t);
+  }
+}
+
+template <int QBITS>
+__device__ __forceinline__ half2v dq_pair(const DqSrc& d, int i) {
+  uint32_t t = 0u;
+#pragma unroll
+  for (int k = 0; k < dq_stages<QBITS>(); ++k) dq_step<QBITS>(d, i, k, t);
+  return as_half2(t);
+}
+
+// All 8 pairs of a prepared word into the two MFMA k-slices.
+template <int QBITS>
+__device__ __forceinline__ void dq_word(const DqSrc& d, half8& lo, half8& hi) {
+  half2v p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = dq_pair<QBITS>(d, i);
+  lo = half8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  hi = half8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+}
+
 // Dequantise 2-bit word w (16 codes) with block scale s2 (scale in both
 // halves) into two MFMA k-slices (8 fp16 each) in the permuted order.
 __device__ __forceinline__ void dq2_word(uint32_t w, half2v s2, half8& lo, half8& hi) {
-  const uint32_t w10 = w >> 10;
-  half2v p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = i < 5 ? i : i - 5;
-    const uint32_t src = i < 5 ? w : w10;
-    const uint32_t v = and_or(src, 0x00030003u << (2 * j), magic_bits(j));
-    const f16 off = magic_val(j) + f16(2.0f);
-    half2v h = as_half2(v) - half2v{off, off};
-    p[i] = h * s2;
-  }
-  lo = half8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
-  hi = half8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+  dq_word<2>(dq2_src(w, s2), lo, hi);
 }
 
 // Spread the 16 bits of h to even bit positions: bit k -> bit 2k.
@@ -196,65 +268,25 @@ __host__ __device__ __forceinline__ uint32_t spread16(uint32_t h) {
 // of codes 0..15 (the block's first 16-code word A) sits at bit 2i + 1 and
 // bit i of codes 16..31 (word B) at bit 2i.  Shifted by a constant, the high
 // bits of either word then line up with the fp16 mantissa slots of its pairs
-// (dq3_word), with the other word's bits on odd positions outside the masks.
+// (dq3_src), with the other word's bits on odd positions outside the masks.
 __host__ __device__ __forceinline__ uint32_t qt_high3_word(uint32_t h) {
   return (spread16(h & 0xffffu) << 1) | spread16(h >> 16);
 }
 
 // The high bits of 16-code word `second` (0 = A, 1 = B) of a block for
-// dq3_word: bit 2 of code j at bit 2j + 2 (pairs 0..3, lo) and of code i at
+// dq3_src: bit 2 of code j at bit 2j + 2 (pairs 0..3, lo) and of code i at
 // bit 2i - 6 (pairs 4..7, hi).
 __device__ __forceinline__ void high3_slots(uint32_t hw, int second, uint32_t& lo, uint32_t& hi) {
   lo = second ? hw << 2 : hw << 1;
   hi = second ? hw >> 6 : hw >> 7;
 }
 
-// 3-bit variant: w holds the low two bits of 16 codes (2-bit layout); hlo
-// and hhi hold bit 2 of code i at bit 2i + 2 (pairs 0..3) and 2i - 6 (pairs
-// 4..7), with bits on odd positions ignored (high3_slots).  Pairs 0..3 use
-// M_0..M_3 (bits up to 2i + 2 <= 8 stay inside the mantissa); pairs 4..7 use
-// w >> 8 with M_0..M_3.  c = q - 4; c * s rounds to fp16 for |c| = 3
-// (relative error <= 2^-11 per weight).
 __device__ __forceinline__ void dq3_word(uint32_t w, uint32_t hlo, uint32_t hhi, half2v s2, half8& lo, half8& hi) {
-  const uint32_t w8 = w >> 8;
-  half2v p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = i < 4 ? i : i - 4;
-    const uint32_t src = i < 4 ? w : w8;
-    const uint32_t hsrc = i < 4 ? hlo : hhi;
-    const uint32_t v = and_or_v(src, 0x00030003u << (2 * j), and_or(hsrc, 0x00040004u << (2 * j), magic_bits(j)));
-    const f16 off = magic_val(j) + f16(4.0f);
-    half2v h = as_half2(v) - half2v{off, off};
-    p[i] = h * s2;
-  }
-  lo = half8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
-  hi = half8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+  dq_word<3>(dq3_src(w, hlo, hhi, s2), lo, hi);
 }
 
-// 4-bit variant: wl holds the low two bits of 16 codes and wh the high two
-// bits, both in the 2-bit layout.  Pairs 0..3 use M_0..M_3 with the high bits
-// moved to 2i+2 .. 2i+3 (wh << 2; bits up to 2i+3 <= 9 stay inside the
-// mantissa, whose bit 2i has weight 1, so the half holds M_i + q, q <= 15);
-// pairs 4..7 use wl >> 8 and wh >> 6 with M_0..M_3.  c = q - 8.  Bits that
-// the shifts carry across the half boundary fall outside the masks.
-// Unlike the 2-bit case, c * s rounds to fp16 where |c| is not a power of two
-// (as in the 3-bit case: relative error <= 2^-11 per weight).
 __device__ __forceinline__ void dq4_word(uint32_t wl, uint32_t wh, half2v s2, half8& lo, half8& hi) {
-  const uint32_t w8 = wl >> 8, hs = wh << 2, h8 = wh >> 6;
-  half2v p[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = i < 4 ? i : i - 4;
-    const uint32_t src = i < 4 ? wl : w8;
-    const uint32_t hsrc = i < 4 ? hs : h8;
-    const uint32_t v = and_or_v(src, 0x00030003u << (2 * j), and_or(hsrc, 0x000C000Cu << (2 * j), magic_bits(j)));
-    const f16 off = magic_val(j) + f16(8.0f);
-    half2v h = as_half2(v) - half2v{off, off};
-    p[i] = h * s2;
-  }
-  lo = half8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
-  hi = half8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+  dq_word<4>(dq4_src(wl, wh, s2), lo, hi);
 }
 
 // Position of weight r (0..15) of a 16-weight group in the permuted order.

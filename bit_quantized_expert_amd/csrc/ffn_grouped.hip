@@ -158,26 +158,39 @@ __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, c
   r.v = (in0 ? 1u : 0u) | (in1 ? 2u : 0u);
 }
 
-// word q (0..3) of a lane's step -> the two permuted k-slices.  sel (half
-// steps, lane h = 1, q < 2): word q of the second block instead (block
-// 4 step + 1).
+// word q (0..3) of a lane's step -> the prepared sources of its 8 pairs.
+// sel (half steps, lane h = 1, q < 2): word q of the second block instead
+// (block 4 step + 1).
 template <int QBITS>
-__device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, half8& lo, half8& hi) {
+__device__ __forceinline__ DqSrc dq_src_b2(const BRaw2<QBITS>& r, int q, bool sel) {
   const bool second = q >= 2 || sel;  // the lane's second block
   const uint32_t sraw = second ? (r.s >> 16) : (r.s & 0xffffu);
   const uint32_t sbits = (r.v >> (q >> 1)) & 1u ? sraw : 0u;  // blocks past K: scale 0, weights 0
   const half2v s2 = as_half2(sbits | (sbits << 16));
   const uint32_t w = q < 2 && sel ? r.c[q + 2] : r.c[q];
   if constexpr (QBITS == 2) {
-    dq2_word(w, s2, lo, hi);
+    return dq2_src(w, s2);
   } else if constexpr (QBITS == 4) {
-    dq4_word(w, q < 2 && sel ? r.hb[q + 2] : r.hb[q], s2, lo, hi);
+    return dq4_src(w, q < 2 && sel ? r.hb[q + 2] : r.hb[q], s2);
   } else {
     uint32_t hlo, hhi;
-    high3_slots(r.hb[second ? 1 : 0], q & 1, hlo, hhi);
-    dq3_word(w, hlo, hhi, s2, lo, hi);
+    high3_slots(second ? r.hb[1] : r.hb[0], q & 1, hlo, hhi);
+    return dq3_src(w, hlo, hhi, s2);
   }
 }
+
+// word q of a lane's step -> the two permuted k-slices
+template <int QBITS>
+__device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, half8& lo, half8& hi) {
+  dq_word<QBITS>(dq_src_b2<QBITS>(r, q, sel), lo, hi);
+}
+
+// The main loop comes in two forms: the software-pipelined one (below) with
+// 96-row tiles at 2 and 3 bits, and a plain one where the pipeline's extra
+// registers would not fit beside 128-row tiles or 4-bit weights (the
+// compiler would spill).
+template <int QBITS, int BM>
+constexpr bool grouped_pipelined() { return BM == 96 && QBITS <= 3; }
 
 // KM: 0 = any K (a multiple of 32), 1 = K a multiple of 64, 2 = K a multiple
 // of 64 that may end in a half step (K % 128 == 64; the checks and selects of
@@ -189,7 +202,8 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
   constexpr int MI = BM / 32;                          // MFMA row tiles per wave
   constexpr int AITEMS = BM * (kBK2 / 16);             // A staging items (16-element groups) per step
   constexpr int AI = (AITEMS + NT - 1) / NT;           // per thread (the last may be past the tile)
-  __shared__ __attribute__((aligned(16))) f16 As[2][BM * kLDA2];
+  constexpr bool PIPE = grouped_pipelined<QBITS, BM>();
+  __shared__ __attribute__((aligned(16))) f16 As[PIPE ? 3 : 2][BM * kLDA2];
 
   // ---- work item (XCD-aware remap over the real items)
   const int n_tiles = a.header[kHdrTiles];
@@ -294,56 +308,172 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // B ring of one step: the weights of the next step are loaded right after
-  // this step's are dequantised.  Every load is unconditional (steps past K
-  // are clamped): a reload before the use needs a register copy, and those
-  // copies, like loads under a branch, make the compiler wait for every load
-  // in flight.
   uint4v ar[AI][2];
-  BRaw2<QBITS> bring[2];
-  load_a(0, ar);
-  if (live) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) load_b(bring[j], j, 0);
-  }
-  store_a(ar, As[0]);
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    load_a(min(step + 1, nsteps - 1), ar);  // the next step's activations (the last step reloads its own)
-    // keep the activation loads here, a whole step ahead of their LDS store
-    // (the scheduler would otherwise sink them to their use)
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PIPE) {
+    // The loop runs over words: word q of step s is MFMA k-steps 2q (half 0)
+    // and 2q + 1 (half 1), 2 MI MFMAs each.  It is software-pipelined so that
+    // the MFMAs of one word overlap the work that feeds the next:
+    //   * the next word's weights are dequantised during this word (column
+    //     set j during half j), their steps spread over the half's MFMAs and
+    //     taken four pairs at a time so that consecutive VALU ops are
+    //     independent;
+    //   * the next half's activation fragments are read from LDS during this
+    //     half;
+    // each MFMA closing a group that a scheduling barrier keeps in this order
+    // (left alone, the compiler issues the dequantisation in bursts between
+    // MFMAs and waits for each LDS read right before its MFMA).
+    // Rings: activations in three LDS buffers, staged two steps ahead (so the
+    // next step's first fragments can be read before this step's barrier);
+    // raw weights in two register sets (even and odd steps), reloaded two
+    // steps ahead right after their last word is dequantised.  Every load is
+    // unconditional (steps past K are clamped and zeroed): a reload before
+    // the use needs a register copy, and those copies, like loads under a
+    // branch, make the compiler wait for every load in flight.
+    // A half step (KM == 2, K % 128 == 64) is always the last step; its words
+    // 2 and 3 are not run, and the word dequantised after its word 1 is never
+    // used.
+    auto half_step = [&](int st) { return KM == 2 && 4 * st + 2 >= K / 32; };
+    constexpr int S = dq_stages<QBITS>(), NOPS = 8 * S;  // dequantisation steps of one word
+    BRaw2<QBITS> rawA[2], rawB[2];  // raw weights of the even and odd steps [column set]
+    half8 bf[2][2][2];              // [word parity][half][column set]
+    half8 af[2][MI];                // [half parity][row tile]
+    auto frag = [&](const f16* Ab, int i, int col) -> half8 {
+      return *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + col);
+    };
+    load_a(0, ar);
+    store_a(ar, As[0]);
+    load_a(min(1, nsteps - 1), ar);
     if (live) {
-      const f16* Ab = As[cur];
-      // half step (K % 128 == 64, the last step): lane h holds block 4 step + h, A columns
-      // 32h .. 32h + 31, and words 2, 3 (k-steps 4 .. 7) are not run
-      const bool half_step = KM == 2 && 4 * step + 2 >= K / 32;
-      const bool sel = half_step && h;
-      const int acol = (half_step ? 32 : 64) * h;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {  // word q of each lane's step: k-steps 2q (lo) and 2q + 1 (hi)
-        if (q >= 2 && half_step) break;
-        half8 blo[2], bhi[2];
+      for (int j = 0; j < 2; ++j) load_b(rawA[j], j, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bring[j], q, sel, blo[j], bhi[j]);
+      for (int j = 0; j < 2; ++j) load_b(rawB[j], j, 1);
+    }
+    store_a(ar, As[1]);
+    __syncthreads();
+    if (live) {
+      const bool hs0 = half_step(0);
 #pragma unroll
-        for (int half_ = 0; half_ < 2; ++half_) {
-          half8 af[MI];
+      for (int j = 0; j < 2; ++j) dq_b2<QBITS>(rawA[j], 0, hs0 && h, bf[0][0][j], bf[0][1][j]);
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
-            af[i] = *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + acol + 16 * q + 8 * half_);
+      for (int i = 0; i < MI; ++i) af[0][i] = frag(As[0], i, (hs0 ? 32 : 64) * h);
+    }
+    // one step; rc: its raw weights (reloaded two steps ahead), rn: the next step's
+    auto run_step = [&](int step, BRaw2<QBITS>(&rc)[2], BRaw2<QBITS>(&rn)[2]) {
+      load_a(min(step + 2, nsteps - 1), ar);  // activations two steps ahead (clamped at the end)
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) {
+        const f16* Ab = As[step % 3];
+        const f16* An = As[(step + 1) % 3];
+        const bool hs = half_step(step), hsn = half_step(step + 1);
+        const int acol = (hs ? 32 : 64) * h, acoln = (hsn ? 32 : 64) * h;
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
+        for (int q = 0; q < 4; ++q) {
+          if (q >= 2 && hs) break;
+          const int c = q & 1;
+          const bool last = q == 3;  // the next word is word 0 of the next step
+          const int qn = last ? 0 : q + 1;
+          const bool seln = (last ? hsn : hs) && h;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], half_ ? bhi[j] : blo[j], acc[i][j]);
+          for (int hf = 0; hf < 2; ++hf) {
+            DqSrc d;
+            uint32_t tw[8];
+#pragma unroll
+            for (int g = 0; g < 2 * MI; ++g) {
+              const int i = g >> 1, j = g & 1;
+              acc[i][j] = mfma32(af[hf][i], bf[c][hf][j], acc[i][j]);
+              // the next half's fragments: half 1 of this word, or half 0 of the next word
+              if (g < MI) {
+                if (hf == 0) af[1][g] = frag(Ab, g, acol + 16 * q + 8);
+                else if (last) af[0][g] = frag(An, g, acoln);
+                else af[0][g] = frag(Ab, g, acol + 16 * (q + 1));
+              }
+              if (g == 0) {
+                if (last) d = dq_src_b2<QBITS>(rn[hf], qn, seln);
+                else d = dq_src_b2<QBITS>(rc[hf], qn, seln);
+              }
+              // this group's share of the word's dequantisation steps, taken four
+              // pairs at a time step by step, so that consecutive VALU ops are
+              // independent
+#pragma unroll
+              for (int o = g * NOPS / (2 * MI); o < (g + 1) * NOPS / (2 * MI); ++o) {
+                const int stage = (o % (4 * S)) / 4, pi = (o / (4 * S)) * 4 + o % 4;
+                dq_step<QBITS>(d, pi, stage, tw[pi]);
+                if (stage == S - 1) {
+                  const half2v v = as_half2(tw[pi]);
+                  half8& dst = bf[c ^ 1][pi >> 2][hf];
+                  dst[2 * (pi & 3)] = v[0];
+                  dst[2 * (pi & 3) + 1] = v[1];
+                }
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          if (q == 2) {  // this step's last word is dequantised: reload its set two steps ahead
+#pragma unroll
+            for (int j = 0; j < 2; ++j) load_b(rc[j], j, step + 2);
+          }
         }
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) load_b(bring[j], j, step + 1);
+      store_a(ar, As[(step + 2) % 3]);
+      __syncthreads();
+    };
+    for (int s0 = 0; s0 < nsteps; s0 += 2) {
+      run_step(s0, rawA, rawB);
+      if (s0 + 1 < nsteps) run_step(s0 + 1, rawB, rawA);
     }
-    store_a(ar, As[cur ^ 1]);  // (after the last step: a buffer nobody reads any more)
+  } else {
+    // B ring of one step: the weights of the next step are loaded right after
+    // this step's are dequantised.  Every load is unconditional (steps past K
+    // are clamped): a reload before the use needs a register copy, and those
+    // copies, like loads under a branch, make the compiler wait for every load
+    // in flight.
+    BRaw2<QBITS> bring[2];
+    load_a(0, ar);
+    if (live) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) load_b(bring[j], j, 0);
+    }
+    store_a(ar, As[0]);
     __syncthreads();
+    for (int step = 0; step < nsteps; ++step) {
+      const int cur = step & 1;
+      load_a(min(step + 1, nsteps - 1), ar);  // the next step's activations (the last step reloads its own)
+      // keep the activation loads here, a whole step ahead of their LDS store
+      // (the scheduler would otherwise sink them to their use)
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) {
+        const f16* Ab = As[cur];
+        // half step (K % 128 == 64, the last step): lane h holds block 4 step + h, A columns
+        // 32h .. 32h + 31, and words 2, 3 (k-steps 4 .. 7) are not run
+        const bool half_step = KM == 2 && 4 * step + 2 >= K / 32;
+        const bool sel = half_step && h;
+        const int acol = (half_step ? 32 : 64) * h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // word q of each lane's step: k-steps 2q (lo) and 2q + 1 (hi)
+          if (q >= 2 && half_step) break;
+          half8 blo[2], bhi[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bring[j], q, sel, blo[j], bhi[j]);
+#pragma unroll
+          for (int half_ = 0; half_ < 2; ++half_) {
+            half8 af[MI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+              af[i] = *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + acol + 16 * q + 8 * half_);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], half_ ? bhi[j] : blo[j], acc[i][j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) load_b(bring[j], j, step + 1);
+      }
+      store_a(ar, As[cur ^ 1]);  // (after the last step: a buffer nobody reads any more)
+      __syncthreads();
+    }
+
   }
 
   // ---- epilogue.  32 x 32 D layout: lane l holds column l % 32 and rows
