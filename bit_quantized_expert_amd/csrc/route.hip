@@ -184,8 +184,9 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
   }
 }
 
-// Many tokens: a 128-token x 128-expert tile per workgroup, 8 waves of
-// 32 tokens x 64 experts (2 x 4 MFMA blocks of 16 x 16).  The classes run
+// Many tokens: a 128-token x ET-expert tile per workgroup (ET = 128, or 64
+// when the 128-wide tiles would leave CUs without a workgroup), ET / 16
+// waves of 32 tokens x 64 experts (2 x 4 MFMA blocks of 16 x 16).  The classes run
 // one after another, so a wave keeps two accumulators per output (the class
 // chain and the running sum S) instead of eight.  K advances RK blocks per
 // step (within a class); the workgroup stages each step's activation and
@@ -196,8 +197,10 @@ __global__ __launch_bounds__(512) void router_mfma_kernel(const uint16_t* __rest
 // tile run one after another on one XCD (its activations are read into one
 // L2).
 // ---------------------------------------------------------------------------
-constexpr int kRtT = 128, kRtE = 128;  // tile: tokens x experts
-constexpr int kRtOutPitch = kRtE + 4;   // LDS row pitch of the logits tile in floats
+constexpr int kRtT = 128;  // tokens per tile
+// LDS row pitch of the logits tile in floats
+template <int ET>
+constexpr int rt_out_pitch() { return ET + 4; }
 constexpr int64_t kRouterGemmMinT = 2048;  // tokens from which the 128 x 128 tiles run
 // experts per workgroup of the router at <= 16 tokens (one workgroup per CU
 // at 512 experts); router_mfma_kernel's 16 x 16 tiles are below
@@ -206,9 +209,9 @@ constexpr int kRouterSmallEpw = 2;
 // units, so the 16 rows of a fragment read hit distinct banks
 template <int RK>
 constexpr int rt_pitch() { return RK * 32 + 8; }
-template <int RK>
+template <int RK, int ET>
 constexpr size_t rt_lds() {
-  return std::max(size_t(kRtT + kRtE) * rt_pitch<RK>() * 2, size_t(kRtT) * kRtOutPitch * 4);
+  return std::max(size_t(kRtT + ET) * rt_pitch<RK>() * 2, size_t(kRtT) * rt_out_pitch<ET>() * 4);
 }
 
 // RK = K blocks (of 32) per step; OCC = waves per SIMD the registers are
@@ -217,40 +220,42 @@ constexpr size_t rt_lds() {
 // steps whose loads are in flight during a step's MFMAs (register sets of
 // the staging ring: 2 fit beside RK = 4 in 256 registers, 1 beside RK = 2 in
 // 128, where the second workgroup of the CU covers the latency).
-template <int RK, int OCC, int PD>
-__global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
+template <int RK, int OCC, int PD, int ET>
+__global__ __launch_bounds__(4 * ET, OCC) void router_gemm_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
                                                             const uint16_t* __restrict__ w,
                                                             const float* __restrict__ bias, int E,
                                                             float* __restrict__ logits, int n_et, int64_t total) {
   constexpr int kPitch = rt_pitch<RK>();
-  extern __shared__ __attribute__((aligned(16))) uint16_t rs[];  // [kRtT + kRtE][kPitch] bf16, then the out tile
+  constexpr int NT = 4 * ET;                // threads: ET / 16 waves
+  constexpr int kOutPitch = rt_out_pitch<ET>();
+  extern __shared__ __attribute__((aligned(16))) uint16_t rs[];  // [kRtT + ET][kPitch] bf16, then the out tile
   const int64_t per = (total + 7) / 8;
   const int64_t L = int64_t(blockIdx.x % 8) * per + blockIdx.x / 8;
   if (L >= total) return;
   const int64_t tt = L / n_et;
   const int et = int(L - tt * n_et);
   const int64_t t0 = tt * kRtT;
-  const int e0 = et * kRtE;
+  const int e0 = et * ET;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int wt = wv >> 1, we = wv & 1;  // wave tile: tokens 32 wt .., experts 64 we ..
+  const int wt = wv / (ET / 64), we = wv % (ET / 64);  // wave tile: tokens 32 wt .., experts 64 we ..
   const int nkb = H / 32, cl = router_class_len(nkb);
 
-  // staging: 16-byte piece p = tid + 512 q (q < NQ) of the step's
-  // (kRtT + kRtE) rows x RK blocks: row p / (4 RK), piece p % (4 RK)
+  // staging: 16-byte piece p = tid + NT q (q < NQ) of the step's
+  // (kRtT + ET) rows x RK blocks: row p / (4 RK), piece p % (4 RK)
   // of the row's 64 RK bytes (block piece / 4 of the step, quarter piece % 4)
-  constexpr int NQ = (kRtT + kRtE) * RK * 4 / 512;
-  static_assert(NQ * 512 == (kRtT + kRtE) * RK * 4 && kRtT * RK * 4 == 512 * (NQ / 2),
-                "staging covers the step; the first NQ / 2 pieces of a thread are activation rows");
+  constexpr int NQ = (kRtT + ET) * RK * 4 / NT, QX = kRtT * RK * 4 / NT;
+  static_assert(NQ * NT == (kRtT + ET) * RK * 4 && QX * NT == kRtT * RK * 4,
+                "staging covers the step; the first QX pieces of a thread are activation rows");
   // element offsets from the tile's first activation / weight row (rows
   // past the end read the last real row; their results are never stored)
   const uint16_t* xt = x + t0 * H;
   const uint16_t* wt_ = w + int64_t(e0) * H;
-  const int t_last = int(min(T - t0, int64_t(kRtT))) - 1, e_last = min(E - e0, kRtE) - 1;
+  const int t_last = int(min(T - t0, int64_t(kRtT))) - 1, e_last = min(E - e0, ET) - 1;
   int off[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const int p = tid + 512 * q, row = p / (4 * RK), pc = p % (4 * RK);
+    const int p = tid + NT * q, row = p / (4 * RK), pc = p % (4 * RK);
     off[q] = (row < kRtT ? min(row, t_last) : min(row - kRtT, e_last)) * H + pc * 8;
   }
   // Steps: class c has sp = ceil(cl / RK) steps, step i of the tile is step
@@ -273,15 +278,15 @@ __global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* _
     const int b = real ? step_b(i) : 0, cend = real ? step_end(i) : 0;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int kb = b + (tid + 512 * q) % (4 * RK) / 4;
-      const uint16_t* base = q < NQ / 2 ? xt : wt_;  // pieces q < NQ/2 are activation rows
+      const int kb = b + (tid + NT * q) % (4 * RK) / 4;
+      const uint16_t* base = q < QX ? xt : wt_;  // pieces q < QX are activation rows
       st[q] = *reinterpret_cast<const uint4v*>(base + off[q] + (kb < cend ? b : 0) * 32);  // clamped, unconditional
     }
   };
   auto store_step = [&](const uint4v (&st)[NQ]) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int p = tid + 512 * q, row = p / (4 * RK), pc = p % (4 * RK);
+      const int p = tid + NT * q, row = p / (4 * RK), pc = p % (4 * RK);
       *reinterpret_cast<uint4v*>(rs + row * kPitch + pc * 8) = st[q];
     }
   };
@@ -340,18 +345,18 @@ __global__ __launch_bounds__(512, OCC) void router_gemm_kernel(const uint16_t* _
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) os[(32 * wt + 16 * i + 4 * g + r) * kRtOutPitch + 64 * we + 16 * j + n] = S[i][j][r];
+      for (int r = 0; r < 4; ++r) os[(32 * wt + 16 * i + 4 * g + r) * kOutPitch + 64 * we + 16 * j + n] = S[i][j][r];
   __syncthreads();
   // 16-byte stores and bias loads when every logits row and the bias are 16-byte aligned
   const bool vec = E % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(bias) & 15) == 0;
 #pragma unroll
-  for (int q = 0; q < kRtT * kRtE / 4 / 512; ++q) {
-    const int p = tid + 512 * q, row = p >> 5, c4 = (p & 31) * 4;
+  for (int q = 0; q < kRtT * ET / 4 / NT; ++q) {
+    const int p = tid + NT * q, row = p / (ET / 4), c4 = (p % (ET / 4)) * 4;
     const int64_t t = t0 + row;
     const int e = e0 + c4;
     if (t >= T || e >= E) continue;
-    float4v v = *reinterpret_cast<const float4v*>(os + row * kRtOutPitch + c4);
+    float4v v = *reinterpret_cast<const float4v*>(os + row * kOutPitch + c4);
     if (vec && e + 3 < E) {
       const float4v bv = bias ? *reinterpret_cast<const float4v*>(bias + e) : float4v{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<float4v*>(logits + t * E + e) = v + bv;
@@ -365,15 +370,21 @@ hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_
                               float* logits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (T >= kRouterGemmMinT) {
-    const int n_et = (E + kRtE - 1) / kRtE;
-    const int64_t total = (T + kRtT - 1) / kRtT * n_et;
-    const int64_t grid = (total + 7) / 8 * 8;
-    if (total >= 512)  // two resident workgroups per CU have work: the 128-register variant
-      router_gemm_kernel<2, 4, 1><<<unsigned(grid), 512, rt_lds<2>(), stream>>>(x, T, H, w, bias, E, logits, n_et,
-                                                                           total);
-    else
-      router_gemm_kernel<4, 2, 2><<<unsigned(grid), 512, rt_lds<4>(), stream>>>(x, T, H, w, bias, E, logits, n_et,
-                                                                           total);
+    const int64_t n_tt = (T + kRtT - 1) / kRtT;
+    const int n_et = (E + 127) / 128;
+    const int64_t total = n_tt * n_et;
+    if (total >= 512) {  // two resident workgroups per CU have work: the 128-register variant
+      router_gemm_kernel<2, 4, 1, 128><<<unsigned((total + 7) / 8 * 8), 512, rt_lds<2, 128>(), stream>>>(
+          x, T, H, w, bias, E, logits, n_et, total);
+    } else if (total >= 256) {
+      router_gemm_kernel<4, 2, 2, 128><<<unsigned((total + 7) / 8 * 8), 512, rt_lds<4, 128>(), stream>>>(
+          x, T, H, w, bias, E, logits, n_et, total);
+    } else {  // fewer 128-wide tiles than CUs: 64-expert tiles, twice as many
+      const int n_et64 = (E + 63) / 64;
+      const int64_t total64 = n_tt * n_et64;
+      router_gemm_kernel<4, 2, 2, 64><<<unsigned((total64 + 7) / 8 * 8), 256, rt_lds<4, 64>(), stream>>>(
+          x, T, H, w, bias, E, logits, n_et64, total64);
+    }
     return hipGetLastError();
   }
   if (T <= 16) {

@@ -127,13 +127,14 @@ def test_route_protocol(name, T):
 
 
 @pytest.mark.parametrize("H,E,T", [(2048, 512, 2100), (96, 40, 2200), (64, 8, 2050), (4096, 130, 2088),
-                                   (2048, 512, 65600), (64, 8, 70000)])
+                                   (2048, 512, 8192), (96, 40, 40000), (2048, 512, 65600), (64, 8, 70000)])
 def test_router_tiles_match_small_batches(H, E, T):
-    """Logits of T >= 2048 tokens at once (128 x 128 tiles, both step
-    variants) are the same bits as the same tokens routed 16 at a time
-    (16 x 16 tiles): one accumulation order for every batch size, ragged
-    token and expert tiles included.  Large T: a sample of the 16-token
-    chunks, the first and the last among them."""
+    """Logits of T >= 2048 tokens at once (128-token tiles 64 experts wide
+    below 256 tiles of 128, else 128 wide with either step variant) are the
+    same bits as the same tokens routed 16 at a time (16 x 16 tiles): one
+    accumulation order for every batch size, ragged token and expert tiles
+    included.  Large T: a sample of the 16-token chunks, the first and the
+    last among them."""
     M = _lib()
     wl = synth.custom("rt", H, 32, E, min(E, 8), 0, 2, T, seed=H + E, act_dtype=torch.bfloat16, zipf_bias=True)
     s = wl.shape
