@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_INDEX = 0, -1, -2, -3, -4, -5
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_F16 = 0, 1, 2
 ALGO = {"auto": 0, "gemv": 1, "grouped": 2}
 FFN_REUSE_PLAN, FFN_SKIP_GATEUP, FFN_SKIP_DOWN = 1, 2, 4
 ROUTE_TAIL_SKIP = 8  # moe_layer_forward option: the verify-window route tail skip
@@ -139,6 +139,8 @@ def _dtype_code(t) -> int:
         return MOE_F32
     if t.dtype == torch.bfloat16:
         return MOE_BF16
+    if t.dtype == torch.float16:
+        return MOE_F16
     raise ValueError(f"unsupported activation dtype {t.dtype}")
 
 

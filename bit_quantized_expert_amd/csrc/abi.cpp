@@ -127,10 +127,20 @@ int check_T(int64_t T, const moe_shape* s) {
   return MOE_OK;
 }
 
+// Router weights: fp32 or bf16.
 int check_dtype(moe_dtype d, const char* what) {
   if (d != MOE_F32 && d != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "%s dtype %d is not MOE_F32 or MOE_BF16", what, int(d));
   return MOE_OK;
 }
+
+// Activations: fp32, bf16 or fp16.
+int check_x_dtype(moe_dtype d) {
+  if (d != MOE_F32 && d != MOE_BF16 && d != MOE_F16)
+    return fail(MOE_ERR_INVALID_ARG, "x dtype %d is not MOE_F32, MOE_BF16 or MOE_F16", int(d));
+  return MOE_OK;
+}
+
+int x_kind(moe_dtype d) { return d == MOE_BF16 ? moe::kXBF16 : d == MOE_F16 ? moe::kXF16 : moe::kXF32; }
 
 int check_qw(const moe_qweights& q, const char* what, int n) {
   for (int m = 0; m < 3; ++m) {
@@ -212,7 +222,7 @@ hipError_t route_logits(const void* x, moe_dtype xd, int64_t T, const moe_layer*
     return moe::launch_router_mfma(static_cast<const uint16_t*>(x), T, s->hidden,
                                    static_cast<const uint16_t*>(L->w_router), L->router_bias, s->n_experts, logits,
                                    st);
-  return moe::launch_router_gemv(x, xd == MOE_BF16, T, s->hidden, L->w_router, L->router_dtype == MOE_BF16,
+  return moe::launch_router_gemv(x, x_kind(xd), T, s->hidden, L->w_router, L->router_dtype == MOE_BF16,
                                  L->router_bias, s->n_experts, logits, st);
 }
 
@@ -228,7 +238,7 @@ moe::FfnArgs ffn_args(const void* x, moe_dtype xd, int64_t T, const moe_layer* L
                       void* ws, const WsLayout& W) {
   moe::FfnArgs a{};
   a.x = x;
-  a.x_bf16 = xd == MOE_BF16;
+  a.x_kind = x_kind(xd);
   a.T = T;
   a.H = s->hidden;
   a.I = s->inter;
@@ -377,7 +387,7 @@ int moe_route(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* laye
     if (int r = check_shape(shape)) return r;
     if (int r = check_T(T, shape)) return r;
     if (int r = check_layer(layer, shape, true, false)) return r;
-    if (int r = check_dtype(x_dtype, "x")) return r;
+    if (int r = check_x_dtype(x_dtype)) return r;
     if (T == 0) return ok();
     if (!x || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "x, topk_idx and topk_w must be non-NULL");
     const WsLayout W = ws_layout(*shape, T);
@@ -419,7 +429,7 @@ int moe_expert_ffn(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer*
     if (int r = check_T(T, shape)) return r;
     if (int r = check_opts(opts, kOptsFfn)) return r;
     if (int r = check_layer(layer, shape, false, true)) return r;
-    if (int r = check_dtype(x_dtype, "x")) return r;
+    if (int r = check_x_dtype(x_dtype)) return r;
     if (T == 0) return ok();
     if (!x || !offsets || !sorted_pair || !y_sorted)
       return fail(MOE_ERR_INVALID_ARG, "x, offsets, sorted_pair and y_sorted must be non-NULL");
@@ -469,7 +479,7 @@ int check_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_l
   if (int r = check_T(T, shape)) return r;
   if (int r = check_opts(opts, kOptsLayer)) return r;
   if (int r = check_layer(layer, shape, true, true)) return r;
-  if (int r = check_dtype(x_dtype, "x")) return r;
+  if (int r = check_x_dtype(x_dtype)) return r;
   if (T == 0) return MOE_OK;
   if (tail_skip_rank(opts, T, shape) && pick_algo(opts, T, shape) != MOE_ALGO_GEMV)
     return fail(MOE_ERR_UNSUPPORTED, "the route tail skip runs on the GEMV (decode) path; T=%lld takes the grouped "

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 typedef _Float16 f16;
@@ -316,6 +318,17 @@ __device__ __forceinline__ void load_raw16(const SRC* src, Raw16<SRC>& r) {
 // hi = {4,12,5,13,6,14,7,15}).
 template <typename SRC>
 __device__ __forceinline__ void cvt_raw16(const Raw16<SRC>& r, half8& lo, half8& hi) {
+  if constexpr (std::is_same<SRC, f16>::value) {  // already fp16: the permutation alone
+    half8 a = __builtin_bit_cast(half8, r.q[0]), b = __builtin_bit_cast(half8, r.q[1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[2 * i] = a[i];
+      lo[2 * i + 1] = b[i];
+      hi[2 * i] = a[4 + i];
+      hi[2 * i + 1] = b[4 + i];
+    }
+    return;
+  }
   float v[16];
   if constexpr (sizeof(SRC) == 4) {
 #pragma unroll

@@ -1324,7 +1324,8 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
 #define GU(U_, X_) \
   gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a, Decode1Sel{}, \
                                                                                                a.slots)
-      if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+      if (a.x_kind == kXBF16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+      else if (a.x_kind == kXF16) { if (u64) GU(64, f16); else GU(32, f16); }
       else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
     } else {
@@ -1335,8 +1336,11 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
         const int n_rb = (a.I + 63) / 64;
         const int G = int(std::min<int64_t>(kPersGrid, int64_t(slots) * n_rb));
         const size_t lds_p = size_t(a.T) * (a.H + 8) * sizeof(f16);
-        if (a.x_bf16)
+        if (a.x_kind == kXBF16)
           gemv_gateup_pers_kernel<QBITS, 64, uint16_t, false>
+              <<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header, SelOut{});
+        else if (a.x_kind == kXF16)
+          gemv_gateup_pers_kernel<QBITS, 64, f16, false>
               <<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header, SelOut{});
         else
           gemv_gateup_pers_kernel<QBITS, 64, float, false>
@@ -1344,7 +1348,8 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
       } else {
         const dim3 grid(unsigned((max_rows + 16 * NW - 1) / (16 * NW)), unsigned(slots));
 #define GU(U_, X_) gemv_gateup_tp_kernel<QBITS, U_, X_, NW><<<grid, 128 * NW, lds, stream>>>(a)
-        if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+        if (a.x_kind == kXBF16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+        else if (a.x_kind == kXF16) { if (u64) GU(64, f16); else GU(32, f16); }
         else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
       }
@@ -1398,16 +1403,18 @@ hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t 
   const int n_rb = (a.I + 63) / 64;
   const int G = int(std::min<int64_t>(kPersGrid, int64_t(slots) * n_rb));
 #define GS(Q_, X_) gemv_gateup_pers_kernel<Q_, 64, X_, true><<<G, 512, lds_p, stream>>>(a, n_rb, G, nullptr, nullptr, so)
+#define GSQ(Q_)                          \
+  if (a.x_kind == kXBF16) GS(Q_, uint16_t); \
+  else if (a.x_kind == kXF16) GS(Q_, f16);  \
+  else GS(Q_, float)
   if (a.qbits == 2) {
-    if (a.x_bf16) GS(2, uint16_t);
-    else GS(2, float);
+    GSQ(2);
   } else if (a.qbits == 3) {
-    if (a.x_bf16) GS(3, uint16_t);
-    else GS(3, float);
+    GSQ(3);
   } else {
-    if (a.x_bf16) GS(4, uint16_t);
-    else GS(4, float);
+    GSQ(4);
   }
+#undef GSQ
 #undef GS
   return hipGetLastError();
 }
@@ -1439,7 +1446,8 @@ static hipError_t launch_decode1_q(const FfnArgs& a_full, const Decode1Sel& sel,
     const dim3 grid(unsigned((max_rows + 15) / 16), unsigned(slots));
 #define GU(U_, X_) \
   gemv_gateup_1tok_kernel<QBITS, U_, X_><<<grid, 64 * k1tokWaves, size_t(a.H) * 2, stream>>>(a_full, sel, a.slots)
-    if (a.x_bf16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+    if (a.x_kind == kXBF16) { if (u64) GU(64, uint16_t); else GU(32, uint16_t); }
+    else if (a.x_kind == kXF16) { if (u64) GU(64, f16); else GU(32, f16); }
     else { if (u64) GU(64, float); else GU(32, float); }
 #undef GU
   }

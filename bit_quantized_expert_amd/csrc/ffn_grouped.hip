@@ -556,9 +556,11 @@ int grouped_tile_rows(int64_t T, int k, int E) {
 hipError_t launch_x16(const FfnArgs& a, hipStream_t stream) {
   const int64_t groups = a.T * (a.H / 16);
   if (groups == 0) return hipSuccess;
-  if (a.x_bf16)
+  if (a.x_kind == kXBF16)
     x16_kernel<uint16_t><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const uint16_t*>(a.x), groups,
                                                                             a.x16);
+  else if (a.x_kind == kXF16)
+    x16_kernel<f16><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const f16*>(a.x), groups, a.x16);
   else
     x16_kernel<float><<<unsigned((groups + 255) / 256), 256, 0, stream>>>(static_cast<const float*>(a.x), groups, a.x16);
   return hipGetLastError();

@@ -26,9 +26,12 @@ struct QMat {
 
 // Everything the expert-FFN kernels read.  Slot s of the slot table is routed
 // expert slots[s].x (or the shared expert when slots[s].x < 0).
+// Activation element type of x.
+enum XKind { kXF32 = 0, kXBF16 = 1, kXF16 = 2 };
+
 struct FfnArgs {
   const void* x;
-  int x_bf16;
+  int x_kind;  // XKind
   int64_t T;
   int H, I, Is, k, E, qbits, has_shared;
   QMat rg, ru, rd;  // routed gate / up / down
@@ -57,7 +60,7 @@ hipError_t launch_repack(const uint8_t* codes, const uint16_t* scales, int64_t r
                          uint8_t* tcodes, uint16_t* tscales, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, int64_t rows, int cols,
                           int qbits, float* out, hipStream_t stream);
-hipError_t launch_router_gemv(const void* x, bool x_bf16, int64_t T, int H, const void* w, bool w_bf16,
+hipError_t launch_router_gemv(const void* x, int x_kind, int64_t T, int H, const void* w, bool w_bf16,
                               const float* bias, int E, float* logits, hipStream_t stream);
 hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_t* w, const float* bias,
                               int E, float* logits, hipStream_t stream);

@@ -24,7 +24,11 @@ namespace moe {
 // ---------------------------------------------------------------------------
 template <typename T_>
 __device__ __forceinline__ void load8(const T_* p, float* v) {
-  if constexpr (sizeof(T_) == 2) {
+  if constexpr (std::is_same<T_, f16>::value) {  // fp16 -> fp32 is exact
+    const half8 u = *reinterpret_cast<const half8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = float(u[i]);
+  } else if constexpr (sizeof(T_) == 2) {  // bf16 bits
     const uint4v u = *reinterpret_cast<const uint4v*>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -456,11 +460,13 @@ static void router_launch(const void* x, int64_t T, int H, const void* w, const 
   }
 }
 
-hipError_t launch_router_gemv(const void* x, bool x_bf16, int64_t T, int H, const void* w, bool w_bf16,
+hipError_t launch_router_gemv(const void* x, int x_kind, int64_t T, int H, const void* w, bool w_bf16,
                               const float* bias, int E, float* logits, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  if (x_bf16 && w_bf16) router_launch<uint16_t, uint16_t>(x, T, H, w, bias, E, logits, stream);
-  else if (x_bf16) router_launch<uint16_t, float>(x, T, H, w, bias, E, logits, stream);
+  if (x_kind == kXBF16 && w_bf16) router_launch<uint16_t, uint16_t>(x, T, H, w, bias, E, logits, stream);
+  else if (x_kind == kXBF16) router_launch<uint16_t, float>(x, T, H, w, bias, E, logits, stream);
+  else if (x_kind == kXF16 && w_bf16) router_launch<f16, uint16_t>(x, T, H, w, bias, E, logits, stream);
+  else if (x_kind == kXF16) router_launch<f16, float>(x, T, H, w, bias, E, logits, stream);
   else if (w_bf16) router_launch<float, uint16_t>(x, T, H, w, bias, E, logits, stream);
   else router_launch<float, float>(x, T, H, w, bias, E, logits, stream);
   return hipGetLastError();

@@ -77,7 +77,11 @@ typedef enum {
   MOE_ERR_INDEX = -5        /* an expert id outside [0, E) reached moe_permute */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* Element types.  Activations x: MOE_F32, MOE_BF16 or MOE_F16 (every kernel
+ * converts them to fp16 MFMA operands, exactly for fp16; the router then
+ * runs its fp32 path unless x and the router weights are both bf16).
+ * Router weights: MOE_F32 or MOE_BF16 (MOE_F16 there is MOE_ERR_INVALID_ARG). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
 
 /* Expert-FFN algorithm.  GEMV: fused dequant-GEMV for few tokens per expert
  * (decode).  GROUPED: dequantise tiles into LDS and run a grouped MFMA GEMM

@@ -87,6 +87,19 @@ def test_validation_before_any_device_call():
     assert st == L.MOE_ERR_WORKSPACE
     assert L.last_required_workspace() == need
     assert "MiB short" in L.last_error_detail()
+    # activation dtypes: fp32, bf16 and fp16 pass the checks (T == 0 then returns before any device work);
+    # another code is refused, and so are fp16 router weights
+    for xd in (L.MOE_F32, L.MOE_BF16, L.MOE_F16):
+        assert lib.moe_layer_forward(fake, xd, 0, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None,
+                                     None, None, None, 0, None) == L.MOE_OK
+    assert lib.moe_layer_forward(fake, 3, 4, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None, None,
+                                 None, fake, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    assert "x dtype" in L.last_error_detail()
+    lay16 = _layer_struct()
+    lay16.router_dtype = L.MOE_F16
+    assert lib.moe_layer_forward(fake, 1, 4, ctypes.byref(lay16), ctypes.byref(s), fake, None, None, None, None,
+                                 None, fake, 1 << 40, None) == L.MOE_ERR_INVALID_ARG
+    assert "router" in L.last_error_detail()
     # bad options
     o = L.Options(0, 1)
     assert lib.moe_layer_forward(fake, 1, 4, ctypes.byref(lay), ctypes.byref(s), fake, None, None, None, None,

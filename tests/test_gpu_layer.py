@@ -111,6 +111,29 @@ def test_ragged_layer(case):
     _check_layer(M, dl, x, "gemv")
 
 
+# fp16 activations (MOE_F16): every path's activation load and the router's
+# fp32 path; the oracle is fed the same fp16 values
+F16_CASES = [
+    # name, H, I, E, k, Is, qbits, T, algo
+    ("f1", 96, 96, 5, 3, 64, 2, 1, "auto"),       # single-token fused layer
+    ("f2", 256, 192, 33, 8, 96, 3, 1, "gemv"),    # single-token kernels, step by step
+    ("f3", 1024, 128, 8, 4, 128, 2, 16, "auto"),  # persistent gate/up with the selection inside
+    ("f4", 96, 96, 5, 3, 64, 3, 12, "gemv"),      # multi-token GEMV
+    ("f5", 128, 160, 12, 4, 0, 2, 37, "grouped"), # grouped GEMM (the fp16 copy kernel)
+    ("f6", 2048, 704, 16, 8, 704, 4, 40, "grouped"),
+]
+
+
+@pytest.mark.parametrize("case", F16_CASES, ids=[c[0] for c in F16_CASES])
+def test_fp16_activations(case):
+    M = _M()
+    name, H, I, E, k, Is, qb, T, algo = case
+    wl = synth.custom(name, H, I, E, k, Is, qb, T, seed=13, act_dtype=torch.bfloat16, zipf_bias=True)
+    dl = _layer(wl)
+    x = synth.tokens(wl, "cuda").half()
+    _check_layer(M, dl, x, algo)
+
+
 def test_decode1_full_shape():
     M = _M()
     dl = _layer(synth.WORKLOADS["decode1"])
