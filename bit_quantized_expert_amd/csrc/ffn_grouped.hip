@@ -186,11 +186,11 @@ __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, ha
 }
 
 // The main loop comes in two forms: the software-pipelined one (below) with
-// 96-row tiles at 2 and 3 bits, and a plain one where the pipeline's extra
-// registers would not fit beside 128-row tiles or 4-bit weights (the
-// compiler would spill).
+// 96-row tiles, and a plain one with 128-row tiles, where the pipeline's
+// extra registers do not fit beside the accumulators (the compiler would
+// spill).
 template <int QBITS, int BM>
-constexpr bool grouped_pipelined() { return BM == 96 && QBITS <= 3; }
+constexpr bool grouped_pipelined() { return BM == 96; }
 
 // KM: 0 = any K (a multiple of 32), 1 = K a multiple of 64, 2 = K a multiple
 // of 64 that may end in a half step (K % 128 == 64; the checks and selects of
