@@ -318,7 +318,8 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
     //     taken four pairs at a time so that consecutive VALU ops are
     //     independent;
     //   * the next half's activation fragments are read from LDS during this
-    //     half;
+    //     half, each row tile's right after its last MFMA of this half, into
+    //     the same registers;
     // each MFMA closing a group that a scheduling barrier keeps in this order
     // (left alone, the compiler issues the dequantisation in bursts between
     // MFMAs and waits for each LDS read right before its MFMA).
@@ -336,7 +337,7 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
     constexpr int S = dq_stages<QBITS>(), NOPS = 8 * S;  // dequantisation steps of one word
     BRaw2<QBITS> rawA[2], rawB[2];  // raw weights of the even and odd steps [column set]
     half8 bf[2][2][2];              // [word parity][half][column set]
-    half8 af[2][MI];                // [half parity][row tile]
+    half8 af[MI];                   // [row tile], refilled for the next half right after its last use
     auto frag = [&](const f16* Ab, int i, int col) -> half8 {
       return *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + col);
     };
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
 #pragma unroll
       for (int j = 0; j < 2; ++j) dq_b2<QBITS>(rawA[j], 0, hs0 && h, bf[0][0][j], bf[0][1][j]);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) af[0][i] = frag(As[0], i, (hs0 ? 32 : 64) * h);
+      for (int i = 0; i < MI; ++i) af[i] = frag(As[0], i, (hs0 ? 32 : 64) * h);
     }
     // one step; rc: its raw weights (reloaded two steps ahead), rn: the next step's
     auto run_step = [&](int step, BRaw2<QBITS>(&rc)[2], BRaw2<QBITS>(&rn)[2]) {
@@ -381,12 +382,13 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
 #pragma unroll
             for (int g = 0; g < 2 * MI; ++g) {
               const int i = g >> 1, j = g & 1;
-              acc[i][j] = mfma32(af[hf][i], bf[c][hf][j], acc[i][j]);
-              // the next half's fragments: half 1 of this word, or half 0 of the next word
-              if (g < MI) {
-                if (hf == 0) af[1][g] = frag(Ab, g, acol + 16 * q + 8);
-                else if (last) af[0][g] = frag(An, g, acoln);
-                else af[0][g] = frag(Ab, g, acol + 16 * (q + 1));
+              acc[i][j] = mfma32(af[i], bf[c][hf][j], acc[i][j]);
+              // after its second MFMA, row tile i's fragment of the next half: half 1
+              // of this word, or half 0 of the next word (read 2 MI - 2 MFMAs ahead)
+              if (j == 1) {
+                if (hf == 0) af[i] = frag(Ab, i, acol + 16 * q + 8);
+                else if (last) af[i] = frag(An, i, acoln);
+                else af[i] = frag(Ab, i, acol + 16 * (q + 1));
               }
               if (g == 0) {
                 if (last) d = dq_src_b2<QBITS>(rn[hf], qn, seln);
