@@ -69,7 +69,10 @@ WsLayout ws_layout(const moe_shape& s, int64_t T) {
   L.slots = take(size_t(E + 1) * 16);
   L.tile_expert = take(size_t(L.max_tiles) * 4);
   L.tile_m0 = take(size_t(L.max_tiles) * 4);
-  const int64_t n_chunks = P > moe::kSmallPairs ? (P + moe::kPermChunk - 1) / moe::kPermChunk : 0;
+  // chunk rows of the multi-workgroup permutation: moe_permute's (kPermChunk pairs each) or the
+  // prefill layer's (moe::select_chunks: 16 tokens each, at least as many)
+  const int64_t n_chunks =
+      P > moe::kSmallPairs ? std::max<int64_t>((P + moe::kPermChunk - 1) / moe::kPermChunk, moe::select_chunks(T)) : 0;
   L.chunk_hist = take(size_t(n_chunks) * size_t(E + 1) * 4);
   L.end_perm = off;
   L.h_routed = take(size_t(P) * s.inter * 2);
@@ -509,20 +512,37 @@ int layer_forward_ws(const void* x, moe_dtype x_dtype, int64_t T, const moe_laye
       return device_status(fused_decode(x, x_dtype, T, layer, shape, out, residual, next_in_bf16, idx, w, ws, W, st,
                                         kc),
                            "moe_layer_forward");
-    hipError_t e = do_route(x, x_dtype, T, layer, shape, at<float>(ws, W.logits), idx, w, st);
-    if (e != hipSuccess) return device_status(e, "moe_layer_forward/route");
     int32_t* offsets = at<int32_t>(ws, W.offsets);
     int32_t* sorted_pair = at<int32_t>(ws, W.sorted_pair);
     int32_t* pair_pos = at<int32_t>(ws, W.pair_pos);
-    e = moe::launch_permute(idx, T * shape->top_k, shape->n_experts, at<int32_t>(ws, W.counts), offsets, sorted_pair,
-                            pair_pos, at<int32_t>(ws, W.header), at<int32_t>(ws, W.chunk_hist), st);
-    if (e != hipSuccess) return device_status(e, "moe_layer_forward/permute");
     float* y = at<float>(ws, W.y_sorted);
     float* s_out = shape->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;
     // the grouped GEMM hands the routed rows to the combine in fp16 (half the bytes of the layer's
     // largest intermediate); the stand-alone moe_expert_ffn / moe_combine keep fp32
     _Float16* yh = algo == MOE_ALGO_GROUPED ? reinterpret_cast<_Float16*>(y) : nullptr;
-    e = do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, algo, ws, W, st, 0, yh);
+    int ffn_flags = 0;
+    hipError_t e;
+    if (algo == MOE_ALGO_GROUPED && T * shape->top_k > moe::kSmallPairs) {
+      // prefill: top-k, permutation, plan and the fp16 copy of x in three launches
+      e = route_logits(x, x_dtype, T, layer, shape, at<float>(ws, W.logits), st);
+      if (e != hipSuccess) return device_status(e, "moe_layer_forward/route");
+      const moe::FfnArgs a = ffn_args(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, ws, W);
+      const moe::PlanOut plan{a.has_shared ? 1 : 0, moe::grouped_tile_rows(T, shape->top_k, shape->n_experts),
+                              at<int32_t>(ws, W.header), at<int4>(ws, W.slots), at<int32_t>(ws, W.tile_expert),
+                              at<int32_t>(ws, W.tile_m0)};
+      e = moe::launch_select_plan(at<float>(ws, W.logits), x, x_kind(x_dtype), T, shape->hidden, shape->n_experts,
+                                  shape->top_k, idx, w, at<int32_t>(ws, W.chunk_hist), at<int32_t>(ws, W.counts),
+                                  offsets, sorted_pair, pair_pos, a.x16, plan, st);
+      if (e != hipSuccess) return device_status(e, "moe_layer_forward/select");
+      ffn_flags = MOE_FFN_REUSE_PLAN;
+    } else {
+      e = do_route(x, x_dtype, T, layer, shape, at<float>(ws, W.logits), idx, w, st);
+      if (e != hipSuccess) return device_status(e, "moe_layer_forward/route");
+      e = moe::launch_permute(idx, T * shape->top_k, shape->n_experts, at<int32_t>(ws, W.counts), offsets,
+                              sorted_pair, pair_pos, at<int32_t>(ws, W.header), at<int32_t>(ws, W.chunk_hist), st);
+      if (e != hipSuccess) return device_status(e, "moe_layer_forward/permute");
+    }
+    e = do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, algo, ws, W, st, ffn_flags, yh);
     if (e != hipSuccess) return device_status(e, "moe_layer_forward/ffn");
     e = yh ? moe::launch_combine_f16y(yh, pair_pos, w, s_out, T, shape->hidden, shape->top_k, out, residual,
                                       next_in_bf16, st)

@@ -20,13 +20,14 @@
 
 #include "common.h"
 #include "launch.h"
+#include "plan.h"
 #include "select.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Plan: slot table (active experts in ascending id order, then the shared
-// expert) and the grouped-GEMM tile list, from offsets.  One workgroup.
+// Plan: slot table and grouped-GEMM tile list from offsets (plan.h).  One
+// workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int64_t T,
                                                    int has_shared, int tile_bm, int32_t* __restrict__ header,
@@ -36,64 +37,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   __shared__ int flag[kMaxExperts];
   __shared__ int ntile[kMaxExperts];
   __shared__ int tmp[16];
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    const int c = offsets[e + 1] - offsets[e];
-    flag[e] = c > 0;
-    ntile[e] = tile_bm > 0 ? (c + tile_bm - 1) / tile_bm : 0;
-  }
-  __syncthreads();
-  const int n_active = block_scan_fast(flag, E, tmp);
-  const int n_routed_tiles = block_scan_fast(ntile, E, tmp);
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    const int lo = offsets[e];
-    const int c = offsets[e + 1] - lo;
-    if (c > 0) {
-      // token mask of the slot for small batches (the GEMV kernels then know
-      // the slot's tokens without reading sorted_pair); 0 = not given.  Pair
-      // ids that are not those of a permutation of T * k pairs cannot make a
-      // correct result; their tokens are clamped into [0, T) so that no
-      // kernel reads outside the activations.
-      uint32_t mask = 0u;
-      if (sorted_pair && T <= kGemvMaxM) {
-        for (int q = lo; q < lo + c; ++q) {
-          const int t = min(max(sorted_pair[q] / k, 0), int(T) - 1);
-          mask |= 1u << t;
-        }
-      }
-      slots[flag[e]] = int4{e, lo, c, int(mask)};
-    }
-    if (tile_bm > 0) {
-      int pos = ntile[e];
-      for (int m0 = 0; m0 < c; m0 += tile_bm, ++pos) {
-        tile_expert[pos] = e;
-        tile_m0[pos] = m0;
-      }
-    }
-  }
-  const int n_valid = n_active + (has_shared ? 1 : 0);
-  if (threadIdx.x == 0 && has_shared)
-    slots[n_active] = int4{-1, 0, int(T), sorted_pair && T <= kGemvMaxM ? int((1u << T) - 1u) : 0};
-  for (int s = n_valid + threadIdx.x; s < n_slots; s += 1024) slots[s] = int4{0, 0, 0, 0};
-  int n_tiles = n_routed_tiles;
-  if (tile_bm > 0 && has_shared) {
-    const int st = int((T + tile_bm - 1) / tile_bm);
-    for (int i = threadIdx.x; i < st; i += 1024) {
-      tile_expert[n_routed_tiles + i] = -1;
-      tile_m0[n_routed_tiles + i] = i * tile_bm;
-    }
-    n_tiles += st;
-  }
-  if (threadIdx.x == 0) {  // the error word belongs to the permutation: left as it is
-    header[kHdrActive] = n_active;
-    header[kHdrValid] = n_valid;
-    header[kHdrTiles] = n_tiles;
-  }
+  plan_from_offsets(offsets, E, T, has_shared, tile_bm, header, slots, tile_expert, tile_m0, n_slots, sorted_pair,
+                    k, flag, ntile, tmp);
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm, int32_t* header,
                        int4* slots, int32_t* tile_expert, int32_t* tile_m0, const int32_t* sorted_pair, int k,
                        hipStream_t stream) {
-  const int n_slots = int(std::min<int64_t>(E, T * 32)) + 1;  // covers min(E, T*k) + 1 for every k <= 32
+  const int n_slots = plan_slots(E, T);
   plan_kernel<<<1, 1024, 0, stream>>>(offsets, E, T, has_shared, tile_bm, header, slots, tile_expert, tile_m0,
                                       n_slots, sorted_pair, k);
   return hipGetLastError();

@@ -77,6 +77,24 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts,
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm,
                        int32_t* header, int4* slots, int32_t* tile_expert, int32_t* tile_m0,
                        const int32_t* sorted_pair, int k, hipStream_t stream);
+// Outputs of the plan (plan.h) for the fused prefill sequence below.
+struct PlanOut {
+  int has_shared, tile_bm;
+  int32_t* header;
+  int4* slots;
+  int32_t* tile_expert;
+  int32_t* tile_m0;
+};
+// The prefill layer's top-k + softmax weights, stable permutation, plan and
+// fp16 operand copy of x (x16) in three launches over chunks of 16 tokens
+// (chunk_hist: select_chunks(T) x (E + 1) ints).  The same results as
+// launch_topk, launch_permute, launch_plan and the grouped FFN's x16 copy.
+// k <= 64 and H % 16 == 0 (else hipErrorInvalidValue, nothing launched).
+int select_chunks(int64_t T);
+hipError_t launch_select_plan(const float* logits, const void* x, int x_kind, int64_t T, int H, int E, int k,
+                              int32_t* idx, float* w, int32_t* chunk_hist, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos, _Float16* x16, const PlanOut& plan,
+                              hipStream_t stream);
 // Decode-layer selection on one workgroup (T <= 16): top-k + softmax weights,
 // permutation and the slot table (int4 {expert or -1 for shared, first sorted
 // position, token count, token mask: bit t set when token t uses the slot};

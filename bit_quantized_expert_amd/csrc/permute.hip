@@ -10,6 +10,7 @@
 // workspace header (word 0).
 #include "common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -123,16 +124,18 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
 }
 
 // Column scan of the per-chunk histograms: chunk_hist[c][e] becomes the
-// number of pairs of expert e in chunks before c.  Workgroup = 64 experts x
-// 16 chunk groups.  Column totals go to counts[e] (and, for the extra column
-// E of out-of-range ids, to the header).
+// number of pairs of expert e in chunks before c.  Workgroup = CG experts x
+// 1024 / CG chunk groups.  Column totals go to counts[e] (and, for the extra
+// column E of out-of-range ids, to the header).
+template <int CG>
 __global__ __launch_bounds__(1024) void permute_colscan_kernel(int32_t* __restrict__ chunk_hist, int n_chunks,
                                                               int E, int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ header) {
-  __shared__ int part[16][64];
-  const int col = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + col;
-  const int per = (n_chunks + 15) / 16;
+  constexpr int RG = 1024 / CG;
+  __shared__ int part[RG][CG];
+  const int col = threadIdx.x % CG, grp = threadIdx.x / CG;
+  const int e = blockIdx.x * CG + col;
+  const int per = (n_chunks + RG - 1) / RG;
   const int c_lo = min(n_chunks, grp * per), c_hi = min(n_chunks, c_lo + per);
   int s = 0;
   if (e <= E)
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(1024) void permute_colscan_kernel(int32_t* __restri
   __syncthreads();
   if (grp == 0) {
     int run = 0;
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < RG; ++g) {
       const int v = part[g][col];
       part[g][col] = run;
       run += v;
@@ -205,9 +208,145 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts,
   }
   const int n_chunks = int((P + kPermChunk - 1) / kPermChunk);
   permute_hist_kernel<<<n_chunks, 256, 0, stream>>>(idx, P, E, chunk_hist);
-  permute_colscan_kernel<<<(E + 1 + 63) / 64, 1024, 0, stream>>>(chunk_hist, n_chunks, E, counts, header);
+  permute_colscan_kernel<64><<<(E + 1 + 63) / 64, 1024, 0, stream>>>(chunk_hist, n_chunks, E, counts, header);
   offsets_scan_kernel<<<1, 1024, 0, stream>>>(counts, E, offsets);
   permute_scatter_kernel<<<n_chunks, 1024, 0, stream>>>(idx, P, E, chunk_hist, offsets, sorted_pair, pair_pos);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The prefill layer's selection, permutation and plan in three launches (the
+// stepwise calls keep the kernels above).  A chunk is kSelChunk consecutive
+// tokens (at most 16 k <= 512 pairs):
+//   1. select_hist_kernel: one workgroup per chunk, one wave per token: the
+//      top-k and weights (the wave routines every path shares), the chunk's
+//      histogram row, and the fp16 operand copy of the chunk's activations
+//      for the grouped GEMM (the x16 layout: permuted 16-groups);
+//   2. permute_colscan_kernel over the chunk rows;
+//   3. scatter_plan_kernel: one workgroup per chunk scans the counts into
+//      offsets itself, then places the chunk's pairs (stable: ascending pair
+//      index within each expert, the result of launch_permute); workgroup 0
+//      also writes the offsets and the plan (plan.h).
+// ---------------------------------------------------------------------------
+constexpr int kSelChunk = 16;
+
+template <int V, typename XT>
+__global__ __launch_bounds__(1024) void select_hist_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                          int k, int32_t* __restrict__ idx_out,
+                                                          float* __restrict__ w_out, int32_t* __restrict__ chunk_hist,
+                                                          const XT* __restrict__ x, int H, f16* __restrict__ x16) {
+  __shared__ int cnt[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t t0 = int64_t(blockIdx.x) * kSelChunk;
+  const int nt = int(min(int64_t(kSelChunk), T - t0));
+  // the chunk's activation groups (16 elements each): the first two per
+  // thread are loaded before the selection and converted after it
+  const int64_t g0 = t0 * (H / 16);
+  const int ng = nt * (H / 16);
+  Raw16<XT> xr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) load_raw16(x + (g0 + min(tid + 1024 * i, ng - 1)) * 16, xr[i]);
+  for (int e = tid; e <= E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  if (wv < nt) {
+    const int64_t t = t0 + wv;
+    int my_idx;
+    float my_w;
+    wave_topk_softmax<V>(logits + t * E, E, k, my_idx, my_w);
+    if (lane < k) {
+      idx_out[t * k + lane] = my_idx;
+      w_out[t * k + lane] = my_w;
+      atomicAdd(&cnt[my_idx], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* row = chunk_hist + int64_t(blockIdx.x) * (E + 1);
+  for (int e = tid; e <= E; e += 1024) row[e] = cnt[e];  // column E (ids out of range) stays 0
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int g = tid + 1024 * i;
+    if (g >= ng) continue;
+    half8 lo, hi;
+    cvt_raw16(xr[i], lo, hi);
+    half8* d = reinterpret_cast<half8*>(x16 + (g0 + g) * 16);
+    d[0] = lo;
+    d[1] = hi;
+  }
+  for (int g = tid + 2048; g < ng; g += 1024) {
+    half8 lo, hi;
+    load_x16<XT>(x + (g0 + g) * 16, lo, hi);
+    half8* d = reinterpret_cast<half8*>(x16 + (g0 + g) * 16);
+    d[0] = lo;
+    d[1] = hi;
+  }
+}
+
+__global__ __launch_bounds__(1024) void scatter_plan_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E,
+                                                           const int32_t* __restrict__ chunk_hist,
+                                                           const int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_pair,
+                                                           int32_t* __restrict__ pair_pos, PlanOut plan) {
+  __shared__ int base[kMaxExperts + 1];
+  __shared__ int flag[kMaxExperts];
+  __shared__ int ntile[kMaxExperts];
+  __shared__ int tmp[16];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) base[e] = counts[e];
+  __syncthreads();
+  const int total = block_scan_fast(base, E, tmp);
+  if (tid == 0) base[E] = total;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += 1024) offsets[e] = base[e];
+    plan_from_offsets(base, E, T, plan.has_shared, plan.tile_bm, plan.header, plan.slots, plan.tile_expert,
+                      plan.tile_m0, plan_slots(E, T), nullptr, k, flag, ntile, tmp);
+    __syncthreads();
+  }
+  const int32_t* row = chunk_hist + int64_t(blockIdx.x) * (E + 1);
+  for (int e = tid; e < E; e += 1024) base[e] += row[e];
+  const int64_t p0 = int64_t(blockIdx.x) * kSelChunk * k;
+  const int np = int(min(int64_t(kSelChunk), T - int64_t(blockIdx.x) * kSelChunk)) * k;
+  const int64_t p = p0 + tid;
+  int e = -1;
+  if (tid < np) {
+    e = idx[p];
+    if (e < 0 || e >= E) e = -1;
+  }
+  __syncthreads();
+  const int pos = stable_place_1024(e, expert_bits(E), base);
+  if (pos >= 0) sorted_pair[pos] = int32_t(p);
+  if (tid < np) pair_pos[p] = pos;
+}
+
+int select_chunks(int64_t T) { return int((T + kSelChunk - 1) / kSelChunk); }
+
+hipError_t launch_select_plan(const float* logits, const void* x, int x_kind, int64_t T, int H, int E, int k,
+                              int32_t* idx, float* w, int32_t* chunk_hist, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pair, int32_t* pair_pos, f16* x16, const PlanOut& plan,
+                              hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (k < 1 || k * kSelChunk > 1024 || H % 16 != 0) return hipErrorInvalidValue;
+  const int nc = select_chunks(T);
+  const int v = (E + 63) / 64;
+#define SH(V_, XT_) \
+  select_hist_kernel<V_, XT_><<<nc, 1024, 0, stream>>>(logits, T, E, k, idx, w, chunk_hist, static_cast<const XT_*>(x), H, x16)
+#define SHX(V_)                       \
+  if (x_kind == kXBF16) SH(V_, uint16_t); \
+  else if (x_kind == kXF16) SH(V_, f16);  \
+  else SH(V_, float)
+  if (v <= 1) { SHX(1); }
+  else if (v <= 2) { SHX(2); }
+  else if (v <= 4) { SHX(4); }
+  else if (v <= 8) { SHX(8); }
+  else if (v <= 16) { SHX(16); }
+  else if (v <= 32) { SHX(32); }
+  else { SHX(64); }
+#undef SHX
+#undef SH
+  permute_colscan_kernel<16><<<(E + 1 + 15) / 16, 1024, 0, stream>>>(chunk_hist, nc, E, counts, plan.header);
+  scatter_plan_kernel<<<nc, 1024, 0, stream>>>(idx, T, k, E, chunk_hist, counts, offsets, sorted_pair, pair_pos,
+                                               plan);
   return hipGetLastError();
 }
 

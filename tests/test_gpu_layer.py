@@ -121,6 +121,7 @@ F16_CASES = [
     ("f4", 96, 96, 5, 3, 64, 3, 12, "gemv"),      # multi-token GEMV
     ("f5", 128, 160, 12, 4, 0, 2, 37, "grouped"), # grouped GEMM (the fp16 copy kernel)
     ("f6", 2048, 704, 16, 8, 704, 4, 40, "grouped"),
+    ("f7", 160, 96, 3, 1, 32, 4, 2100, "grouped"),  # more than 2048 pairs: the fused selection pass
 ]
 
 

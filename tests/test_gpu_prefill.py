@@ -88,6 +88,40 @@ def test_grouped_ragged_layer(case):
     assert_close_output(out.cpu().numpy(), ref, f"{name} grouped")
 
 
+# More than 2048 pairs: the layer's top-k, permutation, plan and fp16 copy of x
+# run as one selection pass over 16-token chunks (ragged last chunks, the
+# smallest and largest expert counts and top-k, hidden beyond 2048 groups per
+# chunk); its selection must equal the stand-alone route's bit for bit
+FUSED = [
+    # name, H, I, E, k, Is, qbits, T, dtype
+    ("v1", 96, 96, 5, 3, 64, 2, 1001, torch.bfloat16),
+    ("v2", 128, 160, 12, 4, 0, 3, 777, torch.float32),
+    ("v3", 64, 32, 4096, 32, 32, 2, 100, torch.bfloat16),
+    ("v4", 160, 96, 3, 1, 32, 4, 2100, torch.bfloat16),
+    ("v5", 2304, 96, 64, 2, 96, 2, 1030, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+def test_grouped_fused_selection(case):
+    M = _M()
+    name, H, I, E, k, Is, qb, T, dt = case
+    wl = synth.custom(name, H, I, E, k, Is, qb, T, seed=23, act_dtype=dt, zipf_bias=True)
+    dl = _layer(wl)
+    s = dl.s
+    x = synth.tokens(wl, "cuda")
+    out, idx, w = _forward(M, dl, x, "grouped")
+    logits = torch.empty(T, E, device="cuda")
+    idx2 = torch.empty_like(idx)
+    w2 = torch.empty_like(w)
+    M.route(x, dl.q, s, idx2, w2, logits=logits)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(w, w2)
+    ref = dl.oracle_forward(x_to_numpy(x), idx=idx.cpu().numpy(), return_all=True)
+    check_route_protocol(logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), ref["logits"], k)
+    assert_close_output(out.cpu().numpy(), ref["out"], f"{name} grouped, fused selection")
+
+
 def test_tiny_grouped():
     M = _M()
     dl = _layer(synth.WORKLOADS["tiny"])
