@@ -275,9 +275,10 @@ moe::FfnArgs ffn_args(const void* x, moe_dtype xd, int64_t T, const moe_layer* L
 hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, const moe_shape* s,
                   const int32_t* offsets, const int32_t* sorted_pair, float* y_sorted, float* shared_out,
                   moe_algo algo, void* ws, const WsLayout& W, hipStream_t st, int flags = 0,
-                  _Float16* y_sorted_h = nullptr) {
+                  _Float16* y_sorted_h = nullptr, _Float16* shared_out_h = nullptr) {
   moe::FfnArgs a = ffn_args(x, xd, T, L, s, offsets, sorted_pair, y_sorted, shared_out, ws, W);
   a.y_sorted_h = y_sorted_h;
+  a.shared_out_h = shared_out_h;
   const int tile_bm = algo == MOE_ALGO_GROUPED ? moe::grouped_tile_rows(T, s->top_k, s->n_experts) : 0;
   if (!(flags & MOE_FFN_REUSE_PLAN)) {
     hipError_t e = moe::launch_plan(offsets, s->n_experts, T, a.has_shared, tile_bm, at<int32_t>(ws, W.header),
@@ -517,9 +518,10 @@ int layer_forward_ws(const void* x, moe_dtype x_dtype, int64_t T, const moe_laye
     int32_t* pair_pos = at<int32_t>(ws, W.pair_pos);
     float* y = at<float>(ws, W.y_sorted);
     float* s_out = shape->shared_inter > 0 ? at<float>(ws, W.shared_out) : nullptr;
-    // the grouped GEMM hands the routed rows to the combine in fp16 (half the bytes of the layer's
-    // largest intermediate); the stand-alone moe_expert_ffn / moe_combine keep fp32
+    // the grouped GEMM hands the routed and shared rows to the combine in fp16 (half the bytes of
+    // the layer's largest intermediates); the stand-alone moe_expert_ffn / moe_combine keep fp32
     _Float16* yh = algo == MOE_ALGO_GROUPED ? reinterpret_cast<_Float16*>(y) : nullptr;
+    _Float16* sh = algo == MOE_ALGO_GROUPED ? reinterpret_cast<_Float16*>(s_out) : nullptr;
     int ffn_flags = 0;
     hipError_t e;
     if (algo == MOE_ALGO_GROUPED && T * shape->top_k > moe::kSmallPairs) {
@@ -542,9 +544,9 @@ int layer_forward_ws(const void* x, moe_dtype x_dtype, int64_t T, const moe_laye
                               sorted_pair, pair_pos, at<int32_t>(ws, W.header), at<int32_t>(ws, W.chunk_hist), st);
       if (e != hipSuccess) return device_status(e, "moe_layer_forward/permute");
     }
-    e = do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, algo, ws, W, st, ffn_flags, yh);
+    e = do_ffn(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, algo, ws, W, st, ffn_flags, yh, sh);
     if (e != hipSuccess) return device_status(e, "moe_layer_forward/ffn");
-    e = yh ? moe::launch_combine_f16y(yh, pair_pos, w, s_out, T, shape->hidden, shape->top_k, out, residual,
+    e = yh ? moe::launch_combine_f16y(yh, pair_pos, w, sh, T, shape->hidden, shape->top_k, out, residual,
                                       next_in_bf16, st)
            : moe::launch_combine(y, pair_pos, w, s_out, T, shape->hidden, shape->top_k, out, residual,
                                  next_in_bf16, st);

@@ -42,8 +42,9 @@ __device__ __forceinline__ void rmsnorm_row(const float* __restrict__ res, int H
 // are loaded per group (the launch picks JG >= k where it can, so no row is
 // loaded twice); RES: a residual row is read (only then).  YT: the expert
 // rows are fp32, or fp16 (the grouped-GEMM layer, where these rows are most
-// of the layer's memory traffic); the sum is fp32 either way.  shared points
-// at [T][H] fp32 rows: the shared expert's output when has_shared, else any
+// of the layer's memory traffic); the sum is fp32 either way.  ST: the
+// shared rows' type (fp32, or fp16 beside fp16 expert rows).  shared points
+// at [T][H] rows: the shared expert's output when has_shared, else any
 // readable rows (their values are replaced by 0; they may be out or res, so
 // the pointer is not restrict).
 template <typename YT>
@@ -62,9 +63,9 @@ struct YRow<f16> {
   }
 };
 
-template <int CPT, int JG, bool RES, typename YT>
+template <int CPT, int JG, bool RES, typename YT, typename ST>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, const int32_t* __restrict__ pos,
-                                                     const float* __restrict__ w, const float* shared,
+                                                     const float* __restrict__ w, const ST* shared,
                                                      int has_shared, int H, int k, float* __restrict__ out,
                                                      float* __restrict__ res, uint16_t* __restrict__ next_in) {
   typedef typename YRow<YT>::raw Raw;
@@ -81,14 +82,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, 
     int cc[CPT];
     bool on[CPT];
     float4v acc[CPT], r[CPT];
-    const float* srow = shared + t * H;
+    const ST* srow = shared + t * H;
     const float* rrow = RES ? res + t * H : nullptr;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = c0 + 256 * u + int(threadIdx.x);
       on[u] = c < H4;
       cc[u] = on[u] ? c : 0;
-      acc[u] = reinterpret_cast<const float4v*>(srow)[cc[u]];  // zeroed below when there is no shared expert
+      acc[u] = YRow<ST>::cvt(reinterpret_cast<const typename YRow<ST>::raw*>(srow)[cc[u]]);  // zeroed below without a shared expert
       if constexpr (RES) r[u] = reinterpret_cast<const float4v*>(rrow)[cc[u]];
     }
     for (int j0 = 0; j0 < k; j0 += JG) {
@@ -170,20 +171,21 @@ hipError_t launch_residual_rmsnorm(const float* res, int64_t T, int H, uint16_t*
   return hipGetLastError();
 }
 
-template <typename YT>
+template <typename YT, typename ST>
 static hipError_t launch_combine_t(const YT* y_sorted, const int32_t* pair_pos, const float* topk_w,
-                                   const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
+                                   const ST* shared_out, int64_t T, int H, int k, float* out, float* residual,
                                    uint16_t* next_in, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const dim3 grid = dim3(unsigned(T));
-  // rows standing in for a missing shared output: out or residual ([T][H] fp32, one is non-null)
-  const float* sh = shared_out ? shared_out : (out ? out : residual);
+  // rows standing in for a missing shared output: out or residual ([T][H] fp32, one is non-null; as
+  // fp16 rows they are read within the first half of each fp32 row)
+  const ST* sh = shared_out ? shared_out : reinterpret_cast<const ST*>(out ? out : residual);
   const int has_sh = shared_out != nullptr;
 #define CB(JG_)                                                                                              \
-  (residual ? combine_kernel<2, JG_, true, YT><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, sh, has_sh, \
-                                                                         H, k, out, residual, next_in)          \
-            : combine_kernel<2, JG_, false, YT><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, sh, has_sh, \
-                                                                          H, k, out, residual, next_in))
+  (residual ? combine_kernel<2, JG_, true, YT, ST><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, sh,      \
+                                                                             has_sh, H, k, out, residual, next_in) \
+            : combine_kernel<2, JG_, false, YT, ST><<<grid, 256, 0, stream>>>(y_sorted, pair_pos, topk_w, sh,     \
+                                                                              has_sh, H, k, out, residual, next_in))
   if (k <= 4) CB(4);
   else if (k <= 8) CB(8);
   else if (k <= 10) CB(10);
@@ -195,13 +197,15 @@ static hipError_t launch_combine_t(const YT* y_sorted, const int32_t* pair_pos, 
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                           const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
                           uint16_t* next_in, hipStream_t stream) {
-  return launch_combine_t<float>(y_sorted, pair_pos, topk_w, shared_out, T, H, k, out, residual, next_in, stream);
+  return launch_combine_t<float, float>(y_sorted, pair_pos, topk_w, shared_out, T, H, k, out, residual, next_in,
+                                        stream);
 }
 
 hipError_t launch_combine_f16y(const _Float16* y_sorted, const int32_t* pair_pos, const float* topk_w,
-                               const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
+                               const _Float16* shared_out, int64_t T, int H, int k, float* out, float* residual,
                                uint16_t* next_in, hipStream_t stream) {
-  return launch_combine_t<f16>(y_sorted, pair_pos, topk_w, shared_out, T, H, k, out, residual, next_in, stream);
+  return launch_combine_t<f16, f16>(y_sorted, pair_pos, topk_w, shared_out, T, H, k, out, residual, next_in,
+                                    stream);
 }
 
 }  // namespace moe

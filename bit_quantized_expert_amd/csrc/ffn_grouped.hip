@@ -185,6 +185,12 @@ __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, ha
   dq_word<QBITS>(dq_src_b2<QBITS>(r, q, sel), lo, hi);
 }
 
+// silu(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (about 1e-7
+// relative error, far below the fp16 rounding of h).
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * g));
+}
+
 // The main loop comes in two forms: the software-pipelined one (below) with
 // 96-row tiles, and a plain one with 128-row tiles, where the pipeline's
 // extra registers do not fit beside the accumulators (the compiler would
@@ -341,16 +347,19 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
     auto frag = [&](const f16* Ab, int i, int col) -> half8 {
       return *reinterpret_cast<const half8*>(Ab + (32 * i + n) * kLDA2 + col);
     };
-    load_a(0, ar);
-    store_a(ar, As[0]);
-    load_a(min(1, nsteps - 1), ar);
-    if (live) {
+    {  // the first two steps' activations and weights are all in flight together
+      uint4v ar1[AI][2];
+      load_a(0, ar);
+      load_a(min(1, nsteps - 1), ar1);
+      if (live) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) load_b(rawA[j], j, 0);
+        for (int j = 0; j < 2; ++j) load_b(rawA[j], j, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) load_b(rawB[j], j, 1);
+        for (int j = 0; j < 2; ++j) load_b(rawB[j], j, 1);
+      }
+      store_a(ar, As[0]);
+      store_a(ar1, As[1]);
     }
-    store_a(ar, As[1]);
     __syncthreads();
     if (live) {
       const bool hs0 = half_step(0);
@@ -479,29 +488,66 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
   }
 
   // ---- epilogue.  32 x 32 D layout: lane l holds column l % 32 and rows
-  // 8*(q/4) + 4*(l/32) + q%4, q = 0..15.
-  if (!live) return;
+  // 8*(q/4) + 4*(l/32) + q%4, q = 0..15.  fp16 outputs (h; the down rows a
+  // layer hands to its combine) are transposed through the activation
+  // buffers (free after the loop's last barrier) and leave as whole 16-byte
+  // row pieces; fp32 rows are stored lane by lane.
+  f16* o16 = nullptr;  // the tile's first output row (fp16), row pitch Nrows, or null
+  if constexpr (GATEUP) {
+    o16 = shared ? a.h_shared + int64_t(m0) * Nrows : a.h_routed + int64_t(lo + m0) * Nrows;
+  } else {
+    f16* y16 = shared ? a.shared_out_h : a.y_sorted_h;
+    if (y16) o16 = y16 + int64_t(shared ? m0 : lo + m0) * Nrows;
+  }
+  if (o16 != nullptr) {
+    constexpr int OW = (GATEUP ? 32 : 64) * NWV;              // output columns of the tile
+    constexpr int AS_H = (PIPE ? 3 : 2) * BM * kLDA2;          // halves of the activation buffers
+    constexpr int NPASS = BM * (OW + 8) <= AS_H ? 1 : 2;       // column passes
+    constexpr int PW = OW / NPASS, OP = PW + 8;                // pass width, LDS row pitch (halves)
+    constexpr int PPR = PW / 8;                                // 16-byte pieces per row
+    static_assert(BM * OP <= AS_H && OW % NPASS == 0, "an output pass fits the activation buffers");
+    f16* ot = &As[0][0];
+    const int c0 = nt * OW;                // the tile's first output column
+    const int wc = (GATEUP ? 32 : 64) * wv;  // this wave's first column in the tile
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+    for (int pass = 0; pass < NPASS; ++pass) {
+      if (live && wc >= pass * PW && wc < (pass + 1) * PW) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
-      if (m >= rows_valid) continue;
-      if constexpr (GATEUP) {
-        const int gr = brow[0];
-        if (bok[0]) {
-          const float g = acc[i][0][q], u = acc[i][1][q];
-          const float hv = g / (1.0f + expf(-g)) * u;
-          const int hw = shared ? a.Is : a.I;
-          f16* hout = shared ? a.h_shared + int64_t(m0 + m) * hw : a.h_routed + int64_t(lo + m0 + m) * hw;
-          hout[hcol(gr)] = f16(hv);
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int m = 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+            if constexpr (GATEUP) {
+              // h in the permuted 16-group column order (hcol keeps a 16-group in place)
+              ot[m * OP + hcol(wc + n) - pass * PW] = f16(silu_fast(acc[i][0][q]) * acc[i][1][q]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 2; ++j) ot[m * OP + wc + 32 * j + n - pass * PW] = f16(acc[i][j][q]);
+            }
+          }
         }
-      } else if (!shared && a.y_sorted_h) {  // routed rows in fp16
-        f16* yrow = a.y_sorted_h + int64_t(lo + m0 + m) * H;
+      }
+      __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (bok[j]) yrow[brow[j]] = f16(acc[i][j][q]);
-      } else {
+      for (int it = tid; it < BM * PPR; it += NT) {
+        const int r = it / PPR, pc = it - r * PPR;
+        const int col = c0 + pass * PW + 8 * pc;
+        if (r < rows_valid && col < Nrows)
+          *reinterpret_cast<uint4v*>(o16 + int64_t(r) * Nrows + col) =
+              *reinterpret_cast<const uint4v*>(ot + r * OP + 8 * pc);
+      }
+      if (pass + 1 < NPASS) __syncthreads();
+    }
+    return;
+  }
+  if (!live) return;
+  if constexpr (!GATEUP) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = 32 * i + 8 * (q >> 2) + 4 * h + (q & 3);
+        if (m >= rows_valid) continue;
         float* yrow = shared ? a.shared_out + int64_t(m0 + m) * H : a.y_sorted + int64_t(lo + m0 + m) * H;
 #pragma unroll
         for (int j = 0; j < 2; ++j)

@@ -51,6 +51,8 @@ struct FfnArgs {
   _Float16* y_sorted_h;        // grouped GEMM: when non-null, the routed down output
                                //   goes here in fp16 instead of y_sorted
   float* shared_out;           // [T][H] or null
+  _Float16* shared_out_h;      // grouped GEMM: when non-null, the shared down output goes
+                               //   here in fp16 instead of shared_out
 };
 
 hipError_t launch_quantize(const float* w, int64_t rows, int cols, int qbits, uint8_t* codes,
@@ -147,9 +149,10 @@ hipError_t launch_residual_rmsnorm(const float* res, int64_t T, int H, uint16_t*
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                           const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
                           uint16_t* next_in, hipStream_t stream);
-// The same combine over fp16 expert rows (the grouped-GEMM layer's y_sorted_h).
+// The same combine over fp16 expert rows and fp16 shared rows (the grouped-GEMM
+// layer's y_sorted_h and shared_out_h).
 hipError_t launch_combine_f16y(const _Float16* y_sorted, const int32_t* pair_pos, const float* topk_w,
-                               const float* shared_out, int64_t T, int H, int k, float* out, float* residual,
+                               const _Float16* shared_out, int64_t T, int H, int k, float* out, float* residual,
                                uint16_t* next_in, hipStream_t stream);
 
 }  // namespace moe
