@@ -46,7 +46,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 constexpr int kMinTileBM = 32;
 
 struct WsLayout {
-  size_t header, slots, tile_expert, tile_m0, chunk_hist, h_routed, h_shared, x16;
+  size_t header, slots, tile_desc, chunk_hist, h_routed, h_shared, x16;
   size_t end_perm, end_ffn;
   size_t logits, end_route;
   size_t topk_idx, topk_w, counts, offsets, sorted_pair, pair_pos, slot_expert, y_sorted, shared_out, total;
@@ -67,8 +67,7 @@ WsLayout ws_layout(const moe_shape& s, int64_t T) {
                 (s.shared_inter > 0 ? (T + kMinTileBM - 1) / kMinTileBM : 0) + 2;
   L.header = take(moe::kHdrWords * 4);
   L.slots = take(size_t(E + 1) * 16);
-  L.tile_expert = take(size_t(L.max_tiles) * 4);
-  L.tile_m0 = take(size_t(L.max_tiles) * 4);
+  L.tile_desc = take(size_t(L.max_tiles) * 16);
   // chunk rows of the multi-workgroup permutation: moe_permute's (kPermChunk pairs each) or the
   // prefill layer's (moe::select_chunks: 16 tokens each, at least as many)
   const int64_t n_chunks =
@@ -262,8 +261,7 @@ moe::FfnArgs ffn_args(const void* x, moe_dtype xd, int64_t T, const moe_layer* L
   a.sorted_pair = sorted_pair;
   a.header = at<int32_t>(ws, W.header);
   a.slots = at<int4>(ws, W.slots);
-  a.tile_expert = at<int32_t>(ws, W.tile_expert);
-  a.tile_m0 = at<int32_t>(ws, W.tile_m0);
+  a.tile_desc = at<int4>(ws, W.tile_desc);
   a.h_routed = at<_Float16>(ws, W.h_routed);
   a.h_shared = at<_Float16>(ws, W.h_shared);
   a.x16 = at<_Float16>(ws, W.x16);
@@ -282,8 +280,7 @@ hipError_t do_ffn(const void* x, moe_dtype xd, int64_t T, const moe_layer* L, co
   const int tile_bm = algo == MOE_ALGO_GROUPED ? moe::grouped_tile_rows(T, s->top_k, s->n_experts) : 0;
   if (!(flags & MOE_FFN_REUSE_PLAN)) {
     hipError_t e = moe::launch_plan(offsets, s->n_experts, T, a.has_shared, tile_bm, at<int32_t>(ws, W.header),
-                                    at<int4>(ws, W.slots), at<int32_t>(ws, W.tile_expert),
-                                    at<int32_t>(ws, W.tile_m0), sorted_pair, s->top_k, st);
+                                    at<int4>(ws, W.slots), at<int4>(ws, W.tile_desc), sorted_pair, s->top_k, st);
     if (e != hipSuccess) return e;
     if (algo == MOE_ALGO_GROUPED) {  // the grouped gate/up GEMM reads x through its fp16 copy
       e = moe::launch_x16(a, st);
@@ -530,8 +527,7 @@ int layer_forward_ws(const void* x, moe_dtype x_dtype, int64_t T, const moe_laye
       if (e != hipSuccess) return device_status(e, "moe_layer_forward/route");
       const moe::FfnArgs a = ffn_args(x, x_dtype, T, layer, shape, offsets, sorted_pair, y, s_out, ws, W);
       const moe::PlanOut plan{a.has_shared ? 1 : 0, moe::grouped_tile_rows(T, shape->top_k, shape->n_experts),
-                              at<int32_t>(ws, W.header), at<int4>(ws, W.slots), at<int32_t>(ws, W.tile_expert),
-                              at<int32_t>(ws, W.tile_m0)};
+                              at<int32_t>(ws, W.header), at<int4>(ws, W.slots), at<int4>(ws, W.tile_desc)};
       e = moe::launch_select_plan(at<float>(ws, W.logits), x, x_kind(x_dtype), T, shape->hidden, shape->n_experts,
                                   shape->top_k, idx, w, at<int32_t>(ws, W.chunk_hist), at<int32_t>(ws, W.counts),
                                   offsets, sorted_pair, pair_pos, a.x16, plan, st);

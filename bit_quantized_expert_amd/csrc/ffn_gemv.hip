@@ -31,22 +31,21 @@ namespace moe {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int64_t T,
                                                    int has_shared, int tile_bm, int32_t* __restrict__ header,
-                                                   int4* __restrict__ slots, int32_t* __restrict__ tile_expert,
-                                                   int32_t* __restrict__ tile_m0, int n_slots,
+                                                   int4* __restrict__ slots, int4* __restrict__ tile_desc, int n_slots,
                                                    const int32_t* __restrict__ sorted_pair, int k) {
   __shared__ int flag[kMaxExperts];
   __shared__ int ntile[kMaxExperts];
   __shared__ int tmp[16];
-  plan_from_offsets(offsets, E, T, has_shared, tile_bm, header, slots, tile_expert, tile_m0, n_slots, sorted_pair,
-                    k, flag, ntile, tmp);
+  plan_from_offsets(offsets, E, T, has_shared, tile_bm, header, slots, tile_desc, n_slots, sorted_pair, k, flag,
+                    ntile, tmp);
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm, int32_t* header,
-                       int4* slots, int32_t* tile_expert, int32_t* tile_m0, const int32_t* sorted_pair, int k,
+                       int4* slots, int4* tile_desc, const int32_t* sorted_pair, int k,
                        hipStream_t stream) {
   const int n_slots = plan_slots(E, T);
-  plan_kernel<<<1, 1024, 0, stream>>>(offsets, E, T, has_shared, tile_bm, header, slots, tile_expert, tile_m0,
-                                      n_slots, sorted_pair, k);
+  plan_kernel<<<1, 1024, 0, stream>>>(offsets, E, T, has_shared, tile_bm, header, slots, tile_desc, n_slots,
+                                      sorted_pair, k);
   return hipGetLastError();
 }
 

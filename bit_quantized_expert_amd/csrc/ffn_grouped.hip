@@ -220,11 +220,11 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
   const int L = (b % 8) * per + b / 8;
   if (L >= total) return;
   const int tile = L / n_ntiles, nt = L - tile * n_ntiles;
-  const int e = a.tile_expert[tile], m0 = a.tile_m0[tile];
+  const int4 td = a.tile_desc[tile];  // {expert (-1 = shared), first row in the segment, first sorted row, rows}
+  const int e = td.x, m0 = td.y;
   const bool shared = e < 0;
-  const int lo = shared ? 0 : a.offsets[e];
-  const int m_count = shared ? int(a.T) : a.offsets[e + 1] - lo;
-  const int rows_valid = min(BM, m_count - m0);
+  const int lo = td.z - m0;  // first sorted row of the expert's segment (0 for the shared expert)
+  const int rows_valid = td.w;
   const int H = a.H;
   const int K = GATEUP ? H : (shared ? a.Is : a.I);
   const int Nrows = GATEUP ? (shared ? a.Is : a.I) : H;  // rows of each weight matrix

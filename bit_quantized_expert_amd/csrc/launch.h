@@ -40,8 +40,8 @@ struct FfnArgs {
   const int32_t* sorted_pair;
   const int32_t* header;       // workspace header (n_active, n_valid, n_tiles)
   const int4* slots;           // slot table, see launch_select_small
-  const int32_t* tile_expert;  // grouped GEMM tiles: expert id (-1 = shared)
-  const int32_t* tile_m0;      //                     first row of the tile
+  const int4* tile_desc;       // grouped GEMM tiles: {expert (-1 = shared), first row of the
+                               //   tile in the expert's rows, first sorted row, rows}
   _Float16* h_routed;          // [P][I] SwiGLU activations, sorted order, columns
                                //   permuted within groups of 16 (MFMA operand order)
   _Float16* h_shared;          // [T][Is]
@@ -77,15 +77,14 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts,
 // T <= kGemvMaxM the slots carry their token masks (else mask 0); the
 // persistent gate/up kernel relies on them.
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm,
-                       int32_t* header, int4* slots, int32_t* tile_expert, int32_t* tile_m0,
-                       const int32_t* sorted_pair, int k, hipStream_t stream);
+                       int32_t* header, int4* slots, int4* tile_desc, const int32_t* sorted_pair, int k,
+                       hipStream_t stream);
 // Outputs of the plan (plan.h) for the fused prefill sequence below.
 struct PlanOut {
   int has_shared, tile_bm;
   int32_t* header;
   int4* slots;
-  int32_t* tile_expert;
-  int32_t* tile_m0;
+  int4* tile_desc;
 };
 // The prefill layer's top-k + softmax weights, stable permutation, plan and
 // fp16 operand copy of x (x16) in three launches over chunks of 16 tokens

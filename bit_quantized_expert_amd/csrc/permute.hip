@@ -299,8 +299,8 @@ __global__ __launch_bounds__(1024) void scatter_plan_kernel(const int32_t* __res
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int e = tid; e <= E; e += 1024) offsets[e] = base[e];
-    plan_from_offsets(base, E, T, plan.has_shared, plan.tile_bm, plan.header, plan.slots, plan.tile_expert,
-                      plan.tile_m0, plan_slots(E, T), nullptr, k, flag, ntile, tmp);
+    plan_from_offsets(base, E, T, plan.has_shared, plan.tile_bm, plan.header, plan.slots, plan.tile_desc,
+                      plan_slots(E, T), nullptr, k, flag, ntile, tmp);
     __syncthreads();
   }
   const int32_t* row = chunk_hist + int64_t(blockIdx.x) * (E + 1);

@@ -4,8 +4,10 @@
 //     expert, each int4 {expert or -1, first sorted position, rows, token
 //     mask (T <= kGemvMaxM with sorted_pair given, else 0)}; slots past the
 //     last valid one are zeroed;
-//   * grouped-GEMM tile list (tile_bm > 0): (expert, first row) of every
-//     tile_bm-row tile of each expert's segment, then the shared expert's;
+//   * grouped-GEMM tile list (tile_bm > 0): int4 {expert (-1 = shared), first
+//     row of the tile in the expert's rows, first sorted row (for the shared
+//     expert: the first token), rows of the tile} of every tile_bm-row tile
+//     of each expert's segment, then the shared expert's;
 //   * header words: active experts, valid slots, tiles (the error word
 //     belongs to the permutation and is left as it is).
 #pragma once
@@ -18,8 +20,7 @@ namespace moe {
 // tmp: 16 ints of LDS.
 __device__ inline void plan_from_offsets(const int32_t* offsets, int E, int64_t T, int has_shared, int tile_bm,
                                          int32_t* __restrict__ header, int4* __restrict__ slots,
-                                         int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_m0,
-                                         int n_slots, const int32_t* __restrict__ sorted_pair, int k, int* flag,
+                                         int4* __restrict__ tile_desc, int n_slots, const int32_t* __restrict__ sorted_pair, int k, int* flag,
                                          int* ntile, int* tmp) {
   for (int e = threadIdx.x; e < E; e += 1024) {
     const int c = offsets[e + 1] - offsets[e];
@@ -49,10 +50,7 @@ __device__ inline void plan_from_offsets(const int32_t* offsets, int E, int64_t 
     }
     if (tile_bm > 0) {
       int pos = ntile[e];
-      for (int m0 = 0; m0 < c; m0 += tile_bm, ++pos) {
-        tile_expert[pos] = e;
-        tile_m0[pos] = m0;
-      }
+      for (int m0 = 0; m0 < c; m0 += tile_bm, ++pos) tile_desc[pos] = int4{e, m0, lo + m0, min(tile_bm, c - m0)};
     }
   }
   const int n_valid = n_active + (has_shared ? 1 : 0);
@@ -62,10 +60,8 @@ __device__ inline void plan_from_offsets(const int32_t* offsets, int E, int64_t 
   int n_tiles = n_routed_tiles;
   if (tile_bm > 0 && has_shared) {
     const int st = int((T + tile_bm - 1) / tile_bm);
-    for (int i = threadIdx.x; i < st; i += 1024) {
-      tile_expert[n_routed_tiles + i] = -1;
-      tile_m0[n_routed_tiles + i] = i * tile_bm;
-    }
+    for (int i = threadIdx.x; i < st; i += 1024)
+      tile_desc[n_routed_tiles + i] = int4{-1, i * tile_bm, i * tile_bm, int(min(int64_t(tile_bm), T - i * tile_bm))};
     n_tiles += st;
   }
   if (threadIdx.x == 0) {
