@@ -24,9 +24,11 @@ namespace moe {
 //   - The 16 waves then take turns in order: wave w reads base[e], places its
 //     pairs at base[e] + rank, and the group's highest lane advances base[e]
 //     (its read of the same word is an earlier instruction of the same wave).
-// Returns the pair's position, or -1 for e < 0 (an id outside [0, E)).
+// Only waves below nw hold pairs (the others place nothing and skip the
+// turns after theirs).  Returns the pair's position, or -1 for e < 0 (an id
+// outside [0, E)).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int stable_place_1024(int e, int nbits, int* base) {
+__device__ __forceinline__ int stable_place_1024(int e, int nbits, int* base, int nw = 16) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint64_t same = __ballot(e >= 0);
   for (int b = 0; b < nbits; ++b) {
@@ -38,7 +40,7 @@ __device__ __forceinline__ int stable_place_1024(int e, int nbits, int* base) {
   const bool last = (same >> lane) == 1ull;  // no higher lane of the group
   const int cnt = __builtin_popcountll(same);
   int pos = -1;
-  for (int w = 0; w < 16; ++w) {
+  for (int w = 0; w < nw; ++w) {
     if (wv == w && e >= 0) {
       const int b = base[e];
       pos = b + rank;
@@ -219,14 +221,15 @@ hipError_t launch_permute(const int32_t* idx, int64_t P, int E, int32_t* counts,
 // stepwise calls keep the kernels above).  A chunk is kSelChunk consecutive
 // tokens (at most 16 k <= 512 pairs):
 //   1. select_hist_kernel: one workgroup per chunk, one wave per token: the
-//      top-k and weights (the wave routines every path shares), the chunk's
-//      histogram row, and the fp16 operand copy of the chunk's activations
-//      for the grouped GEMM (the x16 layout: permuted 16-groups);
+//      top-k and weights (the wave routines every path shares) and the
+//      chunk's histogram row; a second workgroup per chunk writes the fp16
+//      operand copy of the chunk's activations for the grouped GEMM (the x16
+//      layout: permuted 16-groups);
 //   2. permute_colscan_kernel over the chunk rows;
 //   3. scatter_plan_kernel: one workgroup per chunk scans the counts into
 //      offsets itself, then places the chunk's pairs (stable: ascending pair
-//      index within each expert, the result of launch_permute); workgroup 0
-//      also writes the offsets and the plan (plan.h).
+//      index within each expert, the result of launch_permute); one more
+//      workgroup writes the offsets and the plan (plan.h).
 // ---------------------------------------------------------------------------
 constexpr int kSelChunk = 16;
 
@@ -234,18 +237,25 @@ template <int V, typename XT>
 __global__ __launch_bounds__(1024) void select_hist_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                           int k, int32_t* __restrict__ idx_out,
                                                           float* __restrict__ w_out, int32_t* __restrict__ chunk_hist,
-                                                          const XT* __restrict__ x, int H, f16* __restrict__ x16) {
+                                                          const XT* __restrict__ x, int H, f16* __restrict__ x16,
+                                                          int nc) {
   __shared__ int cnt[kMaxExperts + 1];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (int(blockIdx.x) >= nc) {  // workgroups nc..2nc-1: the fp16 copy of chunk blockIdx - nc's activations
+    const int64_t t0 = int64_t(blockIdx.x - nc) * kSelChunk;
+    const int64_t g0 = t0 * (H / 16);
+    const int ng = int(min(int64_t(kSelChunk), T - t0)) * (H / 16);
+    for (int g = tid; g < ng; g += 1024) {
+      half8 lo, hi;
+      load_x16<XT>(x + (g0 + g) * 16, lo, hi);
+      half8* d = reinterpret_cast<half8*>(x16 + (g0 + g) * 16);
+      d[0] = lo;
+      d[1] = hi;
+    }
+    return;
+  }
   const int64_t t0 = int64_t(blockIdx.x) * kSelChunk;
   const int nt = int(min(int64_t(kSelChunk), T - t0));
-  // the chunk's activation groups (16 elements each): the first two per
-  // thread are loaded before the selection and converted after it
-  const int64_t g0 = t0 * (H / 16);
-  const int ng = nt * (H / 16);
-  Raw16<XT> xr[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) load_raw16(x + (g0 + min(tid + 1024 * i, ng - 1)) * 16, xr[i]);
   for (int e = tid; e <= E; e += 1024) cnt[e] = 0;
   __syncthreads();
   if (wv < nt) {
@@ -262,23 +272,6 @@ __global__ __launch_bounds__(1024) void select_hist_kernel(const float* __restri
   __syncthreads();
   int32_t* row = chunk_hist + int64_t(blockIdx.x) * (E + 1);
   for (int e = tid; e <= E; e += 1024) row[e] = cnt[e];  // column E (ids out of range) stays 0
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int g = tid + 1024 * i;
-    if (g >= ng) continue;
-    half8 lo, hi;
-    cvt_raw16(xr[i], lo, hi);
-    half8* d = reinterpret_cast<half8*>(x16 + (g0 + g) * 16);
-    d[0] = lo;
-    d[1] = hi;
-  }
-  for (int g = tid + 2048; g < ng; g += 1024) {
-    half8 lo, hi;
-    load_x16<XT>(x + (g0 + g) * 16, lo, hi);
-    half8* d = reinterpret_cast<half8*>(x16 + (g0 + g) * 16);
-    d[0] = lo;
-    d[1] = hi;
-  }
 }
 
 __global__ __launch_bounds__(1024) void scatter_plan_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int E,
@@ -286,7 +279,7 @@ __global__ __launch_bounds__(1024) void scatter_plan_kernel(const int32_t* __res
                                                            const int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_pair,
-                                                           int32_t* __restrict__ pair_pos, PlanOut plan) {
+                                                           int32_t* __restrict__ pair_pos, PlanOut plan, int nc) {
   __shared__ int base[kMaxExperts + 1];
   __shared__ int flag[kMaxExperts];
   __shared__ int ntile[kMaxExperts];
@@ -295,13 +288,13 @@ __global__ __launch_bounds__(1024) void scatter_plan_kernel(const int32_t* __res
   for (int e = tid; e < E; e += 1024) base[e] = counts[e];
   __syncthreads();
   const int total = block_scan_fast(base, E, tmp);
-  if (tid == 0) base[E] = total;
-  __syncthreads();
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == nc) {  // the extra workgroup: offsets and the plan
+    if (tid == 0) base[E] = total;
+    __syncthreads();
     for (int e = tid; e <= E; e += 1024) offsets[e] = base[e];
     plan_from_offsets(base, E, T, plan.has_shared, plan.tile_bm, plan.header, plan.slots, plan.tile_desc,
                       plan_slots(E, T), nullptr, k, flag, ntile, tmp);
-    __syncthreads();
+    return;
   }
   const int32_t* row = chunk_hist + int64_t(blockIdx.x) * (E + 1);
   for (int e = tid; e < E; e += 1024) base[e] += row[e];
@@ -314,7 +307,7 @@ __global__ __launch_bounds__(1024) void scatter_plan_kernel(const int32_t* __res
     if (e < 0 || e >= E) e = -1;
   }
   __syncthreads();
-  const int pos = stable_place_1024(e, expert_bits(E), base);
+  const int pos = stable_place_1024(e, expert_bits(E), base, (np + 63) / 64);
   if (pos >= 0) sorted_pair[pos] = int32_t(p);
   if (tid < np) pair_pos[p] = pos;
 }
@@ -329,8 +322,9 @@ hipError_t launch_select_plan(const float* logits, const void* x, int x_kind, in
   if (k < 1 || k * kSelChunk > 1024 || H % 16 != 0) return hipErrorInvalidValue;
   const int nc = select_chunks(T);
   const int v = (E + 63) / 64;
-#define SH(V_, XT_) \
-  select_hist_kernel<V_, XT_><<<nc, 1024, 0, stream>>>(logits, T, E, k, idx, w, chunk_hist, static_cast<const XT_*>(x), H, x16)
+#define SH(V_, XT_)                                                                                       \
+  select_hist_kernel<V_, XT_><<<2 * nc, 1024, 0, stream>>>(logits, T, E, k, idx, w, chunk_hist,            \
+                                                           static_cast<const XT_*>(x), H, x16, nc)
 #define SHX(V_)                       \
   if (x_kind == kXBF16) SH(V_, uint16_t); \
   else if (x_kind == kXF16) SH(V_, f16);  \
@@ -345,8 +339,8 @@ hipError_t launch_select_plan(const float* logits, const void* x, int x_kind, in
 #undef SHX
 #undef SH
   permute_colscan_kernel<16><<<(E + 1 + 15) / 16, 1024, 0, stream>>>(chunk_hist, nc, E, counts, plan.header);
-  scatter_plan_kernel<<<nc, 1024, 0, stream>>>(idx, T, k, E, chunk_hist, counts, offsets, sorted_pair, pair_pos,
-                                               plan);
+  scatter_plan_kernel<<<nc + 1, 1024, 0, stream>>>(idx, T, k, E, chunk_hist, counts, offsets, sorted_pair, pair_pos,
+                                                   plan, nc);
   return hipGetLastError();
 }
 
