@@ -296,15 +296,29 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
       r[i][1] = p[1];
     }
   };
+  // rows past the tile's rows are zeroed once in every buffer and never
+  // stored again (their MFMA products are discarded either way; zero operands
+  // cost the matrix cores less power than copies of a real row)
   auto store_a = [&](const uint4v (&r)[AI][2], f16* buf) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      if (AITEMS % NT != 0 && tid + NT * i >= AITEMS) continue;
+      if ((AITEMS % NT != 0 && tid + NT * i >= AITEMS) || arow[i] >= rows_valid) continue;
       uint4v* d = reinterpret_cast<uint4v*>(buf + arow[i] * kLDA2 + agrp[i] * 16);
       d[0] = r[i][0];
       d[1] = r[i][1];
     }
   };
+  if (rows_valid < BM) {
+#pragma unroll
+    for (int bb = 0; bb < (PIPE ? 3 : 2); ++bb)
+#pragma unroll
+      for (int i = 0; i < AI; ++i) {
+        if ((AITEMS % NT != 0 && tid + NT * i >= AITEMS) || arow[i] < rows_valid) continue;
+        uint4v* d = reinterpret_cast<uint4v*>(As[bb] + arow[i] * kLDA2 + agrp[i] * 16);
+        d[0] = uint4v{0u, 0u, 0u, 0u};
+        d[1] = uint4v{0u, 0u, 0u, 0u};
+      }
+  }
 
   float16v acc[MI][2];
 #pragma unroll
