@@ -6,12 +6,13 @@
 // 125-billion-parameter model ...", intro and Step 1 byte table); with many
 // tokens per expert the work is a dense contraction per expert, so it runs
 // on the matrix cores.  Each tile of the list is (expert or shared, first row
-// m0) with BM = 128 rows of the expert's sorted segment.
+// m0) with BM = 128 (8 waves) or 96 (4 waves) rows of the expert's sorted
+// segment.
 //
-//   gate/up : [BM x H] activations x [H x 256 gate + 256 up rows] -> SwiGLU
+//   gate/up : [BM x H] activations x [H x 32 W gate + 32 W up rows] -> SwiGLU
 //             epilogue -> h (fp16, the permuted column order of the GEMV path)
-//   down    : [BM x I] h x [I x 512 down rows] -> y_sorted / shared_out (fp32;
-//             routed rows in fp16 when the caller asks for y_sorted_h)
+//   down    : [BM x I] h x [I x 64 W down rows] -> y_sorted / shared_out (fp32,
+//             or fp16 when the caller asks for y_sorted_h / shared_out_h)
 //
 // The activations keep the permuted 16-group k order the dequantiser
 // produces (pairs (i, i+8)), so codes unpack straight into their slots.  The

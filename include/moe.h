@@ -209,10 +209,12 @@ int moe_combine(const float* y_sorted, const int32_t* pair_pos, const float* top
 /* The whole layer: route, permute, expert FFN, shared expert and combine in
  * one call, with the optional stack glue of moe_combine.  topk_idx / topk_w
  * may be NULL (then the workspace holds them).  With the grouped-GEMM
- * algorithm the routed expert outputs pass from the down projection to the
- * combine as fp16 (the shared output, the weights and the sum stay fp32), so
- * its bits differ from moe_expert_ffn + moe_combine, which keep y_sorted in
- * fp32; both are within the output tolerance of the fp64 layer. */
+ * algorithm the routed and shared expert outputs pass from the down
+ * projection to the combine as fp16 (the weights and the sum stay fp32), so
+ * its bits differ from moe_expert_ffn + moe_combine, which keep y_sorted and
+ * shared_out in fp32;
+ * both are within the output tolerance of the fp64 layer.  The selection
+ * (topk_idx, topk_w) equals moe_route's bit for bit on every path. */
 int moe_layer_forward(const void* x, moe_dtype x_dtype, int64_t T, const moe_layer* layer,
                       const moe_shape* shape, float* out, float* residual,
                       uint16_t* next_in_bf16, int32_t* topk_idx, float* topk_w,
