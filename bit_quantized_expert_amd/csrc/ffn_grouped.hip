@@ -161,13 +161,21 @@ __device__ __forceinline__ void load_b2(BRaw2<QBITS>& r, const uint8_t* codes, c
 
 // word q (0..3) of a lane's step -> the prepared sources of its 8 pairs.
 // sel (half steps, lane h = 1, q < 2): word q of the second block instead
-// (block 4 step + 1).
-template <int QBITS>
+// (block 4 step + 1).  MASK: blocks past K read as zero weights (any K); with
+// K a multiple of 64 a lane's blocks are all real or belong to a column past
+// the matrix or a step past the last, whose products are never stored, so
+// the scale is only duplicated into both halves.
+template <int QBITS, bool MASK = true>
 __device__ __forceinline__ DqSrc dq_src_b2(const BRaw2<QBITS>& r, int q, bool sel) {
   const bool second = q >= 2 || sel;  // the lane's second block
-  const uint32_t sraw = second ? (r.s >> 16) : (r.s & 0xffffu);
-  const uint32_t sbits = (r.v >> (q >> 1)) & 1u ? sraw : 0u;  // blocks past K: scale 0, weights 0
-  const half2v s2 = as_half2(sbits | (sbits << 16));
+  half2v s2;
+  if constexpr (MASK) {
+    const uint32_t sraw = second ? (r.s >> 16) : (r.s & 0xffffu);
+    const uint32_t sbits = (r.v >> (q >> 1)) & 1u ? sraw : 0u;  // blocks past K: scale 0, weights 0
+    s2 = as_half2(sbits | (sbits << 16));
+  } else {
+    s2 = as_half2(__builtin_amdgcn_perm(r.s, r.s, second ? 0x03020302u : 0x01000100u));
+  }
   const uint32_t w = q < 2 && sel ? r.c[q + 2] : r.c[q];
   if constexpr (QBITS == 2) {
     return dq2_src(w, s2);
@@ -181,9 +189,9 @@ __device__ __forceinline__ DqSrc dq_src_b2(const BRaw2<QBITS>& r, int q, bool se
 }
 
 // word q of a lane's step -> the two permuted k-slices
-template <int QBITS>
+template <int QBITS, bool MASK = true>
 __device__ __forceinline__ void dq_b2(const BRaw2<QBITS>& r, int q, bool sel, half8& lo, half8& hi) {
-  dq_word<QBITS>(dq_src_b2<QBITS>(r, q, sel), lo, hi);
+  dq_word<QBITS>(dq_src_b2<QBITS, MASK>(r, q, sel), lo, hi);
 }
 
 // silu(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (about 1e-7
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
     if (live) {
       const bool hs0 = half_step(0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dq_b2<QBITS>(rawA[j], 0, hs0 && h, bf[0][0][j], bf[0][1][j]);
+      for (int j = 0; j < 2; ++j) dq_b2<QBITS, KM == 0>(rawA[j], 0, hs0 && h, bf[0][0][j], bf[0][1][j]);
 #pragma unroll
       for (int i = 0; i < MI; ++i) af[i] = frag(As[0], i, (hs0 ? 32 : 64) * h);
     }
@@ -415,8 +423,8 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
                 else af[i] = frag(Ab, i, acol + 16 * (q + 1));
               }
               if (g == 0) {
-                if (last) d = dq_src_b2<QBITS>(rn[hf], qn, seln);
-                else d = dq_src_b2<QBITS>(rc[hf], qn, seln);
+                if (last) d = dq_src_b2<QBITS, KM == 0>(rn[hf], qn, seln);
+                else d = dq_src_b2<QBITS, KM == 0>(rc[hf], qn, seln);
               }
               // this group's share of the word's dequantisation steps, taken four
               // pairs at a time step by step, so that consecutive VALU ops are
@@ -480,7 +488,7 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
           if (q >= 2 && half_step) break;
           half8 blo[2], bhi[2];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) dq_b2<QBITS>(bring[j], q, sel, blo[j], bhi[j]);
+          for (int j = 0; j < 2; ++j) dq_b2<QBITS, KM == 0>(bring[j], q, sel, blo[j], bhi[j]);
 #pragma unroll
           for (int half_ = 0; half_ < 2; ++half_) {
             half8 af[MI];
