@@ -299,7 +299,8 @@ __global__ __launch_bounds__(64 * NWV, NWV > 4 ? 1 : 2) void grouped_gemm2_kerne
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       // K tail: the group's weights are zero, so any finite values do: the row's first group
-      const int col = step * kBK2 + agrp[i] * 16 < K ? step * kBK2 : -agrp[i] * 16;
+      // (with K a multiple of 128 every step is whole)
+      const int col = KM == 1 || step * kBK2 + agrp[i] * 16 < K ? step * kBK2 : -agrp[i] * 16;
       const uint4v* p = reinterpret_cast<const uint4v*>(asrc[i] + col);
       r[i][0] = p[0];
       r[i][1] = p[1];
