@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const XT* __restrict__
 // from zero in increasing block order; the class sums are added 0, 1, ..., 7
 // (S = a0, S = S + a1, ...), then the bias.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int router_class_len(int nkb) { return (nkb + 7) / 8; }
+__host__ __device__ __forceinline__ int router_class_len(int nkb) { return (nkb + 7) / 8; }
 
 // Few tokens: workgroup = EPW experts x 16 tokens on one 16 x 16 MFMA tile,
 // 8 waves; wave w runs class w and the 8 partial tiles meet in LDS.  With
@@ -224,7 +224,16 @@ constexpr size_t rt_lds() {
 // steps whose loads are in flight during a step's MFMAs (register sets of
 // the staging ring: 2 fit beside RK = 4 in 256 registers, 1 beside RK = 2 in
 // 128, where the second workgroup of the CU covers the latency).
-template <int RK, int OCC, int PD, int ET>
+// WHOLE: every class is PD whole steps of RK blocks (router_whole_classes;
+// the 2048-wide hidden of the stack), so a step's blocks are unrolled and the
+// fold runs once per ring turn.
+template <int RK, int PD>
+__host__ __device__ inline bool router_whole_classes(int H) {
+  const int nkb = H / 32, cl = router_class_len(nkb);
+  return cl % RK == 0 && nkb % cl == 0 && cl / RK == PD;
+}
+
+template <int RK, int OCC, int PD, int ET, bool WHOLE = false>
 __global__ __launch_bounds__(4 * ET, OCC) void router_gemm_kernel(const uint16_t* __restrict__ x, int64_t T, int H,
                                                             const uint16_t* __restrict__ w,
                                                             const float* __restrict__ bias, int E,
@@ -300,27 +309,38 @@ __global__ __launch_bounds__(4 * ET, OCC) void router_gemm_kernel(const uint16_t
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) S[i][j] = acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+  // block k of the staged step: 2 x 4 MFMA tiles of the class chain
+  auto mfma_block = [&](int k) {
+    uint4v af[2], bf[4];
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+      af[i2] = *reinterpret_cast<const uint4v*>(rs + (32 * wt + 16 * i2 + n) * kPitch + k * 32 + 8 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bf[j] = *reinterpret_cast<const uint4v*>(rs + (kRtT + 64 * we + 16 * j + n) * kPitch + k * 32 + 8 * g);
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i2]),
+                                                             __builtin_bit_cast(bf16x8, bf[j]), acc[i2][j], 0, 0, 0);
+  };
+  auto fold = [&](int c) {  // the class is done: S += its chain
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        S[i2][j] = c == 0 ? acc[i2][j] : S[i2][j] + acc[i2][j];
+        acc[i2][j] = float4v{0.f, 0.f, 0.f, 0.f};
+      }
+  };
   auto run_step = [&](uint4v (&st)[NQ], int i) {
     __syncthreads();  // the previous step's fragments are read
     store_step(st);
     __syncthreads();
     load_step(st, i + PD);  // the ring slot is free again: step i + PD's loads
     const int b = step_b(i), nsub = min(RK, step_end(i) - b);
-    for (int k = 0; k < nsub; ++k) {
-      uint4v af[2], bf[4];
-#pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2)
-        af[i2] = *reinterpret_cast<const uint4v*>(rs + (32 * wt + 16 * i2 + n) * kPitch + k * 32 + 8 * g);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const uint4v*>(rs + (kRtT + 64 * we + 16 * j + n) * kPitch + k * 32 + 8 * g);
-#pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i2]),
-                                                               __builtin_bit_cast(bf16x8, bf[j]), acc[i2][j], 0, 0, 0);
-    }
+    for (int k = 0; k < nsub; ++k) mfma_block(k);
     if (i % sp == sp - 1) {  // the class is done: S += its chain
       const int c = i / sp;
 #pragma unroll
@@ -334,12 +354,51 @@ __global__ __launch_bounds__(4 * ET, OCC) void router_gemm_kernel(const uint16_t
   };
 #pragma unroll
   for (int p = 0; p < PD; ++p) load_step(stg[p], p);
-  // whole ring turns: a step past the last one stages block 0 and runs no
-  // MFMA (its class fold adds +0), and every turn issues and waits for the
-  // ring slots in the same order, so the compiler's wait counts stay exact
-  for (int i = 0; i < n_steps; i += PD) {
+  if constexpr (WHOLE) {
+    // whole classes of PD whole steps (the 2048-wide hidden of the stack): the
+    // blocks of a step are unrolled and the class folds once per ring turn
+    for (int c = 0; c < n_cls; ++c) {
 #pragma unroll
-    for (int p = 0; p < PD; ++p) run_step(stg[p], i + p);
+      for (int p = 0; p < PD; ++p) {
+        __syncthreads();  // the previous step's fragments are read
+        store_step(stg[p]);
+        __syncthreads();
+        load_step(stg[p], c * PD + p + PD);  // the ring slot is free again
+        // the blocks one after another, block k + 1's fragments read during block k's MFMAs (two
+        // fragment sets: all RK blocks' would not fit beside the staging ring)
+        uint4v fa[2][2], fb[2][4];
+        auto frags = [&](int k, uint4v(&xa)[2], uint4v(&xb)[4]) {
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2)
+            xa[i2] = *reinterpret_cast<const uint4v*>(rs + (32 * wt + 16 * i2 + n) * kPitch + k * 32 + 8 * g);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            xb[j] = *reinterpret_cast<const uint4v*>(rs + (kRtT + 64 * we + 16 * j + n) * kPitch + k * 32 + 8 * g);
+        };
+        frags(0, fa[0], fb[0]);
+#pragma unroll
+        for (int k = 0; k < RK; ++k) {
+          if (k + 1 < RK) frags(k + 1, fa[(k + 1) & 1], fb[(k + 1) & 1]);
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc[i2][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[k & 1][i2]),
+                                                                   __builtin_bit_cast(bf16x8, fb[k & 1][j]),
+                                                                   acc[i2][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      fold(c);
+    }
+  } else {
+    // whole ring turns: a step past the last one stages block 0 and runs no
+    // MFMA (its class fold adds +0), and every turn issues and waits for the
+    // ring slots in the same order, so the compiler's wait counts stay exact
+    for (int i = 0; i < n_steps; i += PD) {
+#pragma unroll
+      for (int p = 0; p < PD; ++p) run_step(stg[p], i + p);
+    }
   }
   // logits tile through LDS: S block (i, j) element r = token 32 wt + 16 i + 4 g + r, expert 64 we + 16 j + n
   __syncthreads();
@@ -377,17 +436,26 @@ hipError_t launch_router_mfma(const uint16_t* x, int64_t T, int H, const uint16_
     const int64_t n_tt = (T + kRtT - 1) / kRtT;
     const int n_et = (E + 127) / 128;
     const int64_t total = n_tt * n_et;
+    const bool whole = router_whole_classes<4, 2>(H);
     if (total >= 512) {  // two resident workgroups per CU have work: the 128-register variant
       router_gemm_kernel<2, 4, 1, 128><<<unsigned((total + 7) / 8 * 8), 512, rt_lds<2, 128>(), stream>>>(
           x, T, H, w, bias, E, logits, n_et, total);
     } else if (total >= 256) {
-      router_gemm_kernel<4, 2, 2, 128><<<unsigned((total + 7) / 8 * 8), 512, rt_lds<4, 128>(), stream>>>(
-          x, T, H, w, bias, E, logits, n_et, total);
+      if (whole)
+        router_gemm_kernel<4, 2, 2, 128, true><<<unsigned((total + 7) / 8 * 8), 512, rt_lds<4, 128>(), stream>>>(
+            x, T, H, w, bias, E, logits, n_et, total);
+      else
+        router_gemm_kernel<4, 2, 2, 128><<<unsigned((total + 7) / 8 * 8), 512, rt_lds<4, 128>(), stream>>>(
+            x, T, H, w, bias, E, logits, n_et, total);
     } else {  // fewer 128-wide tiles than CUs: 64-expert tiles, twice as many
       const int n_et64 = (E + 63) / 64;
       const int64_t total64 = n_tt * n_et64;
-      router_gemm_kernel<4, 2, 2, 64><<<unsigned((total64 + 7) / 8 * 8), 256, rt_lds<4, 64>(), stream>>>(
-          x, T, H, w, bias, E, logits, n_et64, total64);
+      if (whole)
+        router_gemm_kernel<4, 2, 2, 64, true><<<unsigned((total64 + 7) / 8 * 8), 256, rt_lds<4, 64>(), stream>>>(
+            x, T, H, w, bias, E, logits, n_et64, total64);
+      else
+        router_gemm_kernel<4, 2, 2, 64><<<unsigned((total64 + 7) / 8 * 8), 256, rt_lds<4, 64>(), stream>>>(
+            x, T, H, w, bias, E, logits, n_et64, total64);
     }
     return hipGetLastError();
   }
