@@ -619,7 +619,18 @@ constexpr int kTpD = 4;      // rounds of weight loads in flight in the per-slot
 constexpr int kTpNW = 4;     // row blocks (waves of gate rows) per workgroup of the per-slot kernels
 constexpr int kTpMinW = 1;   // workgroups per CU asked of the per-slot gate/up kernel
 constexpr int kTpEarly = 2;  // items per thread of an early activation staging
-constexpr int kPersGrid = 512;       // persistent gate/up workgroups (two per CU)
+constexpr int kPersGrid = 512;       // persistent gate/up item groups of 8 waves (two per CU)
+// Item groups per persistent gate/up workgroup: 2 (one 16-wave workgroup per
+// CU) above 8 tokens, where the selection made by every workgroup then runs
+// once per CU with one token per wave instead of two; 1 for fewer tokens
+// (each wave already ranks one token at most, and the wider workgroup was
+// measured slower there).
+inline int pers_gateup_groups(int64_t T) { return T > 8 ? 2 : 1; }
+// workgroups of the persistent gate/up launch for at most `slots` slots of
+// n_rb items each
+inline int pers_gateup_grid(int64_t slots, int n_rb, int ng) {
+  return int(std::min<int64_t>(kPersGrid / ng, (slots * n_rb + ng - 1) / ng));
+}
 constexpr int kPersGridDown = 1024;  // persistent down workgroups (four per CU)
 // NW row blocks of 16 per workgroup; waves 0..NW-1 take the gate rows of
 // block wv, waves NW..2NW-1 the up rows (half the dequantisation per wave);
@@ -789,11 +800,12 @@ __global__ __launch_bounds__(128 * NW, kTpMinW) void gemv_gateup_tp_kernel(FfnAr
 // ---------------------------------------------------------------------------
 // Persistent gate/up for 2..kGemvMaxM tokens: the same per-row arithmetic as
 // gemv_gateup_tp_kernel (8 waves, 64 rows per work item, gate and up waves,
-// four round classes), but a fixed grid of G workgroups each walks a
-// contiguous run of the (slot, 64-row block) items.  The tokens of the
-// workgroup's slots are staged in LDS once (rows indexed by token; a slot's
-// MFMA rows pick its tokens through the token mask), and the weight
-// pipeline runs on across items: the next item's
+// four round classes), but a fixed grid of G workgroups, each of NG item
+// groups of 8 waves (pers_gateup_groups), and each group walks a contiguous run
+// of the (slot, 64-row block) items.  The tokens of the workgroup's slots are
+// staged in LDS once for its groups (rows indexed by token; a slot's MFMA
+// rows pick its tokens through the token mask), and (SEL) the selection is
+// made once for them.  The weight pipeline runs on across items: the next item's
 // slot entry is requested when an item starts and its first D rounds of
 // weights while the current item's last D rounds are computed.  So the
 // first-load latency is paid once per workgroup instead of once per item.
@@ -808,31 +820,32 @@ __global__ __launch_bounds__(128 * NW, kTpMinW) void gemv_gateup_tp_kernel(FfnAr
 // Otherwise the slot table and header come from a selection launch.
 constexpr int kSelPersMaxExperts = 512;
 
-template <int QBITS, int UNIT, typename XT, bool SEL>
-__global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_rb, int G,
-                                                               const int4* __restrict__ slots,
-                                                               const int32_t* __restrict__ header, SelOut so) {
+template <int QBITS, int UNIT, typename XT, bool SEL, int NG>
+__global__ __launch_bounds__(512 * NG) void gemv_gateup_pers_kernel(FfnArgs a, int n_rb, int G,
+                                                                   const int4* __restrict__ slots,
+                                                                   const int32_t* __restrict__ header, SelOut so) {
   // slots / header are a.slots / a.header, read-only here: scalar loads,
   // which wait on their own counter instead of behind the weight loads
-  constexpr int NW = 4, D = 4, kThreads = 512;
+  constexpr int NW = 4, D = 4, kThreads = 512 * NG;
   extern __shared__ __attribute__((aligned(16))) f16 xs[];  // [T][H + 8]
   // the up sums of the item loop; before it, the ranking scratch of the selection
   __shared__ union {
-    float4v up_x[NW][64];
-    SelRankLds tk[8];
+    float4v up_x[NG][NW][64];
+    SelRankLds tk[8 * NG];
   } ux;
-  float4v(&up_x)[NW][64] = ux.up_x;
-  __shared__ SelLds<SEL ? kSelPersMaxExperts : 1, SEL ? 8 : 1> sel;
+  __shared__ SelLds<SEL ? kSelPersMaxExperts : 1, SEL ? 8 * NG : 1> sel;
   const int H = a.H, ldsw = H + 8, T = int(a.T);
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-  const int wr = wv % NW, mat = wv / NW;
+  const int ig = wv / 8, wl = wv % 8;  // item group, wave in the group
+  float4v(&up_x)[NW][64] = ux.up_x[ig];
+  const int wr = wl % NW, mat = wl / NW;
   const int n = lane & 15, g = lane >> 4;
   const int n_units = H / UNIT, rounds = n_units / 4;  // a multiple of D (host-checked)
   // Token staging into LDS (fp16, permuted 16-groups; row = token id):
   // item i of a pass is chunk i % chunks of the (i / chunks)-th token of umask.
   const XT* xsrc = static_cast<const XT*>(a.x);
   const int chunks = H / 16;
-  constexpr int NB = sizeof(XT) == 4 ? 2 : 4;
+  constexpr int NB = (sizeof(XT) == 4 ? 2 : 4) / NG;
   auto stage_load = [&](uint32_t umask, int items, int base, Raw16<XT>(&raw)[NB], int(&dst)[NB]) {
 #pragma unroll
     for (int k2 = 0; k2 < NB; ++k2) {
@@ -868,7 +881,7 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
     // the last workgroup writes the selection out: it has the fewest items
     // (none when there are fewer items than workgroups), so the ranks and
     // writes stay off the other workgroups' path
-    n_active = select_in_workgroup<kSelPersMaxExperts / 64, 8, kSelPersMaxExperts>(
+    n_active = select_in_workgroup<kSelPersMaxExperts / 64, 8 * NG, kSelPersMaxExperts>(
         so, T, a.E, a.k, a.has_shared, sel, ux.tk, blockIdx.x == gridDim.x - 1);
     n_valid = n_active + (a.has_shared ? 1 : 0);
   } else {
@@ -887,10 +900,19 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
       return slots[s];
     }
   };
-  const int n_items = n_valid * n_rb;
-  const int q = n_items / G, rem = n_items - q * G, b = blockIdx.x;
-  const int it0 = b * q + min(b, rem), it1 = it0 + q + (b < rem ? 1 : 0);
-  if (it0 >= it1) return;
+  // NG G workers take contiguous runs of the items: worker w = g G + b is
+  // item group g of workgroup b, so that with fewer items than workers every
+  // workgroup's first group has one before any second group does (a CU
+  // streams one item's weights faster than two).  Every group runs as many
+  // barrier pairs as its workgroup's first runs item iterations (the item
+  // loop's barriers are the workgroup's): after its own items, bare ones.
+  const int n_items = n_valid * n_rb, n_workers = NG * G;
+  const int q = n_items / n_workers, rem = n_items - q * n_workers, b = blockIdx.x;
+  auto first = [&](int w) { return w * q + min(w, rem); };
+  const int n_iter = first(b + 1) - first(b);  // the first group's items: the most
+  if (n_iter == 0) return;
+  const int it0 = first(ig * G + b), it1 = first(ig * G + b + 1);  // the group's items
+  const int it_first = it0 < it1 ? it0 : first(b);                  // a real item of the workgroup
 
   // an item's weight source for this wave (plain values: no aggregate copies)
   auto make = [&](int it, int4 si, const uint8_t*& wc, const uint16_t*& wsc, int& rows, int& row, bool& on) {
@@ -905,18 +927,22 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
     wsc = Mq.scales + ex * Mq.scale_stride;
   };
 
-  int4 si_cur = slot_at(it0 / n_rb);
+  int4 si_cur = slot_at(it_first / n_rb);
   const uint8_t* c_wc;
   const uint16_t* c_wsc;
   int c_rows, c_row;
   bool c_on;
-  make(it0, si_cur, c_wc, c_wsc, c_rows, c_row, c_on);
+  make(it_first, si_cur, c_wc, c_wsc, c_rows, c_row, c_on);
   // Weight loads are unconditional (a wave past its rows reads the last row,
   // and the prefetch past a workgroup's last item rereads its own weights):
   // a load under a branch makes the compiler wait for every load in flight.
+  // (A group without items loads nothing: the staging below waits for every
+  // load anyway.)
   Unit<QBITS, UNIT> uw[D];
+  if (it0 < it1) {
 #pragma unroll
-  for (int i = 0; i < D; ++i) load_unit(uw[i], c_wc, c_wsc, c_rows, H, min(c_row, c_rows - 1), i * 4 + g);
+    for (int i = 0; i < D; ++i) load_unit(uw[i], c_wc, c_wsc, c_rows, H, min(c_row, c_rows - 1), i * 4 + g);
+  }
   // the tokens into LDS: with SEL all of them (the first pass is loaded),
   // else the union of the workgroup's slots' token masks
   {
@@ -927,7 +953,11 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
       base0 = NB * kThreads;
     } else {
       umask = 0u;
-      for (int sl = it0 / n_rb; sl <= (it1 - 1) / n_rb; ++sl) umask |= uint32_t(slot_at(sl).w);
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {  // the slots of every group's run
+        const int r0 = first(gg * G + b), r1 = first(gg * G + b + 1);
+        for (int sl = r0 / n_rb; r0 < r1 && sl <= (r1 - 1) / n_rb; ++sl) umask |= uint32_t(slot_at(sl).w);
+      }
     }
     const int items = __builtin_popcount(umask) * chunks;
     for (int base = base0; base < items; base += NB * kThreads) {
@@ -1023,6 +1053,10 @@ __global__ __launch_bounds__(512) void gemv_gateup_pers_kernel(FfnArgs a, int n_
     c_row = n_row;
     c_on = n_on;
     si_cur = si_next;
+  }
+  for (int j = it1 - it0; j < n_iter; ++j) {  // the barriers of the first group's further items
+    __syncthreads();
+    __syncthreads();
   }
 }
 
@@ -1284,17 +1318,16 @@ static hipError_t launch_gemv_q(const FfnArgs& a, hipStream_t stream, int phases
                         (!a.has_shared || a.Is == a.I);
       if (pers) {
         const int n_rb = (a.I + 63) / 64;
-        const int G = int(std::min<int64_t>(kPersGrid, int64_t(slots) * n_rb));
+        const int ng = pers_gateup_groups(a.T);
+        const int G = pers_gateup_grid(slots, n_rb, ng);
         const size_t lds_p = size_t(a.T) * (a.H + 8) * sizeof(f16);
-        if (a.x_kind == kXBF16)
-          gemv_gateup_pers_kernel<QBITS, 64, uint16_t, false>
-              <<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header, SelOut{});
-        else if (a.x_kind == kXF16)
-          gemv_gateup_pers_kernel<QBITS, 64, f16, false>
-              <<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header, SelOut{});
-        else
-          gemv_gateup_pers_kernel<QBITS, 64, float, false>
-              <<<G, 512, lds_p, stream>>>(a, n_rb, G, a.slots, a.header, SelOut{});
+#define GP(X_, NG_) \
+  gemv_gateup_pers_kernel<QBITS, 64, X_, false, NG_><<<G, 512 * NG_, lds_p, stream>>>(a, n_rb, G, a.slots, a.header, \
+                                                                                    SelOut{})
+        if (a.x_kind == kXBF16) { if (ng == 2) GP(uint16_t, 2); else GP(uint16_t, 1); }
+        else if (a.x_kind == kXF16) { if (ng == 2) GP(f16, 2); else GP(f16, 1); }
+        else { if (ng == 2) GP(float, 2); else GP(float, 1); }
+#undef GP
       } else {
         const dim3 grid(unsigned((max_rows + 16 * NW - 1) / (16 * NW)), unsigned(slots));
 #define GU(U_, X_) gemv_gateup_tp_kernel<QBITS, U_, X_, NW><<<grid, 128 * NW, lds, stream>>>(a)
@@ -1351,12 +1384,17 @@ hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t 
   if (!ok) return hipErrorNotSupported;
   const int slots = int(std::min<int64_t>(a.E, P)) + (a.has_shared ? 1 : 0);
   const int n_rb = (a.I + 63) / 64;
-  const int G = int(std::min<int64_t>(kPersGrid, int64_t(slots) * n_rb));
-#define GS(Q_, X_) gemv_gateup_pers_kernel<Q_, 64, X_, true><<<G, 512, lds_p, stream>>>(a, n_rb, G, nullptr, nullptr, so)
+  const int ng = pers_gateup_groups(a.T);
+  const int G = pers_gateup_grid(slots, n_rb, ng);
+#define GS(Q_, X_, NG_) \
+  gemv_gateup_pers_kernel<Q_, 64, X_, true, NG_><<<G, 512 * NG_, lds_p, stream>>>(a, n_rb, G, nullptr, nullptr, so)
+#define GSX(Q_, X_)            \
+  if (ng == 2) GS(Q_, X_, 2); \
+  else GS(Q_, X_, 1)
 #define GSQ(Q_)                          \
-  if (a.x_kind == kXBF16) GS(Q_, uint16_t); \
-  else if (a.x_kind == kXF16) GS(Q_, f16);  \
-  else GS(Q_, float)
+  if (a.x_kind == kXBF16) GSX(Q_, uint16_t); \
+  else if (a.x_kind == kXF16) GSX(Q_, f16);  \
+  else GSX(Q_, float)
   if (a.qbits == 2) {
     GSQ(2);
   } else if (a.qbits == 3) {
@@ -1365,6 +1403,7 @@ hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t 
     GSQ(4);
   }
 #undef GSQ
+#undef GSX
 #undef GS
   return hipGetLastError();
 }

@@ -154,6 +154,19 @@ def test_full_shape_4bit(T):
     _check_layer(M, dl, x, "gemv")
 
 
+@pytest.mark.parametrize("T", [9, 16])
+def test_persistent_gateup_many_items(T):
+    """Uniform routing of 9 or 16 tokens over 512 experts: about 1,500 (slot,
+    64-row block) items of the persistent gate/up kernel with the selection
+    inside, several per item group of its 16-wave workgroups, the two groups
+    of some workgroups with different counts."""
+    M = _M()
+    wl = synth.custom(f"u{T}", 1024, 704, 512, 10, 704, 2, T, seed=13, act_dtype=torch.bfloat16, zipf_bias=False)
+    dl = _layer(wl)
+    x = synth.tokens(wl, "cuda")
+    _check_layer(M, dl, x, "gemv")
+
+
 def test_decode16_layer_and_batch_invariance():
     M = _M()
     wl = synth.WORKLOADS["decode16"]
