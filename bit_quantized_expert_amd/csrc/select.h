@@ -121,25 +121,57 @@ __device__ int select_in_workgroup(const SelOut& o, int T, int E, int k, int has
   // ---- one scan of (count | active << 16): the low half gives the
   // offsets, the high half the slot of each active expert (counts <= 16 T
   // and active experts <= EMAX <= 4096, so neither half carries)
-  for (int e = threadIdx.x; e < E; e += NT) {
+  auto count_of = [&](int e, uint32_t& m) {
     const bool active = skip ? S.hmask[e] != 0u : S.tmask[e] != 0u;
     if (skip && !active) S.tmask[e] = 0u;  // a dropped expert: no pairs, no slot
-    const int c = __builtin_popcount(S.tmask[e]);
+    m = S.tmask[e];
+    const int c = __builtin_popcount(m);
     if (write) o.counts[e] = c;
-    S.cnt[e] = c | (c > 0 ? 1 << 16 : 0);
-  }
-  __syncthreads();
-  const int packed_total = block_scan_fast<NT>(S.cnt, E, S.tmp);
-  const int total = packed_total & 0xffff, n_active = packed_total >> 16;
-  for (int e = threadIdx.x; e < E; e += NT) {
-    const uint32_t m = S.tmask[e];
-    if (m != 0u) S.slot_e[S.cnt[e] >> 16] = uint16_t(e);
+    return c | (c > 0 ? 1 << 16 : 0);
+  };
+  auto place = [&](int e, uint32_t m, int sc) {  // sc: e's scanned (offset | slot << 16)
+    if (m != 0u) S.slot_e[sc >> 16] = uint16_t(e);
     if (write) {
-      const int off = S.cnt[e] & 0xffff;
+      const int off = sc & 0xffff;
       o.offsets[e] = off;
-      if (m != 0u) o.slots[S.cnt[e] >> 16] = int4{e, off, __builtin_popcount(m), int(m)};
+      if (m != 0u) o.slots[sc >> 16] = int4{e, off, __builtin_popcount(m), int(m)};
     }
+  };
+  int packed_total;
+  if (E <= NT) {
+    // one expert per thread: the count, the scan and the placement in one
+    // pass with a single barrier (the wave totals)
+    const int e = threadIdx.x;
+    uint32_t m = 0u;
+    const int v = e < E ? count_of(e, m) : 0;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) S.tmp[wv] = incl;
+    __syncthreads();
+    int base = 0;
+    packed_total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const int t2 = S.tmp[w2];
+      base += w2 < wv ? t2 : 0;
+      packed_total += t2;
+    }
+    if (e < E) {
+      const int sc = base + incl - v;
+      S.cnt[e] = sc;
+      place(e, m, sc);
+    }
+    if (write) __syncthreads();  // the scatter below reads other experts' offsets (uniform: write is)
+  } else {
+    for (int e = threadIdx.x; e < E; e += NT) {
+      uint32_t m;
+      S.cnt[e] = count_of(e, m);
+    }
+    __syncthreads();
+    packed_total = block_scan_fast<NT>(S.cnt, E, S.tmp);
+    for (int e = threadIdx.x; e < E; e += NT) place(e, S.tmask[e], S.cnt[e]);
+    if (write) __syncthreads();
   }
+  const int total = packed_total & 0xffff, n_active = packed_total >> 16;
   if (write) {
     if (threadIdx.x == 0) o.offsets[E] = total;
     // stable scatter: the pairs of expert e before pair (t, j) are those of
