@@ -1388,9 +1388,11 @@ hipError_t launch_gateup_select(const FfnArgs& a, const SelOut& so, hipStream_t 
   const int G = pers_gateup_grid(slots, n_rb, ng);
 #define GS(Q_, X_, NG_) \
   gemv_gateup_pers_kernel<Q_, 64, X_, true, NG_><<<G, 512 * NG_, lds_p, stream>>>(a, n_rb, G, nullptr, nullptr, so)
-#define GSX(Q_, X_)            \
-  if (ng == 2) GS(Q_, X_, 2); \
-  else GS(Q_, X_, 1)
+#define GSX(Q_, X_)             \
+  do {                          \
+    if (ng == 2) GS(Q_, X_, 2); \
+    else GS(Q_, X_, 1);         \
+  } while (0)
 #define GSQ(Q_)                          \
   if (a.x_kind == kXBF16) GSX(Q_, uint16_t); \
   else if (a.x_kind == kXF16) GSX(Q_, f16);  \
