@@ -44,20 +44,21 @@ __global__ __launch_bounds__(256) void x16_kernel(const XT* __restrict__ x, int6
 }
 
 // ---------------------------------------------------------------------------
-// The grouped GEMM.  A workgroup owns BM rows (128, or 96 when experts hold
-// few rows each: fewer padding rows per tile) x 8 waves; each wave a
-// BM x 64 block (BM/32 x 2 MFMA tiles of 32 x 32), so an A fragment read
-// from LDS feeds two MFMAs and a B fragment BM/32.  Every output element
-// goes through the same MFMA sequence for either BM.  The
+// The grouped GEMM.  A workgroup owns BM rows (128 with 8 waves, or 96 with
+// 4 waves when experts hold few rows each: fewer padding rows per tile);
+// each wave a BM x 64 block (BM/32 x 2 MFMA tiles of 32 x 32), so an A
+// fragment read from LDS feeds two MFMAs and a B fragment BM/32.  Every
+// output element goes through the same MFMA sequence for either BM.  The
 // weights never pass through LDS: each wave loads and dequantises its own
 // 64 columns straight into MFMA operands (lane (n, h) of a 32-column set
 // takes 16 code bytes = words 4h .. 4h+3 of the row's 128-weight step; MFMA
 // k-step kk pairs slice kk of lane h = 0 with slice kk of lane h = 1, and
 // the A fragments are read from LDS in the same order).  K advances 128 per
-// step; the activation tile is double-buffered in LDS (fp16, permuted
-// 16-groups), one barrier per step.
-//   gate/up: wave w = gate rows nt*256 + 32w .. +32 and the same up rows;
-//   down   : wave w = output columns nt*512 + 64w .. +64.
+// step; the activation tile is staged in LDS (fp16, permuted 16-groups) in
+// two buffers (plain loop) or three (pipelined loop), one barrier per step.
+// With NWV waves:
+//   gate/up: wave w = gate rows nt*32*NWV + 32w .. +32 and the same up rows;
+//   down   : wave w = output columns nt*64*NWV + 64w .. +64.
 // ---------------------------------------------------------------------------
 constexpr int kBK2 = 128, kLDA2 = kBK2 + 8;  // A row pitch in halves
 
